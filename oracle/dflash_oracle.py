@@ -1,0 +1,306 @@
+"""CPU oracle of the DFlash drafter hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this module.  The product (the HIP library and its
+Python binding) never imports, calls or links it, and this module imports
+nothing from the product.
+
+What it computes: the drafter's work for one speculative cycle, written out
+step by step in float64 numpy, in the order the pages describe it.  Where the
+device stores a tensor in bf16 or feeds it to a bf16 matrix instruction, the
+oracle rounds the same tensor to bf16 (round to nearest, ties to even) with
+``bf16_round`` -- see the list in ``ROUNDING_POINTS``.  Everything else stays
+float64.  For float32 workloads nothing is rounded.
+
+Sources (web pages on DFlash, cited by page and section):
+  [Arch]    zhichai.net, "DFlash 的架构密码——扩散模型如何「寄生」在自回归模型上"
+            sections: 第一层 Feature Fusion, 第二层 KV Injection, 第三层 Block
+            Diffusion, 训练策略 1-3, 技术细节补充 (提取层数, 投影层, 稀疏注意力训练).
+  [Summary] ai-stack.site, "DFlash：基于块扩散的闪存推测解码方法", 实践 2
+            (block verification; keep up to the last correct token) and FAQ 4
+            (output is lossless).
+  [News]    zaocj.com news article on DFlash (ICML 2026): one forward pass with
+            bidirectional attention fills 8-16 token slots; 5-6 target layers.
+
+Readings of points the pages leave open (each repeated where it is used):
+  R1 layer ids are 1-based; "from layer 2 to the third-from-last" is
+     [2, L-2]; uniform positions are rounded half up.
+  R2 the fusion FC has no bias; RMSNorm eps = 1e-6; concat order = ascending id.
+  R3 RoPE (rotate-half pairing i <-> i+d/2, theta = 1e6) on q and k; context
+     token t sits at position t, block slot j at L + j.
+  R4 block slot 0 holds the anchor (the previous cycle's bonus token), slots
+     1..B-1 hold the mask token; draft j is the argmax of slot j's logits.
+  R5 no mask inside a block; a block sees its own sequence's context and block.
+  R6 every argmax breaks ties by the lowest index.
+  R7 verification: a = length of the longest prefix with target_argmax[j] ==
+     draft[j+1]; bonus = target_argmax[a].
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# Tensors the device holds in bf16 (or feeds to bf16 MFMA) on bf16 workloads.
+ROUNDING_POINTS = (
+    "c: fused context feature",
+    "K, V cache entries after RoPE",
+    "u: every RMSNorm output that feeds a projection",
+    "q, k, v of the block after RoPE",
+    "o: attention output feeding the O projection",
+    "h: silu(gate) * up feeding the down projection",
+)
+
+_BF16_MAX = float.fromhex("0x1.fep127")
+
+
+# --------------------------------------------------------------- numerics
+
+def bf16_round(x) -> np.ndarray:
+    """Round to the nearest bf16 value (ties to even), returned as float64.
+
+    bf16 keeps 8 significant bits and float32's exponent range; below 2**-126
+    its spacing is fixed at 2**-133.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    e = np.maximum(e, -125)
+    r = np.ldexp(np.rint(np.ldexp(x, 8 - e)), e - 8)
+    r = np.where(np.abs(r) > _BF16_MAX, np.copysign(np.inf, x), r)
+    return np.where(np.isfinite(x), r, x)
+
+
+def _maybe_round(x, rb: bool):
+    return bf16_round(x) if rb else x
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+def rmsnorm(x, gain, eps: float) -> np.ndarray:
+    """y = x / sqrt(mean(x^2) + eps) * gain over the last axis ([Arch] 投影层: FC + RMSNorm)."""
+    x = _f64(x)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * _f64(gain)
+
+
+def rope(x, positions, theta: float) -> np.ndarray:
+    """Rotary embedding, reading R3.  x: [T, heads, d]; positions: [T].
+
+    Pair (i, i + d/2) is rotated by angle p * theta^(-2i/d).
+    """
+    x = _f64(x)
+    d = x.shape[-1]
+    half = d // 2
+    inv_freq = float(theta) ** (-(2.0 * np.arange(half, dtype=np.float64)) / d)
+    ang = _f64(positions)[:, None, None] * inv_freq[None, None, :]
+    cos, sin = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], axis=-1)
+
+
+def silu(x) -> np.ndarray:
+    x = _f64(x)
+    return x / (1.0 + np.exp(-x))
+
+
+def argmax_lowest(z, axis: int = -1) -> np.ndarray:
+    """Index of the largest entry; ties go to the lowest index (reading R6)."""
+    return np.argmax(z, axis=axis)
+
+
+# ------------------------------------------------------- (a1) layer rule
+
+def target_layer_ids(n_target_layers: int, n_select: int = 5) -> list:
+    """1-based ids of the target layers whose hidden states feed the drafter.
+
+    [Arch] 技术细节补充 / 提取层数: n_select layers sampled uniformly from the
+    2nd layer to the third-from-last layer ([News]: 5 to 6 layers).
+    Reading R1: the k-th id is 2 + k (L - 4) / (n - 1), rounded half up.
+    """
+    L, n = int(n_target_layers), int(n_select)
+    first, last = 2, L - 2
+    if n < 2 or last - first + 1 < n:
+        raise ValueError("need n_target_layers >= n_select + 3 and n_select >= 2")
+    ids = []
+    for k in range(n):
+        num = first * (n - 1) + k * (last - first)   # position times (n - 1)
+        ids.append((2 * num + (n - 1)) // (2 * (n - 1)))
+    return ids
+
+
+# ------------------------------------------- (a2, a3) feature fusion
+
+def fuse_context(feats, w_fc, g_fc, eps: float, round_bf16: bool) -> np.ndarray:
+    """Compact context feature c [T, H] from n target hidden-state slabs.
+
+    [Arch] 第一层 Feature Fusion: the sampled layers' hidden states are
+    concatenated and passed through a light projection; 技术细节补充 / 投影层:
+    the projection is an FC followed by RMSNorm.  Reading R2.
+    """
+    X = np.concatenate([_f64(f) for f in feats], axis=1)     # [T, n*H]
+    Y = X @ _f64(w_fc).T                                       # [T, H]
+    c = rmsnorm(Y, g_fc, eps)
+    return _maybe_round(c, round_bf16)
+
+
+# ------------------------------------------------- (a4) KV injection
+
+def inject_kv(c, positions, layers, shape, round_bf16: bool) -> list:
+    """Per drafter layer, the context K and V that the feature c contributes.
+
+    [Arch] 第二层 KV Injection: the context feature is not fed in as an
+    embedding; it goes straight into every layer's K and V projection, so the
+    drafter's cache holds the target's context at every layer.  Reading: each
+    layer's own W_k / W_v (the ones its block tokens use), RoPE on K at the
+    context positions (R3).  Returns [(K [T, Hkv, d], V [T, Hkv, d]), ...].
+    """
+    c = _f64(c)
+    T = c.shape[0]
+    Hkv, d = shape.n_kv_heads, shape.head_dim
+    out = []
+    for lw in layers:
+        k = (c @ _f64(lw["wk"]).T).reshape(T, Hkv, d)
+        v = (c @ _f64(lw["wv"]).T).reshape(T, Hkv, d)
+        k = rope(k, positions, shape.rope_theta)
+        out.append((_maybe_round(k, round_bf16), _maybe_round(v, round_bf16)))
+    return out
+
+
+# ------------------------------------------------- (a6') block attention
+
+def block_attention(q, K, V) -> np.ndarray:
+    """Softmax attention of one block's queries over the keys it may see.
+
+    q: [B, Hq, d]; K, V: [Lk, Hkv, d] = this sequence's context keys followed
+    by its own block's keys.  Every query sees every one of these keys (no mask
+    inside the block) and nothing else ([Arch] 技术细节补充 / 稀疏注意力训练:
+    bidirectional inside a block, no information flow between blocks; [News]:
+    bidirectional attention).  q-head h reads kv-head h // (Hq / Hkv).
+    """
+    q, K, V = _f64(q), _f64(K), _f64(V)
+    B, Hq, d = q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    out = np.empty((B, Hq, d), dtype=np.float64)
+    for h in range(Hq):
+        g = h // G
+        s = q[:, h, :] @ K[:, g, :].T / np.sqrt(d)            # [B, Lk]
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p = p / p.sum(axis=1, keepdims=True)
+        out[:, h, :] = p @ V[:, g, :]
+    return out
+
+
+# ------------------------------------------------- (a6) decoder layer
+
+def decoder_layer(x, positions, lw, k_ctx, v_ctx, shape, rb: bool) -> np.ndarray:
+    """One pre-norm drafter layer applied to one sequence's block.
+
+    x: [B, H] float64 residual stream; k_ctx, v_ctx: [L, Hkv, d] injected
+    context.  Attention half then SwiGLU feed-forward half, each with its own
+    RMSNorm and a residual add.
+    """
+    B = x.shape[0]
+    Hq, Hkv, d = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
+    eps = shape.rms_eps
+    u = _maybe_round(rmsnorm(x, lw["attn_norm"], eps), rb)
+    q = (u @ _f64(lw["wq"]).T).reshape(B, Hq, d)
+    k = (u @ _f64(lw["wk"]).T).reshape(B, Hkv, d)
+    v = (u @ _f64(lw["wv"]).T).reshape(B, Hkv, d)
+    q = _maybe_round(rope(q, positions, shape.rope_theta), rb)
+    k = _maybe_round(rope(k, positions, shape.rope_theta), rb)
+    v = _maybe_round(v, rb)
+    K = np.concatenate([_f64(k_ctx), k], axis=0)
+    V = np.concatenate([_f64(v_ctx), v], axis=0)
+    o = _maybe_round(block_attention(q, K, V).reshape(B, Hq * d), rb)
+    x = x + o @ _f64(lw["wo"]).T
+    u = _maybe_round(rmsnorm(x, lw["ffn_norm"], eps), rb)
+    h = _maybe_round(silu(u @ _f64(lw["wg"]).T) * (u @ _f64(lw["wu"]).T), rb)
+    return x + h @ _f64(lw["wd"]).T
+
+
+# --------------------------------------- (a5, a6, a7) one block, one pass
+
+def draft_block(weights, shape, caches, anchors, block_size: int) -> dict:
+    """Fill one block of mask slots per sequence in a single forward pass.
+
+    [Arch] 第三层 Block Diffusion: with the target's features as condition the
+    block (e.g. 16 tokens) is produced in one step, one forward pass; 训练策略
+    1: each block starts at an already verified token (the previous cycle's
+    bonus token); 训练策略 3: the drafter reuses the target's embedding and LM
+    head.  Readings R3-R6.
+
+    caches[b] = [(K_ctx [L_b, Hkv, d], V_ctx [L_b, Hkv, d]) per layer].
+    Returns draft_ids [N, B-1], final_hidden [N, B, H] (residual after the
+    last layer), logits [N, B, V], gap [N, B-1] (top-1 minus top-2 logit of
+    each draft slot).
+    """
+    rb = shape.dtype == "bf16"
+    N, B = len(anchors), int(block_size)
+    emb, lm = weights["embed"], weights["lm_head"]
+    final_h = np.empty((N, B, shape.hidden), dtype=np.float64)
+    logits = np.empty((N, B, shape.vocab), dtype=np.float64)
+    for b in range(N):
+        L = caches[b][0][0].shape[0]
+        tokens = [int(anchors[b])] + [shape.mask_token_id] * (B - 1)
+        positions = L + np.arange(B)
+        x = _f64(emb[tokens])                                   # [B, H]
+        for lw, (kc, vc) in zip(weights["layers"], caches[b]):
+            x = decoder_layer(x, positions, lw, kc, vc, shape, rb)
+        final_h[b] = x
+        u = _maybe_round(rmsnorm(x, weights["final_norm"], shape.rms_eps), rb)
+        logits[b] = u @ _f64(lm).T
+    z = logits[:, 1:, :]
+    draft_ids = argmax_lowest(z, axis=2).astype(np.int32)
+    srt = np.sort(z, axis=2)
+    gap = srt[:, :, -1] - srt[:, :, -2]
+    return {"draft_ids": draft_ids, "final_hidden": final_h, "logits": logits, "gap": gap}
+
+
+# ------------------------------------------------- (a8) greedy verify
+
+def verify_greedy(target_logits, drafts) -> tuple:
+    """Accepted draft count and bonus token per sequence.
+
+    The target scores the whole block in one pass; row j is its greedy choice
+    for the token after slot j.  Drafts are kept up to the last one that
+    matches ([Summary] 实践 2: keep up to the last correct token), and the
+    target's own choice at the first mismatch (or after the last draft) is the
+    bonus token that starts the next block ([Arch] 训练策略 1).  Reading R7.
+    target_logits: [N, B, V]; drafts: [N, B-1].  Returns (accept [N], bonus [N]).
+    """
+    t = argmax_lowest(_f64(target_logits), axis=2)
+    drafts = np.asarray(drafts)
+    N, Bm1 = drafts.shape
+    accept = np.zeros(N, dtype=np.int32)
+    bonus = np.zeros(N, dtype=np.int32)
+    for n in range(N):
+        a = 0
+        while a < Bm1 and t[n, a] == drafts[n, a]:
+            a += 1
+        accept[n] = a
+        bonus[n] = t[n, a]
+    return accept, bonus
+
+
+# ------------------------------------------------- whole-cycle helpers
+
+def prefill(weights, shape, feats_per_seq) -> list:
+    """Context caches for each sequence: fuse its features, inject them at 0..L-1."""
+    rb = shape.dtype == "bf16"
+    caches = []
+    for feats in feats_per_seq:
+        c = fuse_context(feats, weights["fc"], weights["fc_norm"], shape.rms_eps, rb)
+        caches.append(inject_kv(c, np.arange(c.shape[0]), weights["layers"], shape, rb))
+    return caches
+
+
+def append_context(cache, weights, shape, feats) -> list:
+    """Append the features of newly committed tokens to one sequence's cache."""
+    rb = shape.dtype == "bf16"
+    L = cache[0][0].shape[0]
+    c = fuse_context(feats, weights["fc"], weights["fc_norm"], shape.rms_eps, rb)
+    new = inject_kv(c, L + np.arange(c.shape[0]), weights["layers"], shape, rb)
+    return [(np.concatenate([k, nk]), np.concatenate([v, nv]))
+            for (k, v), (nk, nv) in zip(cache, new)]
