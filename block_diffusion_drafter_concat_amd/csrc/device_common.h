@@ -1,0 +1,145 @@
+// Device helpers shared by the gfx950 kernels: storage types, 16x16 MFMA
+// fragments, wave reductions, counters.
+//
+// Storage types: `float` (fp32 workloads) and `uint16_t` holding bf16 bit
+// patterns.  Both feed the same 16x16 MFMA tile shape:
+//   A fragment (16 rows x 32 k): lane l holds row l%16, k = (l/16)*8 .. +8
+//   B fragment (32 k x 16 cols): lane l holds col l%16, k = (l/16)*8 .. +8
+//   C (16 x 16 fp32):            lane l holds col l%16, rows (l/16)*4 .. +4
+// bf16 uses one v_mfma_f32_16x16x32_bf16 per 32-k step; fp32 uses eight
+// v_mfma_f32_16x16x4_f32, the i-th taking element i of every lane's 8, which
+// sums over the same 32 k values.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dflash {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest, ties to even.  NaN stays NaN (quiet bit set).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct Store;
+template <> struct Store<float> {
+  static __device__ __forceinline__ float load(float v) { return v; }
+  static __device__ __forceinline__ float make(float v) { return v; }
+};
+template <> struct Store<uint16_t> {
+  static __device__ __forceinline__ float load(uint16_t v) { return bf16_to_f32(v); }
+  static __device__ __forceinline__ uint16_t make(float v) { return f32_to_bf16(v); }
+};
+
+template <typename T> __device__ __forceinline__ float ldf(const T* p) {
+  return Store<T>::load(*p);
+}
+template <typename T> __device__ __forceinline__ void stf(T* p, float v) {
+  *p = Store<T>::make(v);
+}
+
+// Eight consecutive k values of one row.
+template <typename T> struct Frag8;
+template <> struct Frag8<uint16_t> { uint4 v; };
+template <> struct Frag8<float> { float4 lo, hi; };
+
+__device__ __forceinline__ void ld_frag(Frag8<uint16_t>& f, const uint16_t* p) {
+  f.v = *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ void ld_frag(Frag8<float>& f, const float* p) {
+  f.lo = *reinterpret_cast<const float4*>(p);
+  f.hi = *reinterpret_cast<const float4*>(p + 4);
+}
+__device__ __forceinline__ void zero_frag(Frag8<uint16_t>& f) { f.v = make_uint4(0, 0, 0, 0); }
+__device__ __forceinline__ void zero_frag(Frag8<float>& f) {
+  f.lo = make_float4(0.f, 0.f, 0.f, 0.f);
+  f.hi = f.lo;
+}
+
+__device__ __forceinline__ f32x4 mfma16(f32x4 acc, const Frag8<uint16_t>& a,
+                                        const Frag8<uint16_t>& b) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a.v),
+                                                 __builtin_bit_cast(bf16x8_t, b.v), acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(f32x4 acc, const Frag8<float>& a, const Frag8<float>& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.x, b.lo.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.y, b.lo.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.z, b.lo.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.w, b.lo.w, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.x, b.hi.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.y, b.hi.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.z, b.hi.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.w, b.hi.w, acc, 0, 0, 0);
+  return acc;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Wave-wide (64 lanes) reductions with a fixed butterfly order.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// (value, index) pair ordered by value, then by lower index.
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+// 64-bit key whose unsigned order is (value, then lower index).
+__device__ __forceinline__ unsigned long long argmax_key(float v, int idx) {
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<unsigned long long>(u) << 32) |
+         static_cast<unsigned long long>(0xffffffffu - static_cast<uint32_t>(idx));
+}
+__device__ __forceinline__ int argmax_key_index(unsigned long long k) {
+  return static_cast<int>(0xffffffffu - static_cast<uint32_t>(k & 0xffffffffull));
+}
+
+// Cos/sin of RoPE angle pos * theta^(-2i/d), formed in double, stored float.
+__device__ __forceinline__ void rope_cos_sin(int pos, int i, int d, double theta, float& c,
+                                             float& s) {
+  const double inv = pow(theta, -2.0 * static_cast<double>(i) / static_cast<double>(d));
+  const double ang = static_cast<double>(pos) * inv;
+  double sd, cd;
+  sincos(ang, &sd, &cd);
+  c = static_cast<float>(cd);
+  s = static_cast<float>(sd);
+}
+
+// Per-sequence bookkeeping passed by value to kernels.
+constexpr int kMaxBatch = 64;
+constexpr int kMaxLayers = 16;
+struct SeqTable {
+  int32_t len[kMaxBatch];     // committed context rows
+  int32_t row0[kMaxBatch];    // first input row of the sequence (inject)
+  int64_t off[kMaxBatch];     // start row of the sequence inside each head slab
+  int32_t pos0[kMaxBatch];    // position of the first written row (inject)
+  int32_t n;                  // sequences
+};
+
+// Which sequence an input row belongs to (rows grouped by sequence).
+__device__ __forceinline__ int seq_of_row(const SeqTable& t, int row) {
+  int b = 0;
+  for (int s = 1; s < t.n; ++s) b = (row >= t.row0[s]) ? s : b;
+  return b;
+}
+
+}  // namespace dflash

@@ -1,0 +1,233 @@
+// Epilogues of the weight-streaming GEMM.  Each one says which W rows make up
+// pair tile `tile` (rows(): the W row this lane streams for sub-tile 0 and 1)
+// and what to do with the pair of results (apply(): row m, column i of the
+// 16-wide sub-tiles).  tail() runs once per workgroup after all apply() calls.
+#pragma once
+
+#include "device_common.h"
+
+namespace dflash {
+
+// out[m, n] (float32) = A . W^T, 32 consecutive W rows per tile.
+template <typename T>
+struct EpiStoreF32 {
+  const T* W;
+  int K;
+  float* out;
+  int64_t ldo;
+  __device__ void rows(int tile, int r16, const T*& w0, const T*& w1) const {
+    w0 = W + static_cast<int64_t>(tile * 32 + r16) * K;
+    w1 = w0 + static_cast<int64_t>(16) * K;
+  }
+  __device__ void apply(int tile, int m, int i, bool valid, float v0, float v1) const {
+    if (!valid) return;
+    float* o = out + static_cast<int64_t>(m) * ldo + tile * 32 + i;
+    o[0] = v0;
+    o[16] = v1;
+  }
+  __device__ void tail(int, int, int) const {}
+};
+
+// Residual add: x[m, n] += A . W^T (O and down projections).
+template <typename T>
+struct EpiResidual {
+  const T* W;
+  int K;
+  float* x;
+  int64_t ldx;
+  __device__ void rows(int tile, int r16, const T*& w0, const T*& w1) const {
+    w0 = W + static_cast<int64_t>(tile * 32 + r16) * K;
+    w1 = w0 + static_cast<int64_t>(16) * K;
+  }
+  __device__ void apply(int tile, int m, int i, bool valid, float v0, float v1) const {
+    if (!valid) return;
+    float* o = x + static_cast<int64_t>(m) * ldx + tile * 32 + i;
+    o[0] += v0;
+    o[16] += v1;
+  }
+  __device__ void tail(int, int, int) const {}
+};
+
+// SwiGLU: h[m, j] = silu(u . wg[j]) * (u . wu[j]), stored in the handle type.
+template <typename T>
+struct EpiSwiGLU {
+  const T* wg;
+  const T* wu;
+  int K;
+  T* h;
+  int64_t ldh;
+  __device__ void rows(int tile, int r16, const T*& w0, const T*& w1) const {
+    w0 = wg + static_cast<int64_t>(tile * 16 + r16) * K;
+    w1 = wu + static_cast<int64_t>(tile * 16 + r16) * K;
+  }
+  __device__ void apply(int tile, int m, int i, bool valid, float g, float u) const {
+    if (!valid) return;
+    const float s = g / (1.0f + expf(-g));
+    stf(h + static_cast<int64_t>(m) * ldh + tile * 16 + i, s * u);
+  }
+  __device__ void tail(int, int, int) const {}
+};
+
+// Pair tiles of a K or Q projection: tile covers, for one head, columns
+// i0..i0+15 (sub-tile 0) and i0+D/2..i0+D/2+15 (sub-tile 1) -- the two members
+// of every RoPE pair land in the same thread.
+struct RopePairTile {
+  int head, i0;
+};
+__device__ __forceinline__ RopePairTile rope_pair_tile(int t, int d) {
+  const int per_head = d / 32;
+  return RopePairTile{t / per_head, (t % per_head) * 16};
+}
+
+// Block QKV projection of one layer: q (RoPE) -> q buffer; k (RoPE), v -> the
+// cache rows just past each sequence's committed context.
+template <typename T>
+struct EpiQKV {
+  const T* wq;
+  const T* wk;
+  const T* wv;
+  int K, d, Hq, Hkv, B;
+  T* q;
+  int64_t ldq;
+  T* kc;
+  T* vc;
+  int64_t cap;
+  const float2* rope;   // [m][d/2]
+  SeqTable seq;
+  __device__ int nq() const { return Hq * (d / 32); }
+  __device__ int nk() const { return Hkv * (d / 32); }
+  __device__ void rows(int tile, int r16, const T*& w0, const T*& w1) const {
+    if (tile < nq() + nk()) {
+      const bool is_q = tile < nq();
+      const RopePairTile pt = rope_pair_tile(is_q ? tile : tile - nq(), d);
+      const T* W = is_q ? wq : wk;
+      w0 = W + static_cast<int64_t>(pt.head * d + pt.i0 + r16) * K;
+      w1 = w0 + static_cast<int64_t>(d / 2) * K;
+    } else {
+      const int c0 = (tile - nq() - nk()) * 32;
+      w0 = wv + static_cast<int64_t>(c0 + r16) * K;
+      w1 = w0 + static_cast<int64_t>(16) * K;
+    }
+  }
+  __device__ void apply(int tile, int m, int i, bool valid, float v0, float v1) const {
+    if (!valid) return;
+    const int b = m / B, j = m % B;
+    const int64_t row = seq.off[b] + seq.len[b] + j;
+    if (tile < nq() + nk()) {
+      const bool is_q = tile < nq();
+      const RopePairTile pt = rope_pair_tile(is_q ? tile : tile - nq(), d);
+      const int c = pt.i0 + i;
+      const float2 cs = rope[static_cast<int64_t>(m) * (d / 2) + c];
+      const float o0 = v0 * cs.x - v1 * cs.y;
+      const float o1 = v1 * cs.x + v0 * cs.y;
+      T* dst = is_q ? q + static_cast<int64_t>(m) * ldq + pt.head * d
+                    : kc + (static_cast<int64_t>(pt.head) * cap + row) * d;
+      stf(dst + c, o0);
+      stf(dst + c + d / 2, o1);
+    } else {
+      const int ca = (tile - nq() - nk()) * 32 + i, cb = ca + 16;
+      stf(vc + (static_cast<int64_t>(ca / d) * d + ca % d) * cap + row, v0);
+      stf(vc + (static_cast<int64_t>(cb / d) * d + cb % d) * cap + row, v1);
+    }
+  }
+  __device__ void tail(int, int, int) const {}
+};
+
+// KV injection of context rows into every layer's cache: per layer, K pair
+// tiles (RoPE at the row's position) then plain V tiles.
+template <typename T>
+struct EpiInject {
+  const T* wk[kMaxLayers];
+  const T* wv[kMaxLayers];
+  T* kc[kMaxLayers];
+  T* vc[kMaxLayers];
+  int K, d, Hkv;
+  int64_t cap;
+  const float2* rope;   // [m][d/2] at each row's position
+  SeqTable seq;
+  __device__ int kt() const { return Hkv * (d / 32); }
+  __device__ void rows(int tile, int r16, const T*& w0, const T*& w1) const {
+    const int l = tile / (2 * kt()), t = tile % (2 * kt());
+    if (t < kt()) {
+      const RopePairTile pt = rope_pair_tile(t, d);
+      w0 = wk[l] + static_cast<int64_t>(pt.head * d + pt.i0 + r16) * K;
+      w1 = w0 + static_cast<int64_t>(d / 2) * K;
+    } else {
+      w0 = wv[l] + static_cast<int64_t>((t - kt()) * 32 + r16) * K;
+      w1 = w0 + static_cast<int64_t>(16) * K;
+    }
+  }
+  __device__ void apply(int tile, int m, int i, bool valid, float v0, float v1) const {
+    if (!valid) return;
+    const int l = tile / (2 * kt()), t = tile % (2 * kt());
+    const int b = seq_of_row(seq, m);
+    const int64_t row = seq.off[b] + seq.pos0[b] + (m - seq.row0[b]);
+    if (t < kt()) {
+      const RopePairTile pt = rope_pair_tile(t, d);
+      const int c = pt.i0 + i;
+      const float2 cs = rope[static_cast<int64_t>(m) * (d / 2) + c];
+      T* dst = kc[l] + (static_cast<int64_t>(pt.head) * cap + row) * d;
+      stf(dst + c, v0 * cs.x - v1 * cs.y);
+      stf(dst + c + d / 2, v1 * cs.x + v0 * cs.y);
+    } else {
+      const int ca = (t - kt()) * 32 + i, cb = ca + 16;
+      stf(vc[l] + (static_cast<int64_t>(ca / d) * d + ca % d) * cap + row, v0);
+      stf(vc[l] + (static_cast<int64_t>(cb / d) * d + cb % d) * cap + row, v1);
+    }
+  }
+  __device__ void tail(int, int, int) const {}
+};
+
+// LM head with fused argmax: logits never reach memory (unless dbg is set);
+// each workgroup folds its 32 columns into a 64-bit (value, lowest index) key
+// per row with atomicMax; the last workgroup to finish turns the keys of
+// slots 1..B-1 into draft ids (zhichai.net, "DFlash 的架构密码", 训练策略 3:
+// the drafter reads out through the target's own LM head).
+template <typename T>
+struct EpiLMHead {
+  const T* W;
+  int K, V, B, n_tiles;
+  unsigned long long* keys;   // [M], zero on entry
+  int* counter;               // zero on entry, one per launch
+  int32_t* draft;             // [M/B][B-1]
+  float* dbg;                 // [M][V] or null
+  __device__ void rows(int tile, int r16, const T*& w0, const T*& w1) const {
+    const int c0 = min(tile * 32 + r16, V - 1), c1 = min(tile * 32 + 16 + r16, V - 1);
+    w0 = W + static_cast<int64_t>(c0) * K;
+    w1 = W + static_cast<int64_t>(c1) * K;
+  }
+  __device__ void apply(int tile, int m, int i, bool valid, float v0, float v1) const {
+    const int c0 = tile * 32 + i, c1 = c0 + 16;
+    if (valid && dbg) {
+      if (c0 < V) dbg[static_cast<int64_t>(m) * V + c0] = v0;
+      if (c1 < V) dbg[static_cast<int64_t>(m) * V + c1] = v1;
+    }
+    float best = (c0 < V) ? v0 : -INFINITY;
+    int bi = c0;
+    if (c1 < V && v1 > best) { best = v1; bi = c1; }
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(best, o, 16);
+      const int oi = __shfl_xor(bi, o, 16);
+      if (better(ov, oi, best, bi)) { best = ov; bi = oi; }
+    }
+    if (valid && i == 0 && (m % B) != 0) atomicMax(&keys[m], argmax_key(best, bi));
+  }
+  __device__ void tail(int, int m0, int mc) const {
+    __shared__ int s_done;
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) s_done = (atomicAdd(counter, 1) == n_tiles - 1);
+    __syncthreads();
+    if (!s_done) return;
+    __threadfence();
+    for (int m = m0 + threadIdx.x; m < m0 + mc; m += 256) {
+      const int j = m % B;
+      if (j == 0) continue;
+      const unsigned long long k = atomicAdd(&keys[m], 0ull);
+      draft[(m / B) * (B - 1) + (j - 1)] = argmax_key_index(k);
+    }
+  }
+};
+
+}  // namespace dflash

@@ -1,0 +1,261 @@
+// Small memory-bound kernels of the drafter pass: block embedding, RMSNorm,
+// RoPE tables and greedy verification.
+#include "kernels.h"
+
+namespace dflash {
+
+// ------------------------------------------------------------------ zero
+__global__ __launch_bounds__(256) void zero_kernel(int* __restrict__ p, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    p[i] = 0;
+}
+
+hipError_t launch_zero(int* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int64_t g = (n + 255) / 256;
+  zero_kernel<<<static_cast<int>(g < 1024 ? g : 1024), 256, 0, st>>>(p, n);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ embed
+// One workgroup per block slot m = b*B + j.  Slot 0 of a block holds the anchor
+// (the previous cycle's bonus token), the others the mask token (zhichai.net,
+// "DFlash 的架构密码", 训练策略 1: every block starts at a verified token).
+// The shared target embedding supplies the rows (same page, 训练策略 3).
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ embed, int H, int V,
+                                                    const int32_t* __restrict__ anchors,
+                                                    int mask_id, int B, float* __restrict__ x,
+                                                    float2* __restrict__ rope, int d, double theta,
+                                                    SeqTable seq, uint32_t* __restrict__ zero,
+                                                    int64_t n_zero) {
+  const int m = blockIdx.x;
+  const int b = m / B, j = m % B;
+  // an anchor outside [0, V) is clamped into range rather than read out of bounds
+  const int tok = (j == 0) ? min(max(anchors[b], 0), V - 1) : mask_id;
+  const T* src = embed + static_cast<size_t>(tok) * H;
+  float* dst = x + static_cast<size_t>(m) * H;
+  for (int c = threadIdx.x; c < H; c += 256) dst[c] = ldf(src + c);
+  const int pos = seq.len[b] + j;
+  for (int i = threadIdx.x; i < d / 2; i += 256) {
+    float cs, sn;
+    rope_cos_sin(pos, i, d, theta, cs, sn);
+    rope[static_cast<size_t>(m) * (d / 2) + i] = make_float2(cs, sn);
+  }
+  for (int64_t w = static_cast<int64_t>(m) * 256 + threadIdx.x; w < n_zero;
+       w += static_cast<int64_t>(gridDim.x) * 256)
+    zero[w] = 0u;
+}
+
+hipError_t launch_embed(bool bf16, const void* embed, int H, int V, const int32_t* anchors, int mask_id,
+                        int batch, int B, float* x, float2* rope, int d, double theta,
+                        const SeqTable& seq, uint32_t* zero, int64_t n_zero, hipStream_t st) {
+  dim3 grid(batch * B), block(256);
+  if (bf16)
+    embed_kernel<uint16_t><<<grid, block, 0, st>>>(static_cast<const uint16_t*>(embed), H, V,
+                                                   anchors, mask_id, B, x, rope, d, theta, seq,
+                                                   zero, n_zero);
+  else
+    embed_kernel<float><<<grid, block, 0, st>>>(static_cast<const float*>(embed), H, V, anchors,
+                                                mask_id, B, x, rope, d, theta, seq, zero, n_zero);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ RMSNorm
+// y = x / sqrt(mean(x^2) + eps) * g (zhichai.net, "DFlash 的架构密码",
+// 技术细节补充 / 投影层 for the fusion norm; the same form for the layer norms).
+// One workgroup per row; float32 statistics with a fixed reduction order.
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int64_t ldx,
+                                                      const T* __restrict__ gain,
+                                                      T* __restrict__ out, int64_t ldo, int H,
+                                                      float eps) {
+  __shared__ float part[4];
+  const float* xr = x + static_cast<int64_t>(blockIdx.x) * ldx;
+  float ss = 0.f;
+  for (int c = threadIdx.x * 4; c < H; c += 1024) {
+    const float4 v = *reinterpret_cast<const float4*>(xr + c);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+  const float r = 1.0f / sqrtf(tot / static_cast<float>(H) + eps);
+  T* o = out + static_cast<int64_t>(blockIdx.x) * ldo;
+  for (int c = threadIdx.x * 4; c < H; c += 1024) {
+    const float4 v = *reinterpret_cast<const float4*>(xr + c);
+    stf(o + c + 0, v.x * r * ldf(gain + c + 0));
+    stf(o + c + 1, v.y * r * ldf(gain + c + 1));
+    stf(o + c + 2, v.z * r * ldf(gain + c + 2));
+    stf(o + c + 3, v.w * r * ldf(gain + c + 3));
+  }
+}
+
+hipError_t launch_rmsnorm(bool bf16, const float* x, int64_t ldx, const void* gain, void* out,
+                          int64_t ldo, int rows, int H, float eps, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (bf16)
+    rmsnorm_kernel<uint16_t><<<rows, 256, 0, st>>>(x, ldx, static_cast<const uint16_t*>(gain),
+                                                   static_cast<uint16_t*>(out), ldo, H, eps);
+  else
+    rmsnorm_kernel<float><<<rows, 256, 0, st>>>(x, ldx, static_cast<const float*>(gain),
+                                                static_cast<float*>(out), ldo, H, eps);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ RoPE rows
+__global__ __launch_bounds__(256) void rope_rows_kernel(float2* __restrict__ rope, int rows, int d,
+                                                        double theta, SeqTable seq) {
+  const int half = d / 2;
+  const int64_t n = static_cast<int64_t>(rows) * half;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
+       e += static_cast<int64_t>(gridDim.x) * 256) {
+    const int m = static_cast<int>(e / half), i = static_cast<int>(e % half);
+    const int b = seq_of_row(seq, m);
+    const int pos = seq.pos0[b] + (m - seq.row0[b]);
+    float cs, sn;
+    rope_cos_sin(pos, i, d, theta, cs, sn);
+    rope[e] = make_float2(cs, sn);
+  }
+}
+
+hipError_t launch_rope_rows(float2* rope, int rows, int d, double theta, const SeqTable& seq,
+                            hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t n = static_cast<int64_t>(rows) * (d / 2);
+  const int grid = static_cast<int>((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+  rope_rows_kernel<<<grid, 256, 0, st>>>(rope, rows, d, theta, seq);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ verify
+// Stage 1: workgroup (chunk, row) finds the largest logit of one 8192-column
+// chunk of one target row and its lowest column.  Stage 2: one wave per
+// sequence combines the chunks of its B rows and scans for the first draft
+// that disagrees (zhichai.net, "DFlash 的架构密码", 训练策略 1; ai-stack.site,
+// "DFlash：基于块扩散的闪存推测解码方法", 实践 2 and 实践 5).
+constexpr int kVerifyChunk = 8192;
+struct ArgPart {
+  float v;
+  int i;
+};
+
+template <typename T, bool kVec>
+__global__ __launch_bounds__(256) void verify_chunk_kernel(const T* __restrict__ logits, int V,
+                                                           ArgPart* __restrict__ part,
+                                                           int n_chunks) {
+  const int chunk = blockIdx.x, row = blockIdx.y;
+  const T* r = logits + static_cast<int64_t>(row) * V;
+  const int c0 = chunk * kVerifyChunk;
+  const int c1 = min(V, c0 + kVerifyChunk);
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+  constexpr int kPer = 16 / sizeof(T);
+  if (kVec) {
+    // every thread walks its columns in increasing order, so ">" keeps the lowest
+#pragma unroll 4
+    for (int c = c0 + threadIdx.x * kPer; c < c1; c += 256 * kPer) {
+      if (c + kPer <= c1) {
+        T buf[kPer];
+        *reinterpret_cast<uint4*>(buf) = *reinterpret_cast<const uint4*>(r + c);
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+          const float v = Store<T>::load(buf[e]);
+          if (v > best) { best = v; bi = c + e; }
+        }
+      } else {
+        for (int e = c; e < c1; ++e) {
+          const float v = ldf(r + e);
+          if (v > best) { best = v; bi = e; }
+        }
+      }
+    }
+  } else {
+    for (int c = c0 + threadIdx.x; c < c1; c += 256) {
+      const float v = ldf(r + c);
+      if (v > best) { best = v; bi = c; }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(best, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    if (better(ov, oi, best, bi)) { best = ov; bi = oi; }
+  }
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = best; si[threadIdx.x >> 6] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (better(sv[w], si[w], best, bi)) { best = sv[w]; bi = si[w]; }
+    part[static_cast<int64_t>(row) * n_chunks + chunk] = ArgPart{best, bi};
+  }
+}
+
+__global__ __launch_bounds__(64) void verify_scan_kernel(const ArgPart* __restrict__ part,
+                                                         int n_chunks, int B,
+                                                         const int32_t* __restrict__ drafts,
+                                                         int32_t* __restrict__ accept,
+                                                         int32_t* __restrict__ bonus) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  int t[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j >= B) { t[j] = 0; continue; }
+    float best = -INFINITY;
+    int bi = 0x7fffffff;
+    const ArgPart* p = part + static_cast<int64_t>(b * B + j) * n_chunks;
+    for (int c = lane; c < n_chunks; c += 64) {
+      const ArgPart q = p[c];
+      if (better(q.v, q.i, best, bi)) { best = q.v; bi = q.i; }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(best, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (better(ov, oi, best, bi)) { best = ov; bi = oi; }
+    }
+    t[j] = bi;
+  }
+  if (lane == 0) {
+    const int32_t* d = drafts + static_cast<int64_t>(b) * (B - 1);
+    int a = 0;
+    while (a < B - 1 && t[a] == d[a]) ++a;
+    int bon = t[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) bon = (j == a) ? t[j] : bon;
+    accept[b] = a;
+    bonus[b] = bon;
+  }
+}
+
+size_t verify_ws_bytes(int batch, int B, int V) {
+  const size_t n_chunks = (static_cast<size_t>(V) + kVerifyChunk - 1) / kVerifyChunk;
+  return static_cast<size_t>(batch) * B * n_chunks * sizeof(ArgPart);
+}
+
+hipError_t launch_verify(const void* logits, bool bf16, const int32_t* drafts, int batch, int B,
+                         int V, int32_t* accept, int32_t* bonus, void* ws, hipStream_t st) {
+  const int n_chunks = (V + kVerifyChunk - 1) / kVerifyChunk;
+  ArgPart* part = static_cast<ArgPart*>(ws);
+  dim3 grid(n_chunks, batch * B);
+  const bool vec = (static_cast<size_t>(V) * (bf16 ? 2 : 4)) % 16 == 0;
+  if (bf16) {
+    auto p = static_cast<const uint16_t*>(logits);
+    if (vec) verify_chunk_kernel<uint16_t, true><<<grid, 256, 0, st>>>(p, V, part, n_chunks);
+    else verify_chunk_kernel<uint16_t, false><<<grid, 256, 0, st>>>(p, V, part, n_chunks);
+  } else {
+    auto p = static_cast<const float*>(logits);
+    if (vec) verify_chunk_kernel<float, true><<<grid, 256, 0, st>>>(p, V, part, n_chunks);
+    else verify_chunk_kernel<float, false><<<grid, 256, 0, st>>>(p, V, part, n_chunks);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  verify_scan_kernel<<<batch, 64, 0, st>>>(part, n_chunks, B, drafts, accept, bonus);
+  return hipGetLastError();
+}
+
+}  // namespace dflash

@@ -1,0 +1,36 @@
+// Host-side launchers of the gfx950 kernels (internal to libdflash.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "device_common.h"
+
+namespace dflash {
+
+// ---------------------------------------------------------------- small kernels
+// Clear n 32-bit words (a fill kernel, so the call stays graph-capturable).
+hipError_t launch_zero(int* p, int64_t n, hipStream_t st);
+
+// Block inputs: x[m] = embed[token(m)] (fp32), RoPE cos/sin of every block slot
+// at position seq.len[b] + j, and `n_zero` 32-bit words of `zero` cleared.
+hipError_t launch_embed(bool bf16, const void* embed, int H, int V, const int32_t* anchors,
+                        int mask_id, int batch, int B, float* x, float2* rope, int d,
+                        double theta, const SeqTable& seq, uint32_t* zero, int64_t n_zero,
+                        hipStream_t st);
+
+// out[r] = x[r] / sqrt(mean(x[r]^2) + eps) * gain, stored in the handle type.
+hipError_t launch_rmsnorm(bool bf16, const float* x, int64_t ldx, const void* gain, void* out,
+                          int64_t ldo, int rows, int H, float eps, hipStream_t st);
+
+// RoPE cos/sin of inject rows: row m of sequence b sits at seq.pos0[b] + m - seq.row0[b].
+hipError_t launch_rope_rows(float2* rope, int rows, int d, double theta, const SeqTable& seq,
+                            hipStream_t st);
+
+// Greedy verify: per-chunk row argmax, then per-sequence prefix scan.
+size_t verify_ws_bytes(int batch, int B, int V);
+hipError_t launch_verify(const void* logits, bool bf16, const int32_t* drafts, int batch, int B,
+                         int V, int32_t* accept, int32_t* bonus, void* ws, hipStream_t st);
+
+}  // namespace dflash

@@ -1,0 +1,208 @@
+/*
+ * dflash.h -- C ABI of the MI355X (gfx950) drafter hot path for block-diffusion
+ * speculative decoding (DFlash).
+ *
+ * The drafter turns target hidden states into a draft block in one forward
+ * pass and the target's logits into an accepted length.  Four calls carry the
+ * work, in the order a speculative cycle uses them:
+ *
+ *   dflash_fuse_context   hidden states of the sampled target layers -> compact
+ *                         context feature (zhichai.net, "DFlash 的架构密码",
+ *                         第一层 Feature Fusion; 技术细节补充 / 投影层).
+ *   dflash_inject_kv      context feature -> K and V of every drafter layer's
+ *                         cache (same page, 第二层 KV Injection).
+ *   dflash_draft_block    one forward pass over a block [anchor, mask, ...]
+ *                         -> B-1 draft tokens per sequence (same page, 第三层
+ *                         Block Diffusion; 训练策略 1 and 3; 技术细节补充 /
+ *                         稀疏注意力训练).
+ *   dflash_verify_greedy  target logits of the block -> accepted draft count
+ *                         and bonus token (same page, 训练策略 1; ai-stack.site,
+ *                         "DFlash：基于块扩散的闪存推测解码方法", 实践 2).
+ *
+ * Conventions shared by every call
+ *   - Pointers marked (device) are HIP device memory; (host) is host memory.
+ *     All buffers belong to the caller.  The library never allocates device
+ *     memory: scratch comes from the caller's workspace `ws`, sized by
+ *     dflash_workspace_size, 256-byte aligned.  One workspace serves one stream.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and never synchronises it, so a call may be captured
+ *     into a HIP graph.
+ *   - Arguments are checked on the host before anything is enqueued; a failing
+ *     call returns a status and has changed nothing.  A failed launch returns
+ *     DFLASH_ERR_HIP.  No C++ exception crosses this interface.
+ *   - Storage type: every weight, feature, cache and activation tensor of a
+ *     handle has the handle's dtype (float32 or bf16 bit patterns); residual
+ *     stream, statistics, softmax and logits are float32 in every case.
+ *   - Matrices are row-major, `nn.Linear` layout [out_features, in_features].
+ *   - Device pointers must be 16-byte aligned.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DFLASH_MAX_BATCH 64      /* sequences per call */
+#define DFLASH_MAX_BLOCK 16      /* block slots B, anchor included */
+#define DFLASH_MAX_LAYERS 16     /* drafter layers */
+#define DFLASH_MAX_FEAT 6        /* fused target layers */
+
+typedef enum {
+  DFLASH_OK = 0,
+  DFLASH_ERR_INVALID_ARG = 1,  /* null pointer, bad size, misaligned pointer */
+  DFLASH_ERR_CAPACITY = 2,     /* a cache write would pass a sequence's capacity */
+  DFLASH_ERR_UNSUPPORTED = 3,  /* shape the kernels do not cover (see dflash_config) */
+  DFLASH_ERR_HIP = 4           /* a HIP runtime call or launch failed */
+} dflash_status;
+
+typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
+
+/* Drafter shape.  Supported: head_dim 64 or 128; hidden, ffn, n_q_heads*head_dim
+ * multiples of 128; n_q_heads a multiple of n_kv_heads with
+ * (n_q_heads/n_kv_heads) * block_size <= 128; n_feat_layers 1..6;
+ * 1 <= n_layers <= 16; mask_token_id in [0, vocab). */
+typedef struct {
+  int32_t n_layers;
+  int32_t hidden;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t ffn;
+  int32_t vocab;
+  int32_t n_feat_layers;
+  int32_t mask_token_id;
+  float rms_eps;       /* RMSNorm epsilon, e.g. 1e-6 */
+  float rope_theta;    /* RoPE base, e.g. 1e6 */
+  dflash_dtype dtype;
+} dflash_config;
+
+/* One decoder layer (device pointers, handle dtype).  Shapes with H = hidden,
+ * Q = n_q_heads*head_dim, KV = n_kv_heads*head_dim, F = ffn:
+ * attn_norm, ffn_norm [H]; wq [Q,H]; wk, wv [KV,H]; wo [H,Q]; wg, wu [F,H];
+ * wd [H,F]. */
+typedef struct {
+  const void *attn_norm, *wq, *wk, *wv, *wo, *ffn_norm, *wg, *wu, *wd;
+} dflash_layer_weights;
+
+/* All weights.  fc [H, n_feat*H] (column block i multiplies the hidden state
+ * of the i-th fused layer, ascending layer id), fc_norm [H], final_norm [H],
+ * embed [V,H] and lm_head [V,H] (the target's own; they may alias).
+ * `layers` is a host array of n_layers entries.  The handle copies the
+ * pointers; the memory they point to must outlive the handle. */
+typedef struct {
+  const void *fc, *fc_norm;
+  const dflash_layer_weights *layers;
+  const void *final_norm, *embed, *lm_head;
+} dflash_weights;
+
+/* The drafter's KV cache for a batch of sequences (caller-owned).
+ *   k[l] (device) [n_kv_heads][cap_total][head_dim]  keys of layer l, RoPE applied
+ *   v[l] (device) [n_kv_heads][head_dim][cap_total]  values of layer l, transposed
+ * Sequence b owns rows [seq_off[b], seq_off[b] + seq_cap[b]) of the position
+ * axis; its committed context is the first seq_len[b] of them.  seq_off and
+ * seq_cap must be multiples of 32 and the ranges must not overlap.
+ * dflash_draft_block uses rows [seq_len[b], seq_len[b] + B) of each sequence as
+ * scratch for the block's own K/V, so seq_cap[b] >= seq_len[b] + B is needed
+ * there; those rows hold nothing committed.  dflash_inject_kv updates the host
+ * array seq_len. */
+typedef struct {
+  void *const *k;            /* (host) array [n_layers] of device pointers */
+  void *const *v;            /* (host) array [n_layers] of device pointers */
+  int32_t batch;
+  int64_t cap_total;         /* position rows in each head slab */
+  const int64_t *seq_off;    /* (host) [batch] */
+  const int32_t *seq_cap;    /* (host) [batch] */
+  int32_t *seq_len;          /* (host) [batch] */
+} dflash_kv;
+
+typedef struct dflash_handle dflash_handle;
+
+/* 1-based ids of the n_select target layers whose hidden states are fused:
+ * spread uniformly from layer 2 to the third-from-last layer, a grid point
+ * half-way between two layers rounding up (zhichai.net, "DFlash 的架构密码",
+ * 技术细节补充 / 提取层数).  Writes n_select ids to out (host) and returns
+ * n_select, or -1 if n_select < 2, n_select > DFLASH_MAX_FEAT,
+ * n_target_layers < n_select + 3 or out is NULL. */
+int32_t dflash_target_layer_ids(int32_t n_target_layers, int32_t n_select, int32_t *out);
+
+/* Validate a config and weights and make a handle (host memory only). */
+dflash_status dflash_create(const dflash_config *cfg, const dflash_weights *w,
+                            dflash_handle **out);
+dflash_status dflash_destroy(dflash_handle *h);
+
+/* Bytes of workspace that every call below needs for batches up to max_batch,
+ * blocks up to max_block slots and fuse/inject calls of up to max_tokens rows. */
+dflash_status dflash_workspace_size(const dflash_handle *h, int32_t max_batch,
+                                    int32_t max_block, int64_t max_tokens, size_t *bytes);
+
+/* Compact context feature c = RMSNorm(concat(feats) . fc^T) * fc_norm.
+ *   feats    (host) array [n_feat_layers] of device pointers, each [n_tokens, H]
+ *   ctx_out  (device) [n_tokens, H], handle dtype (bf16: rounded to nearest even)
+ * Feature fusion: zhichai.net, "DFlash 的架构密码", 第一层 Feature Fusion and
+ * 技术细节补充 / 投影层 (light FC then RMSNorm, no bias). */
+dflash_status dflash_fuse_context(dflash_handle *h, const void *const *feats, int64_t n_tokens,
+                                  void *ctx_out, void *ws, void *stream);
+
+/* Write the K and V that context features contribute to every drafter layer.
+ * For each sequence b, rows [pos_start[b], pos_start[b] + n_new[b]) of its
+ * cache receive K = RoPE(c . wk^T) at those positions and V = c . wv^T, for
+ * every layer, from the next n_new[b] rows of ctx (rows of sequence 0 first).
+ * Then seq_len[b] = pos_start[b] + n_new[b]: rows past it are dropped, which is
+ * how a caller rewinds.  pos_start == NULL appends (pos_start[b] = seq_len[b]).
+ *   ctx       (device) [sum n_new, H]
+ *   pos_start (host) [batch] or NULL, each 0 <= pos_start[b] <= seq_len[b]
+ *   n_new     (host) [batch], each >= 0
+ * DFLASH_ERR_CAPACITY if pos_start[b] + n_new[b] > seq_cap[b].
+ * KV injection: zhichai.net, "DFlash 的架构密码", 第二层 KV Injection (the
+ * feature enters every layer's K and V projection, not the input embedding). */
+dflash_status dflash_inject_kv(dflash_handle *h, const void *ctx, const int32_t *pos_start,
+                               const int32_t *n_new, dflash_kv *kv, void *ws, void *stream);
+
+/* One forward pass of the drafter over one block per sequence.  Slot 0 holds
+ * the anchor (the bonus token of the previous cycle), slots 1..B-1 the mask
+ * token; slot j sits at position seq_len[b] + j.  Inside a block every slot
+ * attends to every slot; a block also sees its own sequence's committed
+ * context and nothing else.  Draft j is the lowest-index argmax of slot j's
+ * logits through the shared LM head.
+ *   anchor_ids        (device) int32 [batch]
+ *   draft_ids         (device) int32 [batch, B-1]
+ *   dbg_final_hidden  (device) float [batch*B, H] or NULL: residual stream after
+ *                     the last layer
+ *   dbg_logits        (device) float [batch*B, V] or NULL
+ * DFLASH_ERR_CAPACITY if seq_len[b] + B > seq_cap[b] for some b.
+ * zhichai.net, "DFlash 的架构密码": 第三层 Block Diffusion (one step, one
+ * forward pass per block), 训练策略 1 (blocks start at the verified bonus
+ * token), 训练策略 3 (shared embedding and LM head), 技术细节补充 / 稀疏注意力
+ * 训练 (bidirectional inside a block, no flow between blocks). */
+dflash_status dflash_draft_block(dflash_handle *h, dflash_kv *kv, int32_t block_size,
+                                 const int32_t *anchor_ids, int32_t *draft_ids,
+                                 float *dbg_final_hidden, float *dbg_logits, void *ws,
+                                 void *stream);
+
+/* Greedy verification of one block per sequence.  t_j = lowest-index argmax of
+ * target row j; accept[b] = the largest a <= B-1 with t_j == draft[b][j] for
+ * all j < a; bonus[b] = t_a.  a + 1 tokens are committed (anchor and a drafts)
+ * and the bonus token anchors the next block.
+ *   target_logits (device) [batch, B, vocab] in `dtype`
+ *   draft_ids     (device) int32 [batch, B-1]
+ *   accept, bonus (device) int32 [batch]
+ *   ws            (device) at least dflash_verify_workspace_size bytes
+ * Inputs must be finite.  zhichai.net, "DFlash 的架构密码", 训练策略 1;
+ * ai-stack.site, "DFlash：基于块扩散的闪存推测解码方法", 实践 2 (keep up to the
+ * last correct token) and 实践 5 (verification stays in a GPU kernel). */
+dflash_status dflash_verify_greedy(const void *target_logits, dflash_dtype dtype,
+                                   const int32_t *draft_ids, int32_t batch, int32_t block_size,
+                                   int32_t vocab, int32_t *accept, int32_t *bonus, void *ws,
+                                   void *stream);
+size_t dflash_verify_workspace_size(int32_t batch, int32_t block_size, int32_t vocab);
+
+const char *dflash_status_string(dflash_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH_H */

@@ -1,0 +1,84 @@
+"""Shared set-up of the GPU parity tests: seeded inputs go to both sides."""
+from __future__ import annotations
+
+import numpy as np
+
+from block_diffusion_drafter_concat_amd import configs, synth
+from block_diffusion_drafter_concat_amd import lib as L
+
+
+def rel_err(got, want) -> float:
+    """Per-tensor max relative error: max|g - o| / max|o|."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    return float(np.max(np.abs(got - want)) / max(np.max(np.abs(want)), 1e-30))
+
+
+def tol(shape) -> float:
+    return 1e-4 if shape.dtype == "f32" else 2e-2
+
+
+def dev(a, dtype):
+    return L.to_device(a, dtype)
+
+
+def to_np(t):
+    import torch
+    return t.detach().to(torch.float32).cpu().numpy()
+
+
+def feats_dev(feats, dtype):
+    return [dev(f, dtype) for f in feats]
+
+
+def upload_cache(cache: "L.KVCache", caches_np):
+    """Write per-sequence (K, V) [L_b, Hkv, d] into the device cache layout."""
+    import torch
+    for b, per_layer in enumerate(caches_np):
+        o = int(cache.offs[b])
+        for l, (k, v) in enumerate(per_layer):
+            n = k.shape[0]
+            dt = cache.k[l].dtype
+            kt = torch.from_numpy(np.ascontiguousarray(k, dtype=np.float32)).to(dt)
+            vt = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(dt)
+            cache.k[l][:, o:o + n, :] = kt.permute(1, 0, 2).cuda()
+            cache.v[l][:, :, o:o + n] = vt.permute(1, 2, 0).cuda()
+        cache.seq_len[b] = per_layer[0][0].shape[0]
+
+
+def synthetic_cache(shape, wid, lens, std=1.28):
+    """Context K/V drawn directly (bf16/f32 values), per sequence and layer."""
+    out = []
+    for b, n in enumerate(lens):
+        per = []
+        for l in range(shape.n_layers):
+            k = synth.values((n, shape.n_kv_heads, shape.head_dim), shape.dtype, wid,
+                             synth.STREAM_FEATURES, f"cacheK{b}.{l}", std=std)
+            v = synth.values((n, shape.n_kv_heads, shape.head_dim), shape.dtype, wid,
+                             synth.STREAM_FEATURES, f"cacheV{b}.{l}", std=std)
+            per.append((k, v))
+        out.append(per)
+    return out
+
+
+def draft_compare(shape, res, ids_gpu, hid_gpu, z_gpu, label=""):
+    """Draft ids bit-exact outside the top-2 gap exemption; floats within tol."""
+    t = tol(shape)
+    e_h = rel_err(hid_gpu, res["final_hidden"].reshape(hid_gpu.shape))
+    e_z = rel_err(z_gpu, res["logits"].reshape(z_gpu.shape))
+    want = res["draft_ids"]
+    ok = res["gap"] >= 1e-2
+    mism = (ids_gpu != want) & ok
+    info = (f"{label} final_hidden rel {e_h:.2e}, logits rel {e_z:.2e}, "
+            f"exempt {int((~ok).sum())}/{ok.size}, mismatches {int(mism.sum())}")
+    print(info, flush=True)
+    assert e_h <= t, info
+    assert e_z <= t, info
+    assert not mism.any(), info
+    return e_h, e_z
+
+
+def small_bf16_shape():
+    """bf16 drafter with every dimension spanning several tiles and a ragged vocab."""
+    return configs.DrafterShape(n_layers=2, hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                                ffn=1536, vocab=5003, dtype="bf16")

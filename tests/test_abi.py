@@ -1,0 +1,178 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects bad arguments on the host before anything is enqueued."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from block_diffusion_drafter_concat_amd import configs
+from block_diffusion_drafter_concat_amd import lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH),
+                                reason="libdflash.so not built (run __graft_entry__.build())")
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "dflash.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = L.load()
+    names = _declared_functions()
+    assert set(names) == set(L.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_layer_ids_match_oracle():
+    for n in (5, 6):
+        for depth in range(n + 3, 130):
+            assert L.target_layer_ids(depth, n) == O.target_layer_ids(depth, n)
+    lib = L.load()
+    out = (C.c_int32 * 8)()
+    assert lib.dflash_target_layer_ids(7, 5, out) == -1
+    assert lib.dflash_target_layer_ids(40, 1, out) == -1
+    assert lib.dflash_target_layer_ids(40, 7, out) == -1
+    assert lib.dflash_target_layer_ids(40, 5, None) == -1
+
+
+# fake but aligned device addresses: create() only records them
+_FAKE = 1 << 40
+
+
+def _fake_weights(shape, misalign=None):
+    ptr = iter(range(_FAKE, _FAKE + 4096 * 64, 4096))
+    layers = (L.LayerWeights * shape.n_layers)(*[
+        L.LayerWeights(*[next(ptr) for _ in range(9)]) for _ in range(shape.n_layers)])
+    w = L.Weights(next(ptr), next(ptr), layers, next(ptr), next(ptr), next(ptr))
+    if misalign == "fc":
+        w.fc += 2
+    return w, layers
+
+
+def _cfg(shape, **kw):
+    c = L.Config(shape.n_layers, shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
+                 shape.ffn, shape.vocab, shape.n_feat, shape.mask_token_id, shape.rms_eps,
+                 shape.rope_theta, L.BF16 if shape.dtype == "bf16" else L.F32)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def _create(shape, **kw):
+    lib = L.load()
+    w, keep = _fake_weights(shape, kw.pop("misalign", None))
+    cfg = _cfg(shape, **kw)
+    h = C.c_void_p()
+    st = lib.dflash_create(C.byref(cfg), C.byref(w), C.byref(h))
+    return st, h, (w, keep)
+
+
+@pytest.mark.parametrize("shape", [configs.TINY_F32, configs.QWEN3_8B_LIKE, configs.TARGET_27B_LIKE])
+def test_create_accepts_the_workload_shapes(shape):
+    st, h, _ = _create(shape)
+    assert st == L.OK
+    n = C.c_size_t()
+    assert L.load().dflash_workspace_size(h, 16, 16, 4096, C.byref(n)) == L.OK
+    assert n.value > 0
+    assert L.load().dflash_destroy(h) == L.OK
+
+
+@pytest.mark.parametrize("field,value,want", [
+    ("head_dim", 96, L.ERR_UNSUPPORTED),
+    ("hidden", 200, L.ERR_UNSUPPORTED),
+    ("n_layers", 0, L.ERR_INVALID_ARG),
+    ("n_layers", 17, L.ERR_INVALID_ARG),
+    ("n_feat_layers", 7, L.ERR_INVALID_ARG),
+    ("mask_token_id", 1024, L.ERR_INVALID_ARG),
+    ("n_kv_heads", 3, L.ERR_UNSUPPORTED),
+    ("rms_eps", 0.0, L.ERR_INVALID_ARG),
+    ("dtype", 7, L.ERR_INVALID_ARG),
+])
+def test_create_rejects_bad_config(field, value, want):
+    st, h, _ = _create(configs.TINY_F32, **{field: value})
+    assert st == want and not h.value
+
+
+def test_create_rejects_misaligned_weight():
+    st, h, _ = _create(configs.TINY_F32, misalign="fc")
+    assert st == L.ERR_INVALID_ARG and not h.value
+
+
+def _kv(shape, lens, caps, offs=None):
+    caps = np.array(caps, dtype=np.int32)
+    offs = np.concatenate([[0], np.cumsum(caps)[:-1]]).astype(np.int64) if offs is None else \
+        np.array(offs, dtype=np.int64)
+    lens = np.array(lens, dtype=np.int32)
+    k = (C.c_void_p * shape.n_layers)(*[_FAKE + i * 4096 for i in range(shape.n_layers)])
+    v = (C.c_void_p * shape.n_layers)(*[_FAKE + (64 + i) * 4096 for i in range(shape.n_layers)])
+    kv = L.KV(k, v, len(lens), int(caps.sum()), offs.ctypes.data_as(C.POINTER(C.c_int64)),
+              caps.ctypes.data_as(C.POINTER(C.c_int32)), lens.ctypes.data_as(C.POINTER(C.c_int32)))
+    return kv, (k, v, caps, offs, lens)
+
+
+def test_draft_and_inject_host_checks():
+    lib = L.load()
+    shape = configs.TINY_F32
+    st, h, keep = _create(shape)
+    assert st == L.OK
+    ws = C.c_void_p(_FAKE)
+    ids = C.c_void_p(_FAKE + 256)
+    # capacity: len + B > cap
+    kv, k1 = _kv(shape, [60], [64])
+    assert lib.dflash_draft_block(h, C.byref(kv), 8, ids, ids, None, None, ws, None) == L.ERR_CAPACITY
+    # block size out of range
+    kv, k2 = _kv(shape, [10], [64])
+    for B in (1, 17):
+        assert lib.dflash_draft_block(h, C.byref(kv), B, ids, ids, None, None, ws, None) == \
+            L.ERR_INVALID_ARG
+    # null outputs
+    assert lib.dflash_draft_block(h, C.byref(kv), 8, None, ids, None, None, ws, None) == \
+        L.ERR_INVALID_ARG
+    # offsets not multiples of 32, overlapping sequences
+    kv, k3 = _kv(shape, [1, 1], [64, 64], offs=[0, 48])
+    assert lib.dflash_draft_block(h, C.byref(kv), 8, ids, ids, None, None, ws, None) == \
+        L.ERR_INVALID_ARG
+    kv, k4 = _kv(shape, [1, 1], [64, 64], offs=[0, 32])
+    assert lib.dflash_draft_block(h, C.byref(kv), 8, ids, ids, None, None, ws, None) == \
+        L.ERR_INVALID_ARG
+    # inject: past capacity, and a start beyond the committed length
+    kv, k5 = _kv(shape, [10], [64])
+    n_new = (C.c_int32 * 1)(60)
+    assert lib.dflash_inject_kv(h, ids, None, n_new, C.byref(kv), ws, None) == L.ERR_CAPACITY
+    pos = (C.c_int32 * 1)(11)
+    n_new = (C.c_int32 * 1)(1)
+    assert lib.dflash_inject_kv(h, ids, pos, n_new, C.byref(kv), ws, None) == L.ERR_INVALID_ARG
+    assert k5[4][0] == 10          # rejected calls leave seq_len alone
+    # a zero-row inject only moves seq_len (rewind), without touching the device
+    pos = (C.c_int32 * 1)(4)
+    n_new = (C.c_int32 * 1)(0)
+    assert lib.dflash_inject_kv(h, None, pos, n_new, C.byref(kv), ws, None) == L.OK
+    assert k5[4][0] == 4
+    assert lib.dflash_destroy(h) == L.OK
+
+
+def test_fuse_and_verify_host_checks():
+    lib = L.load()
+    st, h, keep = _create(configs.TINY_F32)
+    feats = (C.c_void_p * 5)(*[_FAKE + i * 4096 for i in range(5)])
+    out = C.c_void_p(_FAKE)
+    assert lib.dflash_fuse_context(h, feats, -1, out, out, None) == L.ERR_INVALID_ARG
+    assert lib.dflash_fuse_context(h, None, 4, out, out, None) == L.ERR_INVALID_ARG
+    bad = (C.c_void_p * 5)(*[_FAKE + i * 4096 + (2 if i == 3 else 0) for i in range(5)])
+    assert lib.dflash_fuse_context(h, bad, 4, out, out, None) == L.ERR_INVALID_ARG
+    assert lib.dflash_fuse_context(h, feats, 0, out, out, None) == L.OK   # nothing to do
+    p = C.c_void_p(_FAKE)
+    assert lib.dflash_verify_greedy(p, 0, p, 1, 1, 10, p, p, p, None) == L.ERR_INVALID_ARG
+    assert lib.dflash_verify_greedy(p, 5, p, 1, 8, 10, p, p, p, None) == L.ERR_INVALID_ARG
+    assert lib.dflash_verify_greedy(None, 0, p, 1, 8, 10, p, p, p, None) == L.ERR_INVALID_ARG
+    assert lib.dflash_verify_workspace_size(16, 16, 151936) >= 16 * 16 * 8
+    assert L.status_string(L.ERR_CAPACITY) == "cache capacity exceeded"
+    lib.dflash_destroy(h)
