@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Draft-block throughput of the DFlash drafter hot path on one MI355X.
+
+Workload: Qwen3-8B-shaped bf16 drafter (5 layers, hidden 4096, 32/8 heads of
+128, SwiGLU 12288, shared embedding / LM head over 151936 tokens), batch 1,
+context 2048, blocks of 16 slots.  Synthetic seeded weights and inputs.
+
+One step = the drafter's share of one speculative cycle, every row of the hot
+path once:
+  fuse the target features of the n tokens committed last cycle (n ~ accept
+  length, Geometric(0.15) capped at 16) -> inject them into every layer's
+  cache at positions 2048-n .. 2047 (the context stays 2048) -> draft one
+  16-slot block in one forward pass -> greedy-verify it against synthetic
+  target logits.  The bonus token of step i anchors step i+1 on the device.
+
+Prints one JSON line: blocks/s, the dominant kernel's roofline figures
+(measured live with HIP events on the library's stream) and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "draft blocks/s (16-tok, 5-layer drafter, ctx 2048) + % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+CTX, BLOCK, BATCH = 2048, 16, 1
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def step_bytes(shape, n_new: int) -> dict:
+    """Algorithmic HBM bytes of one step (each tensor read or written once)."""
+    H, V, L = shape.hidden, shape.vocab, shape.n_layers
+    s = 2
+    layer_w = shape.layer_params() * s
+    lm = V * H * s
+    kv = (CTX + BLOCK) * shape.kv_dim * 2 * s * L
+    fuse = shape.n_feat * H * H * s + shape.n_feat * n_new * H * s + n_new * H * s
+    inject = L * 2 * shape.kv_dim * H * s + n_new * H * s + L * 2 * n_new * shape.kv_dim * s
+    verify = BLOCK * V * s
+    return {"layers": L * layer_w, "lm_head": lm, "kv": kv, "fuse": fuse, "inject": inject,
+            "verify": verify, "embed": BLOCK * H * s}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from block_diffusion_drafter_concat_amd import configs, synth
+    from block_diffusion_drafter_concat_amd import lib as L
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    L.load()
+    shape = configs.QWEN3_8B_LIKE
+    wid = 2
+    K, W = args.steps, args.warmup
+
+    t0 = time.time()
+    w = configs.make_weights(shape, wid)
+    dr = L.Drafter(shape, w)
+    log(f"weights ready in {time.time() - t0:.1f}s")
+
+    # prefill (untimed): fuse and inject the 2048-token context
+    feats = configs.make_features(shape, wid, CTX)
+    cache = L.KVCache(shape, [CTX + 64])
+    ws = dr.workspace(BATCH, BLOCK, CTX)
+    ctx_all = torch.empty((CTX, shape.hidden), dtype=torch.bfloat16, device="cuda")
+    dr.fuse_context([L.to_device(f, "bf16") for f in feats], ctx_all, ws)
+    dr.inject_kv(ctx_all, [CTX], cache, ws)
+    del ctx_all
+
+    # per-step inputs
+    n_steps = W + K
+    tau = synth.geometric_capped(n_steps, 0.15, BLOCK, wid, synth.STREAM_INDICES, "bench_tau")
+    new_feats = [L.to_device(f, "bf16") for f in
+                 configs.make_features(shape, wid, BLOCK, name="bench_new")]
+    rand_drafts = synth.integers((BATCH, BLOCK - 1), 0, shape.vocab - 2, wid,
+                                 synth.STREAM_LOGITS, "bench_drafts")
+    logits_np = synth.plant_target_logits(
+        synth.values((BATCH, BLOCK, shape.vocab), "bf16", wid, synth.STREAM_LOGITS, "bench_lg"),
+        rand_drafts, np.array([int(tau[0]) - 1]), "bf16", workload=wid)
+    logits = L.to_device(logits_np.reshape(BATCH * BLOCK, -1), "bf16").reshape(
+        BATCH, BLOCK, shape.vocab)
+    ctx_new = torch.empty((BLOCK, shape.hidden), dtype=torch.bfloat16, device="cuda")
+    anchor = torch.from_numpy(configs.make_anchors(shape, wid, BATCH)).cuda()
+    draft = torch.empty((BATCH, BLOCK - 1), dtype=torch.int32, device="cuda")
+    accept = torch.empty(BATCH, dtype=torch.int32, device="cuda")
+    vws = torch.empty(L.verify_workspace_size(BATCH, BLOCK, shape.vocab), dtype=torch.uint8,
+                      device="cuda")
+
+    def step(i, verify_events=None):
+        n = int(tau[i])
+        dr.fuse_context([f[:n] for f in new_feats], ctx_new, ws)
+        dr.inject_kv(ctx_new, [n], cache, ws, pos_start=[CTX - n])
+        dr.draft_block(cache, BLOCK, anchor, draft, ws)
+        if verify_events:
+            verify_events[0].record()
+        L.verify_greedy(logits, draft, accept, anchor, vws)   # bonus -> next anchor
+        if verify_events:
+            verify_events[1].record()
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, eager launches on the current stream
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record()
+    for i in range(W, W + K):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = gpu_ms / K
+    blocks_per_s = BATCH * K / (gpu_ms / 1e3)
+    log(f"timed: {K} steps, {ms_per_step:.3f} ms/step (wall {wall * 1e3 / K:.3f} ms/step)")
+
+    # ---- kernel-timing pass: HIP events around each section, same steps
+    sections = [("lm_head", -1), ("fuse_gemm", -1), ("inject", -1), ("embed", -1),
+                ("final_norm", -1)]
+    for l in range(shape.n_layers):
+        sections += [("qkv", l), ("attention", l), ("o_proj", l), ("gate_up", l), ("down", l)]
+    per_step = []
+    for i in range(K):
+        pts = []
+        for s, l in sections:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            b.record()
+            pts.append((s, l, a, b))
+        ve = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        per_step.append((pts, ve))
+    torch.cuda.synchronize()
+    for i in range(K):
+        pts, ve = per_step[i]
+        dr.set_timing(pts)
+        step(W + i, verify_events=ve)
+    dr.set_timing([])
+    torch.cuda.synchronize()
+    sec_ms = {}
+    for pts, ve in per_step:
+        for s, l, a, b in pts:
+            key = s if l < 0 else s
+            sec_ms.setdefault(key, []).append(a.elapsed_time(b))
+        sec_ms.setdefault("verify", []).append(ve[0].elapsed_time(ve[1]))
+    # per-layer sections: mean per launch (average over layers and steps)
+    kern = {k: float(np.mean(v)) for k, v in sec_ms.items()}
+    lm_ms = kern["lm_head"]
+    M = BATCH * BLOCK
+    lm_bytes = shape.vocab * shape.hidden * 2 + M * shape.hidden * 2
+    lm_gbs = lm_bytes / (lm_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": "skinny_gemm_kernel<EpiLMHead> (LM head + argmax)",
+                "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "bytes_per_launch": lm_bytes, "avg_launch_us": round(lm_ms * 1e3, 2)}
+
+    # per-kernel HBM fractions of the weight-streaming GEMMs (per launch)
+    H, F, qd, kvd = shape.hidden, shape.ffn, shape.q_dim, shape.kv_dim
+    kbytes = {"qkv": (qd + 2 * kvd) * H * 2, "o_proj": H * qd * 2, "gate_up": 2 * F * H * 2,
+              "down": H * F * 2, "lm_head": lm_bytes,
+              "attention": (CTX + BLOCK) * kvd * 2 * 2,
+              "fuse_gemm": shape.n_feat * H * H * 2, "inject": shape.n_layers * 2 * kvd * H * 2,
+              "verify": BATCH * BLOCK * shape.vocab * 2}
+    kernels = {}
+    for k, ms in kern.items():
+        ent = {"avg_us": round(ms * 1e3, 2)}
+        if k in kbytes:
+            gbs = kbytes[k] / (ms * 1e-3) / 1e9
+            ent.update({"bytes": kbytes[k], "GB/s": round(gbs, 1),
+                        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+        kernels[k] = ent
+
+    mean_n = float(np.mean(tau[W:W + K]))
+    sb = step_bytes(shape, int(round(mean_n)))
+    tot = sum(sb.values())
+    step_roof = {"bytes_per_step": tot, "roofline_ms": tot / (HBM_PEAK_GBS * 1e9) * 1e3,
+                 "frac": round(tot / (HBM_PEAK_GBS * 1e9) / (ms_per_step * 1e-3), 4)}
+
+    # ---- CPU oracle on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(shape, w, feats, new_feats_np=configs.make_features(
+            shape, wid, BLOCK, name="bench_new"), tau=tau, logits=logits_np,
+            budget=args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(blocks_per_s, 2), "unit": "blocks/s",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen3-8b-shaped drafter, batch 1, ctx 2048, block 16",
+                   "layers": shape.n_layers, "hidden": shape.hidden, "heads": "32q/8kv x 128",
+                   "ffn": shape.ffn, "vocab": shape.vocab, "batch": BATCH, "ctx": CTX,
+                   "block": BLOCK, "mean_new_tokens_per_step": round(mean_n, 2),
+                   "launch": "eager"},
+        "tokens_per_s": round(blocks_per_s * BLOCK, 1),
+        "draft_tokens_per_s": round(blocks_per_s * (BLOCK - 1), 1),
+        "roofline": roofline,
+        "step_roofline": step_roof,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(shape, w, feats, new_feats_np, tau, logits, budget: float) -> dict:
+    """Time the oracle's step (same workload) on the host, untuned."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(p.get("num_threads", 1)) for p in threadpool_info()
+                     if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    t0 = time.perf_counter()
+    cache = O.prefill(w, shape, [feats])[0]
+    log(f"oracle prefill {time.perf_counter() - t0:.1f}s")
+    anchors = np.array([7], dtype=np.int32)
+    done, t_start = 0, time.perf_counter()
+    while True:
+        n = int(tau[done % len(tau)])
+        c = [(k[:CTX - n], v[:CTX - n]) for k, v in cache]
+        c = O.append_context(c, w, shape, [f[:n] for f in new_feats_np])
+        res = O.draft_block(w, shape, [c], anchors, BLOCK)
+        acc, bonus = O.verify_greedy(logits, res["draft_ids"])
+        anchors = bonus
+        done += 1
+        el = time.perf_counter() - t_start
+        if el >= budget or done >= 50:
+            break
+    return {"value": round(done / el, 4), "unit": "blocks/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} oracle steps of the same workload (fuse+inject of the step's new "
+                      f"rows, one 16-slot block through 5 layers at ctx 2048, LM-head argmax, "
+                      f"verify), float64 numpy, {el:.1f}s"}
+
+
+if __name__ == "__main__":
+    main()

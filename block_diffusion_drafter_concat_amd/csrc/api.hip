@@ -19,6 +19,8 @@ struct dflash_handle {
   dflash_config cfg;
   dflash_weights w;
   dflash_layer_weights layers[DFLASH_MAX_LAYERS];
+  dflash_timing_point timing[32];
+  int n_timing;
 };
 
 namespace {
@@ -38,6 +40,8 @@ inline dflash_status hip_status(hipError_t e) { return e == hipSuccess ? DFLASH_
 constexpr int kMaxAttnChunks = 32;
 // Rows per launch of the weight-streaming GEMM.
 constexpr int kMaxRowsPerLaunch = 128;
+// LM-head tiles (32 vocabulary rows each) walked by one workgroup.
+constexpr int kLmTilesPerWg = 8;
 
 struct Dims {
   int L, H, Hq, Hkv, d, F, V, nf, G, qd, kvd;
@@ -50,28 +54,26 @@ Dims dims(const dflash_config& c) {
   return r;
 }
 
-// Split of K over workgroups for a weight-streaming GEMM: enough workgroups to
-// keep bytes in flight on 256 CUs, each wave still streaming >= 256 k.
+struct GemmPlan {
+  int tiles_qkv, tiles_o, tiles_gu, tiles_d, tiles_lm, tiles_fc, tiles_inj;
+  int ks_o, ks_d;      // K-splits of the O and down projections (partials -> next norm)
+  int wg_lm;           // LM-head workgroups
+};
+
+// K-split of a partial-product GEMM: enough workgroups (>= 512) to keep bytes
+// in flight on 256 CUs while every wave still streams >= 256 k (4 waves).
 int pick_ksplit(int n_tiles, int K) {
   int ks = 1;
-  while (ks < 8 && n_tiles * ks * 2 <= 1024 && (K / (4 * ks * 2)) >= 256 &&
-         (K % (4 * ks * 2 * 32)) == 0)
+  while (ks < 8 && n_tiles * ks < 512 && K % (4 * ks * 2 * 32) == 0 && K / (4 * ks * 2) >= 256)
     ks *= 2;
   return ks;
 }
+// Fusion: K-split only for the short incremental calls (the partial slabs are
+// ks * T * H floats).
+int fuse_ksplit(const Dims& D, int64_t T) {
+  return T <= 64 ? pick_ksplit(D.H / 32, D.nf * D.H) : 1;
+}
 
-// ------------------------------------------------------------- workspace
-struct Layout {
-  size_t zero_off, zero_bytes;        // argmax keys + counters, cleared per call
-  size_t keys_off, cnt_off;
-  size_t rope_off, x_off, u_off, q_off, o_off, h_off, part_off, ao_off, aml_off, y_off, ver_off;
-  size_t total;
-  int n_counters;
-};
-
-struct GemmPlan {
-  int tiles_qkv, tiles_o, tiles_gu, tiles_d, tiles_lm, tiles_fc, tiles_inj;
-};
 GemmPlan gemm_plan(const Dims& D) {
   GemmPlan g;
   g.tiles_qkv = (D.qd + 2 * D.kvd) / 32;
@@ -81,8 +83,19 @@ GemmPlan gemm_plan(const Dims& D) {
   g.tiles_lm = (D.V + 31) / 32;
   g.tiles_fc = D.H / 32;
   g.tiles_inj = D.L * 2 * D.kvd / 32;
+  g.ks_o = pick_ksplit(g.tiles_o, D.qd);
+  g.ks_d = pick_ksplit(g.tiles_d, D.F);
+  g.wg_lm = (g.tiles_lm + kLmTilesPerWg - 1) / kLmTilesPerWg;
   return g;
 }
+
+// ------------------------------------------------------------- workspace
+// Every call lays out its own scratch from offset 0 with sizes that grow with
+// (batch, block, tokens); dflash_workspace_size takes the largest.
+struct Layout {
+  size_t rope_off, x_off, u_off, q_off, o_off, h_off, part_off, lm_off, ao_off, aml_off, ver_off;
+  size_t total;
+};
 
 Layout layout(const dflash_handle* h, int max_batch, int max_block, int64_t max_tokens) {
   const Dims D = dims(h->cfg);
@@ -90,23 +103,8 @@ Layout layout(const dflash_handle* h, int max_batch, int max_block, int64_t max_
   const size_t M = static_cast<size_t>(max_batch) * max_block;
   const size_t T = static_cast<size_t>(max_tokens > 0 ? max_tokens : 1);
   const GemmPlan g = gemm_plan(D);
-  const int row_launches = static_cast<int>((M + kMaxRowsPerLaunch - 1) / kMaxRowsPerLaunch);
-  const int t_launches = static_cast<int>((T + kMaxRowsPerLaunch - 1) / kMaxRowsPerLaunch);
   Layout L{};
-  // counters: per layer QKV, O, GU, D tiles and attention (batch x kv heads),
-  // per row-launch; LM head one per row-launch; fuse / inject tiles per launch
-  const size_t per_layer = static_cast<size_t>(g.tiles_qkv + g.tiles_o + g.tiles_gu + g.tiles_d) *
-                               row_launches + static_cast<size_t>(max_batch) * D.Hkv;
-  const size_t n_cnt = per_layer * D.L + row_launches +
-                       static_cast<size_t>(g.tiles_fc + g.tiles_inj) * t_launches;
-  L.n_counters = static_cast<int>(n_cnt);
   size_t off = 0;
-  L.zero_off = off;
-  L.keys_off = off;
-  off += align_up(M * 8);
-  L.cnt_off = off;
-  off += align_up(n_cnt * 4);
-  L.zero_bytes = off - L.zero_off;
   const size_t rope_rows = M > T ? M : T;
   L.rope_off = off; off += align_up(rope_rows * (D.d / 2) * 8);
   L.x_off = off;    off += align_up(M * D.H * 4);
@@ -114,65 +112,76 @@ Layout layout(const dflash_handle* h, int max_batch, int max_block, int64_t max_
   L.q_off = off;    off += align_up(M * D.qd * es);
   L.o_off = off;    off += align_up(M * D.qd * es);
   L.h_off = off;    off += align_up(M * D.F * es);
-  // split-K partials: per (tile, split) 128 rows x 16 columns x (v0, v1) floats
-  constexpr size_t kPartPerTile = static_cast<size_t>(kMaxRowsPerLaunch) * 16 * 2 * 4;
-  size_t part = 0;
-  const int gemms[6][2] = {{g.tiles_qkv, D.H}, {g.tiles_o, D.qd}, {g.tiles_gu, D.H},
-                           {g.tiles_d, D.F},   {g.tiles_fc, D.nf * D.H}, {g.tiles_inj, D.H}};
-  for (const auto& gk : gemms) {
-    const size_t p = static_cast<size_t>(gk[0]) * pick_ksplit(gk[0], gk[1]) * kPartPerTile;
-    part = p > part ? p : part;
-  }
+  // K-split partial slabs: O / down projections [ks][M][H], fusion [ks][T][H]
+  size_t part = static_cast<size_t>(g.ks_o > g.ks_d ? g.ks_o : g.ks_d) * M * D.H * 4;
+  const size_t pf = static_cast<size_t>(fuse_ksplit(D, static_cast<int64_t>(T))) * T * D.H * 4;
+  part = pf > part ? pf : part;
   L.part_off = off; off += align_up(part);
+  L.lm_off = off;   off += align_up(M * g.wg_lm * 8);
   const size_t qr = static_cast<size_t>((D.G * max_block + 15) / 16 * 16);
   const size_t slots = static_cast<size_t>(max_batch) * D.Hkv * kMaxAttnChunks;
   L.ao_off = off;  off += align_up(slots * qr * D.d * 4);
   L.aml_off = off; off += align_up(slots * qr * 8);
-  L.y_off = off;   off += align_up(T * D.H * 4);
   L.ver_off = off; off += align_up(verify_ws_bytes(max_batch, max_block, D.V));
   L.total = off;
   return L;
 }
+
+// Record the caller's timing event for (section, layer), if one is set.
+hipError_t mark(const dflash_handle* h, int section, int layer, bool stop, hipStream_t st) {
+  for (int i = 0; i < h->n_timing; ++i) {
+    const dflash_timing_point& p = h->timing[i];
+    if (p.section == section && (p.layer == layer || layer < 0)) {
+      hipError_t e = hipEventRecord(static_cast<hipEvent_t>(stop ? p.ev_stop : p.ev_start), st);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+#define DF_MARK(sec, layer, stop) DF_HIP(mark(h, sec, layer, stop, st))
 
 template <typename P> P* at(void* ws, size_t off) {
   return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
 }
 
 // ------------------------------------------------------------- GEMM launcher
-template <typename T, class Epi>
-hipError_t run_skinny(AOperand<T> A, int K, int n_tiles, const Epi& epi, int ksplit, float* part,
-                      int* counters, hipStream_t st) {
-  const int kper = K / (4 * ksplit);
-  dim3 grid(n_tiles, ksplit);
+// One launch over rows [A.m0, A.m0 + A.mc): ksplit workgroups per tile group
+// (grid.y), nw waves per workgroup, tiles_per_wg consecutive tiles each.
+template <typename T, int NW, class Epi>
+hipError_t launch_skinny_nw(const AOperand<T>& A, int K, int n_tiles, int tiles_per_wg,
+                            int ksplit, const Epi& epi, hipStream_t st) {
+  const int kper = K / (NW * ksplit);
+  dim3 grid((n_tiles + tiles_per_wg - 1) / tiles_per_wg, ksplit);
   const int mc = A.mc;
   if (mc <= 16) {
-    if (kper % 128 == 0) skinny_gemm_kernel<T, 1, 4, Epi><<<grid, 256, 0, st>>>(A, K, ksplit, part, counters, epi);
-    else skinny_gemm_kernel<T, 1, 1, Epi><<<grid, 256, 0, st>>>(A, K, ksplit, part, counters, epi);
+    if (kper % 256 == 0) skinny_gemm_kernel<T, 1, 4, NW, Epi><<<grid, NW * 64, 0, st>>>(A, K, n_tiles, tiles_per_wg, epi);
+    else if (kper % 64 == 0) skinny_gemm_kernel<T, 1, 2, NW, Epi><<<grid, NW * 64, 0, st>>>(A, K, n_tiles, tiles_per_wg, epi);
+    else skinny_gemm_kernel<T, 1, 1, NW, Epi><<<grid, NW * 64, 0, st>>>(A, K, n_tiles, tiles_per_wg, epi);
   } else if (mc <= 32) {
-    if (kper % 128 == 0) skinny_gemm_kernel<T, 2, 4, Epi><<<grid, 256, 0, st>>>(A, K, ksplit, part, counters, epi);
-    else skinny_gemm_kernel<T, 2, 1, Epi><<<grid, 256, 0, st>>>(A, K, ksplit, part, counters, epi);
+    if (kper % 64 == 0) skinny_gemm_kernel<T, 2, 2, NW, Epi><<<grid, NW * 64, 0, st>>>(A, K, n_tiles, tiles_per_wg, epi);
+    else skinny_gemm_kernel<T, 2, 1, NW, Epi><<<grid, NW * 64, 0, st>>>(A, K, n_tiles, tiles_per_wg, epi);
   } else if (mc <= 64) {
-    if (kper % 64 == 0) skinny_gemm_kernel<T, 4, 2, Epi><<<grid, 256, 0, st>>>(A, K, ksplit, part, counters, epi);
-    else skinny_gemm_kernel<T, 4, 1, Epi><<<grid, 256, 0, st>>>(A, K, ksplit, part, counters, epi);
+    skinny_gemm_kernel<T, 4, 1, NW, Epi><<<grid, NW * 64, 0, st>>>(A, K, n_tiles, tiles_per_wg, epi);
   } else if (mc <= 128) {
-    skinny_gemm_kernel<T, 8, 1, Epi><<<grid, 256, 0, st>>>(A, K, ksplit, part, counters, epi);
+    skinny_gemm_kernel<T, 8, 1, NW, Epi><<<grid, NW * 64, 0, st>>>(A, K, n_tiles, tiles_per_wg, epi);
   } else {
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-// Rows [0, M) in launches of at most 128 rows.  `counters` advances by
-// n_tiles per launch; `per_launch` adjusts per-launch epilogue state.
+// Rows [0, M) in launches of at most 128 rows; `per_launch` adjusts
+// per-launch epilogue state.  8 waves per workgroup when tiles are few.
 template <typename T, class Epi, class PerLaunch>
-hipError_t run_rows(AOperand<T> A, int K, int n_tiles, Epi epi, int ksplit, float* part,
-                    int* counters, hipStream_t st, PerLaunch per_launch) {
+hipError_t run_rows(AOperand<T> A, int K, int n_tiles, int tiles_per_wg, int ksplit, Epi epi,
+                    hipStream_t st, PerLaunch per_launch) {
+  const bool wide = (n_tiles / tiles_per_wg) * ksplit < 512 && K % (8 * ksplit * 32) == 0;
   for (int m0 = 0, li = 0; m0 < A.M; m0 += kMaxRowsPerLaunch, ++li) {
     A.m0 = m0;
     A.mc = A.M - m0 < kMaxRowsPerLaunch ? A.M - m0 : kMaxRowsPerLaunch;
     per_launch(epi, li);
-    hipError_t e = run_skinny<T, Epi>(A, K, n_tiles, epi, ksplit, part,
-                                      counters + static_cast<size_t>(li) * n_tiles, st);
+    hipError_t e = wide ? launch_skinny_nw<T, 8, Epi>(A, K, n_tiles, tiles_per_wg, ksplit, epi, st)
+                        : launch_skinny_nw<T, 4, Epi>(A, K, n_tiles, tiles_per_wg, ksplit, epi, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -205,6 +214,7 @@ bool unsupported_cfg(const dflash_config& c) {
   if (c.head_dim != 64 && c.head_dim != 128) return true;
   if (c.n_q_heads % c.n_kv_heads != 0) return true;
   if (c.hidden % 128 || c.ffn % 128 || (c.n_q_heads * c.head_dim) % 128) return true;
+  if (c.hidden > 8192) return true;
   return false;
 }
 
@@ -233,6 +243,7 @@ dflash_status check_kv(const dflash_handle* h, const dflash_kv* kv) {
   return DFLASH_OK;
 }
 
+// ------------------------------------------------------------- the calls
 template <typename T>
 dflash_status fuse_impl(dflash_handle* h, const void* const* feats, int64_t n_tokens,
                         void* ctx_out, void* ws, hipStream_t st) {
@@ -246,17 +257,17 @@ dflash_status fuse_impl(dflash_handle* h, const void* const* feats, int64_t n_to
   A.slab_k = D.H;
   A.M = T_;
   const int K = D.nf * D.H;
-  const int ks = pick_ksplit(g.tiles_fc, K);
-  float* Y = at<float>(ws, L.y_off);
-  int* cnt = at<int>(ws, L.cnt_off);
-  if (ks > 1) {
-    const int t_launches = (T_ + kMaxRowsPerLaunch - 1) / kMaxRowsPerLaunch;
-    DF_HIP(launch_zero(cnt, static_cast<int64_t>(g.tiles_fc) * t_launches, st));
-  }
-  EpiStoreF32<T> epi{static_cast<const T*>(h->w.fc), K, Y, D.H};
-  DF_HIP(run_rows<T>(A, K, g.tiles_fc, epi, ks, at<float>(ws, L.part_off), cnt, st, NoPerLaunch{}));
-  DF_HIP(launch_rmsnorm(h->cfg.dtype == DFLASH_BF16, Y, D.H, h->w.fc_norm, ctx_out, D.H, T_, D.H,
-                        h->cfg.rms_eps, st));
+  const int ks = fuse_ksplit(D, n_tokens);
+  float* Y = at<float>(ws, L.part_off);
+  DF_MARK(DFLASH_SEC_FUSE_GEMM, -1, false);
+  EpiPartialF32<T> epi{static_cast<const T*>(h->w.fc), K, Y, D.H, T_};
+  DF_HIP(run_rows<T>(A, K, g.tiles_fc, 1, ks, epi, st, NoPerLaunch{}));
+  DF_MARK(DFLASH_SEC_FUSE_GEMM, -1, true);
+  DF_MARK(DFLASH_SEC_FUSE_NORM, -1, false);
+  DF_HIP(launch_resid_rmsnorm(h->cfg.dtype == DFLASH_BF16, nullptr, Y, ks,
+                              static_cast<int64_t>(T_) * D.H, h->w.fc_norm, ctx_out, T_, D.H,
+                              h->cfg.rms_eps, st));
+  DF_MARK(DFLASH_SEC_FUSE_NORM, -1, true);
   return DFLASH_OK;
 }
 
@@ -267,6 +278,7 @@ dflash_status inject_impl(dflash_handle* h, const void* ctx, const SeqTable& seq
   const Layout L = layout(h, 1, 1, total);
   const GemmPlan g = gemm_plan(D);
   float2* rope = at<float2>(ws, L.rope_off);
+  DF_MARK(DFLASH_SEC_INJECT, -1, false);
   DF_HIP(launch_rope_rows(rope, total, D.d, static_cast<double>(h->cfg.rope_theta), seq, st));
   EpiInject<T> epi{};
   for (int l = 0; l < D.L; ++l) {
@@ -281,14 +293,9 @@ dflash_status inject_impl(dflash_handle* h, const void* ctx, const SeqTable& seq
   epi.cap = kv->cap_total;
   epi.rope = rope;
   epi.seq = seq;
-  const int ks = pick_ksplit(g.tiles_inj, D.H);
-  int* cnt = at<int>(ws, L.cnt_off);
-  if (ks > 1) {
-    const int t_launches = (total + kMaxRowsPerLaunch - 1) / kMaxRowsPerLaunch;
-    DF_HIP(launch_zero(cnt, static_cast<int64_t>(g.tiles_inj) * t_launches, st));
-  }
-  DF_HIP(run_rows<T>(a_single<T>(ctx, D.H, D.H, total), D.H, g.tiles_inj, epi, ks,
-                     at<float>(ws, L.part_off), cnt, st, NoPerLaunch{}));
+  DF_HIP(run_rows<T>(a_single<T>(ctx, D.H, D.H, total), D.H, g.tiles_inj, 1, 1, epi, st,
+                     NoPerLaunch{}));
+  DF_MARK(DFLASH_SEC_INJECT, -1, true);
   return DFLASH_OK;
 }
 
@@ -300,7 +307,7 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
   const bool bf = h->cfg.dtype == DFLASH_BF16;
   const Layout L = layout(h, nb, B, 1);
   const GemmPlan g = gemm_plan(D);
-  const int row_launches = (M + kMaxRowsPerLaunch - 1) / kMaxRowsPerLaunch;
+  const float eps = h->cfg.rms_eps;
 
   SeqTable seq{};
   seq.n = nb;
@@ -310,8 +317,6 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
     seq.off[b] = kv->seq_off[b];
     max_keys = (kv->seq_len[b] + B > max_keys) ? kv->seq_len[b] + B : max_keys;
   }
-  unsigned long long* keys = at<unsigned long long>(ws, L.keys_off);
-  int* cnt = at<int>(ws, L.cnt_off);
   float2* rope = at<float2>(ws, L.rope_off);
   float* x = at<float>(ws, L.x_off);
   T* u = at<T>(ws, L.u_off);
@@ -319,10 +324,12 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
   T* ob = at<T>(ws, L.o_off);
   T* hb = at<T>(ws, L.h_off);
   float* part = at<float>(ws, L.part_off);
+  const int64_t pstride = static_cast<int64_t>(M) * D.H;   // one K-split slab
 
+  DF_MARK(DFLASH_SEC_EMBED, -1, false);
   DF_HIP(launch_embed(bf, h->w.embed, D.H, D.V, anchors, h->cfg.mask_token_id, nb, B, x, rope, D.d,
-                      static_cast<double>(h->cfg.rope_theta), seq, at<uint32_t>(ws, L.zero_off),
-                      static_cast<int64_t>(L.zero_bytes / 4), st));
+                      static_cast<double>(h->cfg.rope_theta), seq, nullptr, 0, st));
+  DF_MARK(DFLASH_SEC_EMBED, -1, true);
 
   // attention split: chunks of >= 256 keys, at most kMaxAttnChunks per sequence
   int chunk = 256;
@@ -342,11 +349,14 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
   aa.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(D.d)));
   aa.seq = seq;
 
-  int* c = cnt;
+  int pending = 0;   // K-split slabs of the last projection, not yet added to x
   for (int l = 0; l < D.L; ++l) {
     const dflash_layer_weights& w = h->layers[l];
-    // attention half
-    DF_HIP(launch_rmsnorm(bf, x, D.H, w.attn_norm, u, D.H, M, D.H, h->cfg.rms_eps, st));
+    // attention half: x += (down partials of the previous layer); u = RMSNorm(x)
+    DF_MARK(DFLASH_SEC_ATTN_NORM, l, false);
+    DF_HIP(launch_resid_rmsnorm(bf, x, part, pending, pstride, w.attn_norm, u, M, D.H, eps, st));
+    DF_MARK(DFLASH_SEC_ATTN_NORM, l, true);
+    DF_MARK(DFLASH_SEC_QKV, l, false);
     {
       EpiQKV<T> e{};
       e.wq = static_cast<const T*>(w.wq);
@@ -359,55 +369,71 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
       e.cap = kv->cap_total;
       e.rope = rope;
       e.seq = seq;
-      const int ks = pick_ksplit(g.tiles_qkv, D.H);
-      DF_HIP(run_rows<T>(a_single<T>(u, D.H, D.H, M), D.H, g.tiles_qkv, e, ks, part, c, st,
+      DF_HIP(run_rows<T>(a_single<T>(u, D.H, D.H, M), D.H, g.tiles_qkv, 1, 1, e, st,
                          NoPerLaunch{}));
-      c += g.tiles_qkv * row_launches;
     }
+    DF_MARK(DFLASH_SEC_QKV, l, true);
     aa.kc = kv->k[l];
     aa.vc = kv->v[l];
-    aa.counters = c;
-    c += nb * D.Hkv;
+    DF_MARK(DFLASH_SEC_ATTENTION, l, false);
     DF_HIP(launch_block_attention(bf, D.d, aa, nb, st));
+    DF_MARK(DFLASH_SEC_ATTENTION, l, true);
+    DF_MARK(DFLASH_SEC_O_PROJ, l, false);
     {
-      EpiResidual<T> e{static_cast<const T*>(w.wo), D.qd, x, D.H};
-      const int ks = pick_ksplit(g.tiles_o, D.qd);
-      DF_HIP(run_rows<T>(a_single<T>(ob, D.qd, D.qd, M), D.qd, g.tiles_o, e, ks, part, c, st,
+      EpiPartialF32<T> e{static_cast<const T*>(w.wo), D.qd, part, D.H, M};
+      DF_HIP(run_rows<T>(a_single<T>(ob, D.qd, D.qd, M), D.qd, g.tiles_o, 1, g.ks_o, e, st,
                          NoPerLaunch{}));
-      c += g.tiles_o * row_launches;
     }
-    // feed-forward half
-    DF_HIP(launch_rmsnorm(bf, x, D.H, w.ffn_norm, u, D.H, M, D.H, h->cfg.rms_eps, st));
+    DF_MARK(DFLASH_SEC_O_PROJ, l, true);
+    // feed-forward half: x += O partials; u = RMSNorm(x)
+    DF_MARK(DFLASH_SEC_FFN_NORM, l, false);
+    DF_HIP(launch_resid_rmsnorm(bf, x, part, g.ks_o, pstride, w.ffn_norm, u, M, D.H, eps, st));
+    DF_MARK(DFLASH_SEC_FFN_NORM, l, true);
+    DF_MARK(DFLASH_SEC_GATE_UP, l, false);
     {
       EpiSwiGLU<T> e{static_cast<const T*>(w.wg), static_cast<const T*>(w.wu), D.H, hb, D.F};
-      const int ks = pick_ksplit(g.tiles_gu, D.H);
-      DF_HIP(run_rows<T>(a_single<T>(u, D.H, D.H, M), D.H, g.tiles_gu, e, ks, part, c, st,
+      DF_HIP(run_rows<T>(a_single<T>(u, D.H, D.H, M), D.H, g.tiles_gu, 1, 1, e, st,
                          NoPerLaunch{}));
-      c += g.tiles_gu * row_launches;
     }
+    DF_MARK(DFLASH_SEC_GATE_UP, l, true);
+    DF_MARK(DFLASH_SEC_DOWN, l, false);
     {
-      EpiResidual<T> e{static_cast<const T*>(w.wd), D.F, x, D.H};
-      const int ks = pick_ksplit(g.tiles_d, D.F);
-      DF_HIP(run_rows<T>(a_single<T>(hb, D.F, D.F, M), D.F, g.tiles_d, e, ks, part, c, st,
+      EpiPartialF32<T> e{static_cast<const T*>(w.wd), D.F, part, D.H, M};
+      DF_HIP(run_rows<T>(a_single<T>(hb, D.F, D.F, M), D.F, g.tiles_d, 1, g.ks_d, e, st,
                          NoPerLaunch{}));
-      c += g.tiles_d * row_launches;
     }
+    DF_MARK(DFLASH_SEC_DOWN, l, true);
+    pending = g.ks_d;
   }
+  // x += down partials of the last layer; u = RMSNorm(x)
+  DF_MARK(DFLASH_SEC_FINAL_NORM, -1, false);
+  DF_HIP(launch_resid_rmsnorm(bf, x, part, pending, pstride, h->w.final_norm, u, M, D.H, eps, st));
+  DF_MARK(DFLASH_SEC_FINAL_NORM, -1, true);
   if (dbg_h)
     DF_HIP(hipMemcpyAsync(dbg_h, x, static_cast<size_t>(M) * D.H * 4, hipMemcpyDeviceToDevice, st));
-  DF_HIP(launch_rmsnorm(bf, x, D.H, h->w.final_norm, u, D.H, M, D.H, h->cfg.rms_eps, st));
+  DF_MARK(DFLASH_SEC_LM_HEAD, -1, false);
   {
-    EpiLMHead<T> e{};
-    e.W = static_cast<const T*>(h->w.lm_head);
-    e.K = D.H; e.V = D.V; e.B = B; e.n_tiles = g.tiles_lm;
-    e.keys = keys;
-    e.counter = c;
-    e.draft = draft;
-    e.dbg = dbg_z;
-    int* lm_cnt = c;
-    DF_HIP(run_rows<T>(a_single<T>(u, D.H, D.H, M), D.H, g.tiles_lm, e, 1, part, c, st,
-                       [lm_cnt](EpiLMHead<T>& ep, int li) { ep.counter = lm_cnt + li; }));
+    float2* lm_part = at<float2>(ws, L.lm_off);
+    EpiLMHead<T, 1> e1{static_cast<const T*>(h->w.lm_head), D.H, D.V, g.wg_lm, lm_part, dbg_z};
+    EpiLMHead<T, 2> e2{static_cast<const T*>(h->w.lm_head), D.H, D.V, g.wg_lm, lm_part, dbg_z};
+    EpiLMHead<T, 4> e4{static_cast<const T*>(h->w.lm_head), D.H, D.V, g.wg_lm, lm_part, dbg_z};
+    EpiLMHead<T, 8> e8{static_cast<const T*>(h->w.lm_head), D.H, D.V, g.wg_lm, lm_part, dbg_z};
+    const AOperand<T> A = a_single<T>(u, D.H, D.H, M);
+    for (int m0 = 0; m0 < M; m0 += kMaxRowsPerLaunch) {
+      AOperand<T> Ai = A;
+      Ai.m0 = m0;
+      Ai.mc = M - m0 < kMaxRowsPerLaunch ? M - m0 : kMaxRowsPerLaunch;
+      const int mt = (Ai.mc + 15) / 16;
+      hipError_t e;
+      if (mt <= 1) e = launch_skinny_nw<T, 4>(Ai, D.H, g.tiles_lm, kLmTilesPerWg, 1, e1, st);
+      else if (mt <= 2) e = launch_skinny_nw<T, 4>(Ai, D.H, g.tiles_lm, kLmTilesPerWg, 1, e2, st);
+      else if (mt <= 4) e = launch_skinny_nw<T, 4>(Ai, D.H, g.tiles_lm, kLmTilesPerWg, 1, e4, st);
+      else e = launch_skinny_nw<T, 4>(Ai, D.H, g.tiles_lm, kLmTilesPerWg, 1, e8, st);
+      DF_HIP(e);
+    }
+    DF_HIP(launch_lm_argmax_finalize(lm_part, g.wg_lm, M, B, draft, st));
   }
+  DF_MARK(DFLASH_SEC_LM_HEAD, -1, true);
   return DFLASH_OK;
 }
 
@@ -463,6 +489,7 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, d
   h->w = *w;
   for (int l = 0; l < cfg->n_layers; ++l) h->layers[l] = w->layers[l];
   h->w.layers = h->layers;
+  h->n_timing = 0;
   *out = h;
   return DFLASH_OK;
 }
@@ -551,6 +578,17 @@ dflash_status dflash_draft_block(dflash_handle* h, dflash_kv* kv, int32_t block_
                                     dbg_logits, ws, st)
              : draft_impl<float>(h, kv, block_size, anchor_ids, draft_ids, dbg_final_hidden,
                                  dbg_logits, ws, st);
+}
+
+dflash_status dflash_set_timing(dflash_handle* h, const dflash_timing_point* points, int32_t n) {
+  if (!h || n < 0 || n > 32 || (n > 0 && !points)) return DFLASH_ERR_INVALID_ARG;
+  for (int i = 0; i < n; ++i)
+    if (points[i].section < DFLASH_SEC_FUSE_GEMM || points[i].section > DFLASH_SEC_LM_HEAD ||
+        !points[i].ev_start || !points[i].ev_stop)
+      return DFLASH_ERR_INVALID_ARG;
+  for (int i = 0; i < n; ++i) h->timing[i] = points[i];
+  h->n_timing = n;
+  return DFLASH_OK;
 }
 
 size_t dflash_verify_workspace_size(int32_t batch, int32_t block_size, int32_t vocab) {

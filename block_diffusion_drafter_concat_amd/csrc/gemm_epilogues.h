@@ -1,71 +1,63 @@
 // Epilogues of the weight-streaming GEMM.  Each one says which W rows make up
 // pair tile `tile` (rows(): the W row this lane streams for sub-tile 0 and 1)
 // and what to do with the pair of results (apply(): row m, column i of the
-// 16-wide sub-tiles).  tail() runs once per workgroup after all apply() calls.
+// 16-wide sub-tiles, K-split `split`).  State is per-thread scratch that lives
+// across the tiles one workgroup walks; finish() runs once per workgroup.
 #pragma once
 
 #include "device_common.h"
 
 namespace dflash {
 
-// out[m, n] (float32) = A . W^T, 32 consecutive W rows per tile.
+struct NoState {};
+
+// Float32 partial products, one slab per K-split:
+//   out[(split * slab_rows + m) * ldo + n] = sum over this split's K of A[m] . W[n]
+// with 32 consecutive W rows per tile.  The consumer sums the slabs in order.
 template <typename T>
-struct EpiStoreF32 {
+struct EpiPartialF32 {
+  using State = NoState;
   const T* W;
   int K;
   float* out;
   int64_t ldo;
+  int64_t slab_rows;   // rows per split slab
+  __device__ void init(State&) const {}
   __device__ void rows(int tile, int r16, const T*& w0, const T*& w1) const {
     w0 = W + static_cast<int64_t>(tile * 32 + r16) * K;
     w1 = w0 + static_cast<int64_t>(16) * K;
   }
-  __device__ void apply(int tile, int m, int i, bool valid, float v0, float v1) const {
+  __device__ void apply(State&, int, int tile, int split, int m, int i, bool valid, float v0,
+                        float v1) const {
     if (!valid) return;
-    float* o = out + static_cast<int64_t>(m) * ldo + tile * 32 + i;
+    float* o = out + (split * slab_rows + m) * ldo + tile * 32 + i;
     o[0] = v0;
     o[16] = v1;
   }
-  __device__ void tail(int, int, int) const {}
-};
-
-// Residual add: x[m, n] += A . W^T (O and down projections).
-template <typename T>
-struct EpiResidual {
-  const T* W;
-  int K;
-  float* x;
-  int64_t ldx;
-  __device__ void rows(int tile, int r16, const T*& w0, const T*& w1) const {
-    w0 = W + static_cast<int64_t>(tile * 32 + r16) * K;
-    w1 = w0 + static_cast<int64_t>(16) * K;
-  }
-  __device__ void apply(int tile, int m, int i, bool valid, float v0, float v1) const {
-    if (!valid) return;
-    float* o = x + static_cast<int64_t>(m) * ldx + tile * 32 + i;
-    o[0] += v0;
-    o[16] += v1;
-  }
-  __device__ void tail(int, int, int) const {}
+  __device__ void finish(State&, int, int, int) const {}
 };
 
 // SwiGLU: h[m, j] = silu(u . wg[j]) * (u . wu[j]), stored in the handle type.
 template <typename T>
 struct EpiSwiGLU {
+  using State = NoState;
   const T* wg;
   const T* wu;
   int K;
   T* h;
   int64_t ldh;
+  __device__ void init(State&) const {}
   __device__ void rows(int tile, int r16, const T*& w0, const T*& w1) const {
     w0 = wg + static_cast<int64_t>(tile * 16 + r16) * K;
     w1 = wu + static_cast<int64_t>(tile * 16 + r16) * K;
   }
-  __device__ void apply(int tile, int m, int i, bool valid, float g, float u) const {
+  __device__ void apply(State&, int, int tile, int, int m, int i, bool valid, float g,
+                        float u) const {
     if (!valid) return;
     const float s = g / (1.0f + expf(-g));
     stf(h + static_cast<int64_t>(m) * ldh + tile * 16 + i, s * u);
   }
-  __device__ void tail(int, int, int) const {}
+  __device__ void finish(State&, int, int, int) const {}
 };
 
 // Pair tiles of a K or Q projection: tile covers, for one head, columns
@@ -83,6 +75,7 @@ __device__ __forceinline__ RopePairTile rope_pair_tile(int t, int d) {
 // cache rows just past each sequence's committed context.
 template <typename T>
 struct EpiQKV {
+  using State = NoState;
   const T* wq;
   const T* wk;
   const T* wv;
@@ -94,6 +87,7 @@ struct EpiQKV {
   int64_t cap;
   const float2* rope;   // [m][d/2]
   SeqTable seq;
+  __device__ void init(State&) const {}
   __device__ int nq() const { return Hq * (d / 32); }
   __device__ int nk() const { return Hkv * (d / 32); }
   __device__ void rows(int tile, int r16, const T*& w0, const T*& w1) const {
@@ -109,7 +103,8 @@ struct EpiQKV {
       w1 = w0 + static_cast<int64_t>(16) * K;
     }
   }
-  __device__ void apply(int tile, int m, int i, bool valid, float v0, float v1) const {
+  __device__ void apply(State&, int, int tile, int, int m, int i, bool valid, float v0,
+                        float v1) const {
     if (!valid) return;
     const int b = m / B, j = m % B;
     const int64_t row = seq.off[b] + seq.len[b] + j;
@@ -130,13 +125,14 @@ struct EpiQKV {
       stf(vc + (static_cast<int64_t>(cb / d) * d + cb % d) * cap + row, v1);
     }
   }
-  __device__ void tail(int, int, int) const {}
+  __device__ void finish(State&, int, int, int) const {}
 };
 
 // KV injection of context rows into every layer's cache: per layer, K pair
 // tiles (RoPE at the row's position) then plain V tiles.
 template <typename T>
 struct EpiInject {
+  using State = NoState;
   const T* wk[kMaxLayers];
   const T* wv[kMaxLayers];
   T* kc[kMaxLayers];
@@ -145,6 +141,7 @@ struct EpiInject {
   int64_t cap;
   const float2* rope;   // [m][d/2] at each row's position
   SeqTable seq;
+  __device__ void init(State&) const {}
   __device__ int kt() const { return Hkv * (d / 32); }
   __device__ void rows(int tile, int r16, const T*& w0, const T*& w1) const {
     const int l = tile / (2 * kt()), t = tile % (2 * kt());
@@ -157,7 +154,8 @@ struct EpiInject {
       w1 = w0 + static_cast<int64_t>(16) * K;
     }
   }
-  __device__ void apply(int tile, int m, int i, bool valid, float v0, float v1) const {
+  __device__ void apply(State&, int, int tile, int, int m, int i, bool valid, float v0,
+                        float v1) const {
     if (!valid) return;
     const int l = tile / (2 * kt()), t = tile % (2 * kt());
     const int b = seq_of_row(seq, m);
@@ -175,57 +173,65 @@ struct EpiInject {
       stf(vc[l] + (static_cast<int64_t>(cb / d) * d + cb % d) * cap + row, v1);
     }
   }
-  __device__ void tail(int, int, int) const {}
+  __device__ void finish(State&, int, int, int) const {}
 };
 
-// LM head with fused argmax: logits never reach memory (unless dbg is set);
-// each workgroup folds its 32 columns into a 64-bit (value, lowest index) key
-// per row with atomicMax; the last workgroup to finish turns the keys of
-// slots 1..B-1 into draft ids (zhichai.net, "DFlash 的架构密码", 训练策略 3:
-// the drafter reads out through the target's own LM head).
-template <typename T>
+// LM head with fused argmax: logits never reach memory (unless dbg is set).
+// Each thread keeps, for its rows, the best (value, lowest column) over the
+// columns it sees across the workgroup's tiles; finish() folds the 16 columns
+// of a row and writes one partial per (row, workgroup) for the finalize
+// kernel (zhichai.net, "DFlash 的架构密码", 训练策略 3: the drafter reads out
+// through the target's own LM head).
+template <typename T, int MT>
 struct EpiLMHead {
+  struct State {
+    float best[MT];
+    int idx[MT];
+  };
   const T* W;
-  int K, V, B, n_tiles;
-  unsigned long long* keys;   // [M], zero on entry
-  int* counter;               // zero on entry, one per launch
-  int32_t* draft;             // [M/B][B-1]
-  float* dbg;                 // [M][V] or null
+  int K, V;
+  int n_wg;            // workgroups of this launch
+  float2* part;        // [rows][n_wg]: (value, index as float bits)
+  float* dbg;          // [rows][V] or null
+  __device__ void init(State& s) const {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) { s.best[mt] = -INFINITY; s.idx[mt] = 0x7fffffff; }
+  }
   __device__ void rows(int tile, int r16, const T*& w0, const T*& w1) const {
     const int c0 = min(tile * 32 + r16, V - 1), c1 = min(tile * 32 + 16 + r16, V - 1);
     w0 = W + static_cast<int64_t>(c0) * K;
     w1 = W + static_cast<int64_t>(c1) * K;
   }
-  __device__ void apply(int tile, int m, int i, bool valid, float v0, float v1) const {
+  __device__ void apply(State& s, int mt, int tile, int, int m, int i, bool valid, float v0,
+                        float v1) const {
     const int c0 = tile * 32 + i, c1 = c0 + 16;
     if (valid && dbg) {
       if (c0 < V) dbg[static_cast<int64_t>(m) * V + c0] = v0;
       if (c1 < V) dbg[static_cast<int64_t>(m) * V + c1] = v1;
     }
-    float best = (c0 < V) ? v0 : -INFINITY;
-    int bi = c0;
-    if (c1 < V && v1 > best) { best = v1; bi = c1; }
 #pragma unroll
-    for (int o = 8; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(best, o, 16);
-      const int oi = __shfl_xor(bi, o, 16);
-      if (better(ov, oi, best, bi)) { best = ov; bi = oi; }
+    for (int q = 0; q < MT; ++q) {
+      if (q != mt) continue;
+      // columns grow with the tile, so ">" keeps the lowest on ties
+      if (c0 < V && v0 > s.best[q]) { s.best[q] = v0; s.idx[q] = c0; }
+      if (c1 < V && v1 > s.best[q]) { s.best[q] = v1; s.idx[q] = c1; }
     }
-    if (valid && i == 0 && (m % B) != 0) atomicMax(&keys[m], argmax_key(best, bi));
   }
-  __device__ void tail(int, int m0, int mc) const {
-    __shared__ int s_done;
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) s_done = (atomicAdd(counter, 1) == n_tiles - 1);
-    __syncthreads();
-    if (!s_done) return;
-    __threadfence();
-    for (int m = m0 + threadIdx.x; m < m0 + mc; m += 256) {
-      const int j = m % B;
-      if (j == 0) continue;
-      const unsigned long long k = atomicAdd(&keys[m], 0ull);
-      draft[(m / B) * (B - 1) + (j - 1)] = argmax_key_index(k);
+  __device__ void finish(State& s, int wg, int m0, int mc) const {
+    const int t = threadIdx.x, i = t & 15, rr = t >> 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      float best = s.best[mt];
+      int bi = s.idx[mt];
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(best, o, 16);
+        const int oi = __shfl_xor(bi, o, 16);
+        if (better(ov, oi, best, bi)) { best = ov; bi = oi; }
+      }
+      const int m = mt * 16 + rr;
+      if (i == 0 && m < mc)
+        part[static_cast<int64_t>(m0 + m) * n_wg + wg] = make_float2(best, __int_as_float(bi));
     }
   }
 };

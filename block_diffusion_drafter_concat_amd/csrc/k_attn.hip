@@ -17,7 +17,7 @@
 //   O^T[d x queries]   += V^T[d x keys] . P^T (V^T straight from the transposed
 //                                             V cache, 16 contiguous bytes/lane)
 // Softmax is online in fp32 (base-2 with the scale folded in).  Chunks meet in
-// the workspace; the last chunk to finish merges them in chunk order.
+// the workspace; a separate merge kernel combines them in chunk order.
 #include "kernels_attn.h"
 
 namespace dflash {
@@ -60,7 +60,6 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs p) {
   constexpr int QR = NQ * 16;  // query rows (padded)
   __shared__ float s_m[4][QR], s_l[4][QR];
   __shared__ float s_o[QR][D + 4];
-  __shared__ int s_last;
 
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -206,7 +205,8 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs p) {
     return;
   }
 
-  // ---- several chunks: publish this chunk, the last one merges in order
+  // ---- several chunks: publish this chunk's (unnormalised O, max, sum); the
+  // merge kernel combines the chunks of a (sequence, kv head) in chunk order
   const int64_t slot = (static_cast<int64_t>(b) * p.n_kv + g) * p.max_chunks;
   float* po = p.part_o + (slot + c) * (QR * D);
   float2* pml = p.part_ml + (slot + c) * QR;
@@ -217,41 +217,57 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs p) {
                     s_l[2][r] * exp2f(s_m[2][r] - M) + s_l[3][r] * exp2f(s_m[3][r] - M);
     pml[r] = make_float2(M, L);
   }
-  __threadfence();
-  __syncthreads();
-  if (t == 0) s_last = (atomicAdd(&p.counters[b * p.n_kv + g], 1) == n_chunks_b - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const float* all_o = p.part_o + slot * (QR * D);
-  const float2* all_ml = p.part_ml + slot * QR;
-  for (int e = t; e < GB * D; e += 256) {
-    const int r = e / D, dd = e % D;
-    float M = -1e30f;
-    for (int cc = 0; cc < n_chunks_b; ++cc) M = fmaxf(M, all_ml[cc * QR + r].x);
-    float num = 0.f, den = 0.f;
-    for (int cc = 0; cc < n_chunks_b; ++cc) {
-      const float2 ml = all_ml[cc * QR + r];
-      const float w = exp2f(ml.x - M);
-      num += w * all_o[static_cast<int64_t>(cc) * QR * D + e];
-      den += w * ml.y;
-    }
-    const int h = r / B, j = r % B;
-    stf(out + static_cast<int64_t>(b * B + j) * p.ldq + (g * G + h) * D + dd, num / den);
+}
+
+// One workgroup per (row block of 256 output elements, kv head, sequence):
+// o = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c over the sequence's chunks.
+template <typename T, int D, int QR>
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p) {
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int B = p.B, G = p.G, GB = G * B;
+  const int n_keys = p.seq.len[b] + B;
+  const int n_chunks_b = (n_keys + p.chunk - 1) / p.chunk;
+  if (n_chunks_b <= 1) return;   // written directly by the attention kernel
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= GB * D) return;
+  const int r = e / D, dd = e % D;
+  const int64_t slot = (static_cast<int64_t>(b) * p.n_kv + g) * p.max_chunks;
+  const float2* ml = p.part_ml + slot * QR + r;
+  const float* po = p.part_o + slot * (QR * D) + e;
+  float M = -1e30f;
+  for (int cc = 0; cc < n_chunks_b; ++cc) M = fmaxf(M, ml[cc * QR].x);
+  float num = 0.f, den = 0.f;
+  for (int cc = 0; cc < n_chunks_b; ++cc) {
+    const float2 v = ml[cc * QR];
+    const float w = exp2f(v.x - M);
+    num += w * po[static_cast<int64_t>(cc) * QR * D];
+    den += w * v.y;
   }
+  const int h = r / B, j = r % B;
+  stf(static_cast<T*>(p.o) + static_cast<int64_t>(b * B + j) * p.ldq + (g * G + h) * D + dd,
+      num / den);
+}
+
+template <typename T, int D, int NQ>
+static hipError_t launch_attn_nq(const AttnArgs& a, dim3 grid, int batch, hipStream_t st) {
+  block_attn_kernel<T, D, NQ><<<grid, 256, 0, st>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.max_chunks <= 1) return e;
+  dim3 mgrid((a.G * a.B * D + 255) / 256, a.n_kv, batch);
+  attn_merge_kernel<T, D, NQ * 16><<<mgrid, 256, 0, st>>>(a);
+  return hipGetLastError();
 }
 
 template <typename T, int D>
-static hipError_t launch_attn_t(const AttnArgs& a, int nq, dim3 grid, hipStream_t st) {
+static hipError_t launch_attn_t(const AttnArgs& a, int nq, dim3 grid, int batch, hipStream_t st) {
   switch (nq) {
-    case 1: block_attn_kernel<T, D, 1><<<grid, 256, 0, st>>>(a); break;
-    case 2: block_attn_kernel<T, D, 2><<<grid, 256, 0, st>>>(a); break;
-    case 3: block_attn_kernel<T, D, 3><<<grid, 256, 0, st>>>(a); break;
-    case 4: block_attn_kernel<T, D, 4><<<grid, 256, 0, st>>>(a); break;
-    case 5: block_attn_kernel<T, D, 5><<<grid, 256, 0, st>>>(a); break;
+    case 1: return launch_attn_nq<T, D, 1>(a, grid, batch, st);
+    case 2: return launch_attn_nq<T, D, 2>(a, grid, batch, st);
+    case 3: return launch_attn_nq<T, D, 3>(a, grid, batch, st);
+    case 4: return launch_attn_nq<T, D, 4>(a, grid, batch, st);
+    case 5: return launch_attn_nq<T, D, 5>(a, grid, batch, st);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_block_attention(bool bf16, int head_dim, const AttnArgs& a, int batch,
@@ -259,11 +275,11 @@ hipError_t launch_block_attention(bool bf16, int head_dim, const AttnArgs& a, in
   const int nq = (a.G * a.B + 15) / 16;
   dim3 grid(a.max_chunks, a.n_kv, batch);
   if (bf16) {
-    if (head_dim == 128) return launch_attn_t<uint16_t, 128>(a, nq, grid, st);
-    if (head_dim == 64) return launch_attn_t<uint16_t, 64>(a, nq, grid, st);
+    if (head_dim == 128) return launch_attn_t<uint16_t, 128>(a, nq, grid, batch, st);
+    if (head_dim == 64) return launch_attn_t<uint16_t, 64>(a, nq, grid, batch, st);
   } else {
-    if (head_dim == 128) return launch_attn_t<float, 128>(a, nq, grid, st);
-    if (head_dim == 64) return launch_attn_t<float, 64>(a, nq, grid, st);
+    if (head_dim == 128) return launch_attn_t<float, 128>(a, nq, grid, batch, st);
+    if (head_dim == 64) return launch_attn_t<float, 64>(a, nq, grid, batch, st);
   }
   return hipErrorInvalidValue;
 }

@@ -63,45 +63,103 @@ hipError_t launch_embed(bool bf16, const void* embed, int H, int V, const int32_
 }
 
 // ------------------------------------------------------------------ RMSNorm
-// y = x / sqrt(mean(x^2) + eps) * g (zhichai.net, "DFlash 的架构密码",
-// 技术细节补充 / 投影层 for the fusion norm; the same form for the layer norms).
-// One workgroup per row; float32 statistics with a fixed reduction order.
+// Row m: v = x[m] (if x) + sum over splits s of part[s][m] (in split order);
+// x[m] = v (if x); out[m] = v / sqrt(mean(v^2) + eps) * g (if out).
+// The split-K partials of the producing GEMM meet here, together with the
+// residual add, so no GEMM has to wait on another workgroup.  RMSNorm:
+// zhichai.net, "DFlash 的架构密码", 技术细节补充 / 投影层 for the fusion norm;
+// the same form for the layer norms.  One workgroup per row, H <= 8192,
+// float32 statistics with a fixed reduction order.
 template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, int64_t ldx,
-                                                      const T* __restrict__ gain,
-                                                      T* __restrict__ out, int64_t ldo, int H,
-                                                      float eps) {
-  __shared__ float part[4];
-  const float* xr = x + static_cast<int64_t>(blockIdx.x) * ldx;
+__global__ __launch_bounds__(256) void resid_rmsnorm_kernel(float* __restrict__ x,
+                                                            const float* __restrict__ part,
+                                                            int n_split, int64_t split_stride,
+                                                            const T* __restrict__ gain,
+                                                            T* __restrict__ out, int H, float eps) {
+  __shared__ float red[4];
+  const int m = blockIdx.x;
+  constexpr int kMaxPer = 8;   // float4 groups per thread: H <= 8192
+  float4 v[kMaxPer];
   float ss = 0.f;
-  for (int c = threadIdx.x * 4; c < H; c += 1024) {
-    const float4 v = *reinterpret_cast<const float4*>(xr + c);
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+#pragma unroll
+  for (int q = 0; q < kMaxPer; ++q) {
+    const int c = (q * 256 + threadIdx.x) * 4;
+    if (c < H) {
+      float4 a = x ? *reinterpret_cast<const float4*>(x + static_cast<int64_t>(m) * H + c)
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int s = 0; s < n_split; ++s) {
+        const float4 p = *reinterpret_cast<const float4*>(part + s * split_stride +
+                                                         static_cast<int64_t>(m) * H + c);
+        a.x += p.x; a.y += p.y; a.z += p.z; a.w += p.w;
+      }
+      if (x && n_split > 0) *reinterpret_cast<float4*>(x + static_cast<int64_t>(m) * H + c) = a;
+      v[q] = a;
+      ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+    }
   }
+  if (!out) return;
   ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
-  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
   const float r = 1.0f / sqrtf(tot / static_cast<float>(H) + eps);
-  T* o = out + static_cast<int64_t>(blockIdx.x) * ldo;
-  for (int c = threadIdx.x * 4; c < H; c += 1024) {
-    const float4 v = *reinterpret_cast<const float4*>(xr + c);
-    stf(o + c + 0, v.x * r * ldf(gain + c + 0));
-    stf(o + c + 1, v.y * r * ldf(gain + c + 1));
-    stf(o + c + 2, v.z * r * ldf(gain + c + 2));
-    stf(o + c + 3, v.w * r * ldf(gain + c + 3));
+  T* o = out + static_cast<int64_t>(m) * H;
+#pragma unroll
+  for (int q = 0; q < kMaxPer; ++q) {
+    const int c = (q * 256 + threadIdx.x) * 4;
+    if (c < H) {
+      stf(o + c + 0, v[q].x * r * ldf(gain + c + 0));
+      stf(o + c + 1, v[q].y * r * ldf(gain + c + 1));
+      stf(o + c + 2, v[q].z * r * ldf(gain + c + 2));
+      stf(o + c + 3, v[q].w * r * ldf(gain + c + 3));
+    }
   }
 }
 
-hipError_t launch_rmsnorm(bool bf16, const float* x, int64_t ldx, const void* gain, void* out,
-                          int64_t ldo, int rows, int H, float eps, hipStream_t st) {
+hipError_t launch_resid_rmsnorm(bool bf16, float* x, const float* part, int n_split,
+                                int64_t split_stride, const void* gain, void* out, int rows,
+                                int H, float eps, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
+  if (H > 8192 || H % 4) return hipErrorInvalidValue;
   if (bf16)
-    rmsnorm_kernel<uint16_t><<<rows, 256, 0, st>>>(x, ldx, static_cast<const uint16_t*>(gain),
-                                                   static_cast<uint16_t*>(out), ldo, H, eps);
+    resid_rmsnorm_kernel<uint16_t><<<rows, 256, 0, st>>>(
+        x, part, n_split, split_stride, static_cast<const uint16_t*>(gain),
+        static_cast<uint16_t*>(out), H, eps);
   else
-    rmsnorm_kernel<float><<<rows, 256, 0, st>>>(x, ldx, static_cast<const float*>(gain),
-                                                static_cast<float*>(out), ldo, H, eps);
+    resid_rmsnorm_kernel<float><<<rows, 256, 0, st>>>(x, part, n_split, split_stride,
+                                                      static_cast<const float*>(gain),
+                                                      static_cast<float*>(out), H, eps);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ LM-head argmax
+// Row m (block slot j = m % B >= 1): fold the per-workgroup (value, lowest
+// column) partials of the LM-head GEMM into the draft id of that slot.
+__global__ __launch_bounds__(64) void lm_argmax_finalize_kernel(const float2* __restrict__ part,
+                                                                int n_wg, int B,
+                                                                int32_t* __restrict__ draft) {
+  const int m = blockIdx.x, j = m % B;
+  if (j == 0) return;
+  float best = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int w = threadIdx.x; w < n_wg; w += 64) {
+    const float2 p = part[static_cast<int64_t>(m) * n_wg + w];
+    const int pi = __float_as_int(p.y);
+    if (better(p.x, pi, best, bi)) { best = p.x; bi = pi; }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(best, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    if (better(ov, oi, best, bi)) { best = ov; bi = oi; }
+  }
+  if (threadIdx.x == 0) draft[(m / B) * (B - 1) + (j - 1)] = bi;
+}
+
+hipError_t launch_lm_argmax_finalize(const float2* part, int n_wg, int rows, int B, int32_t* draft,
+                                     hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  lm_argmax_finalize_kernel<<<rows, 64, 0, st>>>(part, n_wg, B, draft);
   return hipGetLastError();
 }
 
@@ -195,16 +253,15 @@ __global__ __launch_bounds__(256) void verify_chunk_kernel(const T* __restrict__
   }
 }
 
-__global__ __launch_bounds__(64) void verify_scan_kernel(const ArgPart* __restrict__ part,
-                                                         int n_chunks, int B,
-                                                         const int32_t* __restrict__ drafts,
-                                                         int32_t* __restrict__ accept,
-                                                         int32_t* __restrict__ bonus) {
-  const int b = blockIdx.x, lane = threadIdx.x;
-  int t[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    if (j >= B) { t[j] = 0; continue; }
+// One workgroup per sequence, wave j folds the chunks of row j.
+__global__ __launch_bounds__(1024) void verify_scan_kernel(const ArgPart* __restrict__ part,
+                                                           int n_chunks, int B,
+                                                           const int32_t* __restrict__ drafts,
+                                                           int32_t* __restrict__ accept,
+                                                           int32_t* __restrict__ bonus) {
+  __shared__ int s_t[16];
+  const int b = blockIdx.x, j = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (j < B) {
     float best = -INFINITY;
     int bi = 0x7fffffff;
     const ArgPart* p = part + static_cast<int64_t>(b * B + j) * n_chunks;
@@ -218,17 +275,15 @@ __global__ __launch_bounds__(64) void verify_scan_kernel(const ArgPart* __restri
       const int oi = __shfl_xor(bi, o, 64);
       if (better(ov, oi, best, bi)) { best = ov; bi = oi; }
     }
-    t[j] = bi;
+    if (lane == 0) s_t[j] = bi;
   }
-  if (lane == 0) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
     const int32_t* d = drafts + static_cast<int64_t>(b) * (B - 1);
     int a = 0;
-    while (a < B - 1 && t[a] == d[a]) ++a;
-    int bon = t[0];
-#pragma unroll
-    for (int j = 1; j < 16; ++j) bon = (j == a) ? t[j] : bon;
+    while (a < B - 1 && s_t[a] == d[a]) ++a;
     accept[b] = a;
-    bonus[b] = bon;
+    bonus[b] = s_t[a];
   }
 }
 
@@ -254,7 +309,7 @@ hipError_t launch_verify(const void* logits, bool bf16, const int32_t* drafts, i
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  verify_scan_kernel<<<batch, 64, 0, st>>>(part, n_chunks, B, drafts, accept, bonus);
+  verify_scan_kernel<<<batch, 64 * B, 0, st>>>(part, n_chunks, B, drafts, accept, bonus);
   return hipGetLastError();
 }
 

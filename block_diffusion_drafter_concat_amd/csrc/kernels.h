@@ -20,9 +20,15 @@ hipError_t launch_embed(bool bf16, const void* embed, int H, int V, const int32_
                         double theta, const SeqTable& seq, uint32_t* zero, int64_t n_zero,
                         hipStream_t st);
 
-// out[r] = x[r] / sqrt(mean(x[r]^2) + eps) * gain, stored in the handle type.
-hipError_t launch_rmsnorm(bool bf16, const float* x, int64_t ldx, const void* gain, void* out,
-                          int64_t ldo, int rows, int H, float eps, hipStream_t st);
+// Row m: v = x[m] + sum_s part[s * split_stride + m*H ...] (x and part may be
+// null); x[m] = v when x; out[m] = RMSNorm(v) * gain when out (handle type).
+hipError_t launch_resid_rmsnorm(bool bf16, float* x, const float* part, int n_split,
+                                int64_t split_stride, const void* gain, void* out, int rows,
+                                int H, float eps, hipStream_t st);
+
+// Draft ids from the LM head's per-workgroup (value, index) partials [rows][n_wg].
+hipError_t launch_lm_argmax_finalize(const float2* part, int n_wg, int rows, int B, int32_t* draft,
+                                     hipStream_t st);
 
 // RoPE cos/sin of inject rows: row m of sequence b sits at seq.pos0[b] + m - seq.row0[b].
 hipError_t launch_rope_rows(float2* rope, int rows, int d, double theta, const SeqTable& seq,

@@ -14,7 +14,6 @@ struct AttnArgs {
   void* o;              // [batch*B, n_q*D] attention output
   float* part_o;        // [batch][n_kv][max_chunks][ceil16(G*B)][D]
   float2* part_ml;      // [batch][n_kv][max_chunks][ceil16(G*B)]  (max, sum), base 2
-  int* counters;        // [batch*n_kv], zero on entry
   int B, G, n_kv;
   int chunk;            // keys per workgroup, multiple of 128
   int max_chunks;       // grid.x

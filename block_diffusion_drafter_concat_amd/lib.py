@@ -26,7 +26,12 @@ F32, BF16 = 0, 1
 EXPORTS = ("dflash_target_layer_ids", "dflash_create", "dflash_destroy",
            "dflash_workspace_size", "dflash_fuse_context", "dflash_inject_kv",
            "dflash_draft_block", "dflash_verify_greedy", "dflash_verify_workspace_size",
-           "dflash_status_string")
+           "dflash_set_timing", "dflash_status_string")
+
+# dflash_section
+SECTIONS = {"fuse_gemm": 1, "fuse_norm": 2, "inject": 3, "embed": 4, "attn_norm": 5, "qkv": 6,
+            "attention": 7, "o_proj": 8, "ffn_norm": 9, "gate_up": 10, "down": 11,
+            "final_norm": 12, "lm_head": 13}
 
 
 class DflashError(RuntimeError):
@@ -58,6 +63,11 @@ class KV(C.Structure):
                 ("batch", C.c_int32), ("cap_total", C.c_int64),
                 ("seq_off", C.POINTER(C.c_int64)), ("seq_cap", C.POINTER(C.c_int32)),
                 ("seq_len", C.POINTER(C.c_int32))]
+
+
+class TimingPoint(C.Structure):
+    _fields_ = [("section", C.c_int32), ("layer", C.c_int32), ("ev_start", C.c_void_p),
+                ("ev_stop", C.c_void_p)]
 
 
 _lib = None
@@ -92,6 +102,8 @@ def load() -> C.CDLL:
     lib.dflash_verify_greedy.restype = C.c_int
     lib.dflash_verify_workspace_size.argtypes = [i32, i32, i32]
     lib.dflash_verify_workspace_size.restype = C.c_size_t
+    lib.dflash_set_timing.argtypes = [vp, C.POINTER(TimingPoint), i32]
+    lib.dflash_set_timing.restype = C.c_int
     lib.dflash_status_string.argtypes = [C.c_int]
     lib.dflash_status_string.restype = C.c_char_p
     _lib = lib
@@ -198,6 +210,14 @@ class Drafter:
         torch = _torch()
         return torch.empty(self.workspace_size(max_batch, max_block, max_tokens),
                            dtype=torch.uint8, device=device)
+
+    def set_timing(self, points) -> None:
+        """points: list of (section name, layer, start event, stop event) with
+        torch.cuda.Event objects that have been recorded once (so they exist)."""
+        arr = (TimingPoint * max(1, len(points)))(*[
+            TimingPoint(SECTIONS[s], int(l), int(a.cuda_event), int(b.cuda_event))
+            for s, l, a, b in points])
+        _check(self.lib.dflash_set_timing(self.handle, arr, len(points)), "dflash_set_timing")
 
     # -------------------------------------------------------------- calls
     def fuse_context(self, feats, out, ws, stream=None) -> None:

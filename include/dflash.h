@@ -63,7 +63,7 @@ typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
 
 /* Drafter shape.  Supported: head_dim 64 or 128; hidden, ffn, n_q_heads*head_dim
  * multiples of 128; n_q_heads a multiple of n_kv_heads with
- * (n_q_heads/n_kv_heads) * block_size <= 128; n_feat_layers 1..6;
+ * (n_q_heads/n_kv_heads) * block_size <= 80; n_feat_layers 1..6;
  * 1 <= n_layers <= 16; mask_token_id in [0, vocab). */
 typedef struct {
   int32_t n_layers;
@@ -168,7 +168,8 @@ dflash_status dflash_inject_kv(dflash_handle *h, const void *ctx, const int32_t 
  * attends to every slot; a block also sees its own sequence's committed
  * context and nothing else.  Draft j is the lowest-index argmax of slot j's
  * logits through the shared LM head.
- *   anchor_ids        (device) int32 [batch]
+ *   anchor_ids        (device) int32 [batch]; an id outside [0, vocab) is
+ *                     clamped into range
  *   draft_ids         (device) int32 [batch, B-1]
  *   dbg_final_hidden  (device) float [batch*B, H] or NULL: residual stream after
  *                     the last layer
@@ -199,6 +200,36 @@ dflash_status dflash_verify_greedy(const void *target_logits, dflash_dtype dtype
                                    int32_t vocab, int32_t *accept, int32_t *bonus, void *ws,
                                    void *stream);
 size_t dflash_verify_workspace_size(int32_t batch, int32_t block_size, int32_t vocab);
+
+/* Timing hook for profiling.  Sections of the launch sequence: */
+typedef enum {
+  DFLASH_SEC_FUSE_GEMM = 1,   /* dflash_fuse_context: the fusion GEMM launches */
+  DFLASH_SEC_FUSE_NORM = 2,   /* dflash_fuse_context: the RMSNorm launch */
+  DFLASH_SEC_INJECT = 3,      /* dflash_inject_kv: RoPE table and injection GEMM launches */
+  DFLASH_SEC_EMBED = 4,       /* dflash_draft_block: block embedding */
+  DFLASH_SEC_ATTN_NORM = 5,   /* per layer: attention RMSNorm */
+  DFLASH_SEC_QKV = 6,         /* per layer: QKV projection (+RoPE, cache write) */
+  DFLASH_SEC_ATTENTION = 7,   /* per layer: block attention */
+  DFLASH_SEC_O_PROJ = 8,      /* per layer: O projection + residual */
+  DFLASH_SEC_FFN_NORM = 9,    /* per layer: FFN RMSNorm */
+  DFLASH_SEC_GATE_UP = 10,    /* per layer: gate/up projection + SwiGLU */
+  DFLASH_SEC_DOWN = 11,       /* per layer: down projection + residual */
+  DFLASH_SEC_FINAL_NORM = 12, /* final RMSNorm */
+  DFLASH_SEC_LM_HEAD = 13     /* LM head with fused argmax */
+} dflash_section;
+
+typedef struct {
+  int32_t section;   /* a dflash_section */
+  int32_t layer;     /* drafter layer for per-layer sections, else ignored */
+  void *ev_start;    /* hipEvent_t, caller-owned */
+  void *ev_stop;     /* hipEvent_t, caller-owned */
+} dflash_timing_point;
+
+/* While set, each call that launches a listed section records ev_start on its
+ * stream just before the section's first launch and ev_stop just after its
+ * last.  The handle copies up to 32 points; n = 0 clears the hook.  For
+ * profiling tools (the recorded events add stream markers, no other work). */
+dflash_status dflash_set_timing(dflash_handle *h, const dflash_timing_point *points, int32_t n);
 
 const char *dflash_status_string(dflash_status s);
 
