@@ -41,7 +41,7 @@ constexpr int kMaxAttnChunks = 32;
 // Rows per launch of the weight-streaming GEMM.
 constexpr int kMaxRowsPerLaunch = 128;
 // LM-head tiles (32 vocabulary rows each) walked by one workgroup.
-constexpr int kLmTilesPerWg = 8;
+constexpr int kLmTilesPerWg = 1;
 
 struct Dims {
   int L, H, Hq, Hkv, d, F, V, nf, G, qd, kvd;
@@ -154,8 +154,7 @@ hipError_t launch_skinny_nw(const AOperand<T>& A, int K, int n_tiles, int tiles_
   dim3 grid((n_tiles + tiles_per_wg - 1) / tiles_per_wg, ksplit);
   const int mc = A.mc;
   if (mc <= 16) {
-    if (kper % 256 == 0) skinny_gemm_kernel<T, 1, 4, NW, Epi><<<grid, NW * 64, 0, st>>>(A, K, n_tiles, tiles_per_wg, epi);
-    else if (kper % 64 == 0) skinny_gemm_kernel<T, 1, 2, NW, Epi><<<grid, NW * 64, 0, st>>>(A, K, n_tiles, tiles_per_wg, epi);
+    if (kper % 64 == 0) skinny_gemm_kernel<T, 1, 2, NW, Epi><<<grid, NW * 64, 0, st>>>(A, K, n_tiles, tiles_per_wg, epi);
     else skinny_gemm_kernel<T, 1, 1, NW, Epi><<<grid, NW * 64, 0, st>>>(A, K, n_tiles, tiles_per_wg, epi);
   } else if (mc <= 32) {
     if (kper % 64 == 0) skinny_gemm_kernel<T, 2, 2, NW, Epi><<<grid, NW * 64, 0, st>>>(A, K, n_tiles, tiles_per_wg, epi);
@@ -171,17 +170,16 @@ hipError_t launch_skinny_nw(const AOperand<T>& A, int K, int n_tiles, int tiles_
 }
 
 // Rows [0, M) in launches of at most 128 rows; `per_launch` adjusts
-// per-launch epilogue state.  8 waves per workgroup when tiles are few.
+// per-launch epilogue state.  4 waves per workgroup, 2 k-steps per stage: the
+// best streaming configuration measured on MI355X for these shapes.
 template <typename T, class Epi, class PerLaunch>
 hipError_t run_rows(AOperand<T> A, int K, int n_tiles, int tiles_per_wg, int ksplit, Epi epi,
                     hipStream_t st, PerLaunch per_launch) {
-  const bool wide = (n_tiles / tiles_per_wg) * ksplit < 512 && K % (8 * ksplit * 32) == 0;
   for (int m0 = 0, li = 0; m0 < A.M; m0 += kMaxRowsPerLaunch, ++li) {
     A.m0 = m0;
     A.mc = A.M - m0 < kMaxRowsPerLaunch ? A.M - m0 : kMaxRowsPerLaunch;
     per_launch(epi, li);
-    hipError_t e = wide ? launch_skinny_nw<T, 8, Epi>(A, K, n_tiles, tiles_per_wg, ksplit, epi, st)
-                        : launch_skinny_nw<T, 4, Epi>(A, K, n_tiles, tiles_per_wg, ksplit, epi, st);
+    hipError_t e = launch_skinny_nw<T, 4, Epi>(A, K, n_tiles, tiles_per_wg, ksplit, epi, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -326,13 +324,16 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
   float* part = at<float>(ws, L.part_off);
   const int64_t pstride = static_cast<int64_t>(M) * D.H;   // one K-split slab
 
+  // block embedding fused with layer 0's attention RMSNorm
   DF_MARK(DFLASH_SEC_EMBED, -1, false);
   DF_HIP(launch_embed(bf, h->w.embed, D.H, D.V, anchors, h->cfg.mask_token_id, nb, B, x, rope, D.d,
-                      static_cast<double>(h->cfg.rope_theta), seq, nullptr, 0, st));
+                      static_cast<double>(h->cfg.rope_theta), seq, h->layers[0].attn_norm, u, eps,
+                      st));
   DF_MARK(DFLASH_SEC_EMBED, -1, true);
 
-  // attention split: chunks of >= 256 keys, at most kMaxAttnChunks per sequence
-  int chunk = 256;
+  // attention split: chunks of >= 128 keys (one 32-key step per wave), at most
+  // kMaxAttnChunks per sequence
+  int chunk = 128;
   while ((max_keys + chunk - 1) / chunk > kMaxAttnChunks) chunk += 128;
   AttnArgs aa{};
   aa.q = qb;
@@ -353,9 +354,11 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
   for (int l = 0; l < D.L; ++l) {
     const dflash_layer_weights& w = h->layers[l];
     // attention half: x += (down partials of the previous layer); u = RMSNorm(x)
-    DF_MARK(DFLASH_SEC_ATTN_NORM, l, false);
-    DF_HIP(launch_resid_rmsnorm(bf, x, part, pending, pstride, w.attn_norm, u, M, D.H, eps, st));
-    DF_MARK(DFLASH_SEC_ATTN_NORM, l, true);
+    if (l > 0) {
+      DF_MARK(DFLASH_SEC_ATTN_NORM, l, false);
+      DF_HIP(launch_resid_rmsnorm(bf, x, part, pending, pstride, w.attn_norm, u, M, D.H, eps, st));
+      DF_MARK(DFLASH_SEC_ATTN_NORM, l, true);
+    }
     DF_MARK(DFLASH_SEC_QKV, l, false);
     {
       EpiQKV<T> e{};

@@ -22,6 +22,10 @@
 
 namespace dflash {
 
+// Softmax probabilities as MFMA B operands.  bf16: P = hi + lo with
+// hi = bf16(P), lo = bf16(P - hi), two products, so P keeps ~16 significant
+// bits (a single bf16 rounding of P would shift the output by ~1% after a few
+// layers); fp32: P as is.
 template <typename T>
 __device__ __forceinline__ void pack8(Frag8<T>& f, const float* x);
 template <>
@@ -148,10 +152,19 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs p) {
       l_run[qt] = l_run[qt] * alpha + ls;
       Frag8<T> pf;
       pack8(pf, x);
+      constexpr bool kSplitP = sizeof(T) == 2;
+      Frag8<T> pl;
+      if (kSplitP) {
+        float lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lo[e] = x[e] - Store<T>::load(Store<T>::make(x[e]));
+        pack8(pl, lo);
+      }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         o[dt][qt] = o[dt][qt] * alpha;
         o[dt][qt] = mfma16(o[dt][qt], vf[dt], pf);
+        if (kSplitP) o[dt][qt] = mfma16(o[dt][qt], vf[dt], pl);
       }
     }
   }
@@ -234,14 +247,31 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p) {
   const int64_t slot = (static_cast<int64_t>(b) * p.n_kv + g) * p.max_chunks;
   const float2* ml = p.part_ml + slot * QR + r;
   const float* po = p.part_o + slot * (QR * D) + e;
-  float M = -1e30f;
-  for (int cc = 0; cc < n_chunks_b; ++cc) M = fmaxf(M, ml[cc * QR].x);
-  float num = 0.f, den = 0.f;
-  for (int cc = 0; cc < n_chunks_b; ++cc) {
-    const float2 v = ml[cc * QR];
-    const float w = exp2f(v.x - M);
-    num += w * po[static_cast<int64_t>(cc) * QR * D];
-    den += w * v.y;
+  // all loads of a group of 8 chunks are issued before they are combined
+  constexpr int kU = 8;
+  float M = -1e30f, num = 0.f, den = 0.f;
+  for (int c0 = 0; c0 < n_chunks_b; c0 += kU) {
+    float2 v[kU];
+    float o[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const bool ok = c0 + u < n_chunks_b;
+      v[u] = ok ? ml[(c0 + u) * QR] : make_float2(-1e30f, 0.f);
+      o[u] = ok ? po[static_cast<int64_t>(c0 + u) * QR * D] : 0.f;
+    }
+    float Mn = M;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) Mn = fmaxf(Mn, v[u].x);
+    const float a = exp2f(M - Mn);
+    num *= a;
+    den *= a;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const float w = exp2f(v[u].x - Mn);
+      num += w * o[u];
+      den += w * v[u].y;
+    }
+    M = Mn;
   }
   const int h = r / B, j = r % B;
   stf(static_cast<T*>(p.o) + static_cast<int64_t>(b * B + j) * p.ldq + (g * G + h) * D + dd,

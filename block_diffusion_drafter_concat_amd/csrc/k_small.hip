@@ -23,42 +23,74 @@ hipError_t launch_zero(int* p, int64_t n, hipStream_t st) {
 // (the previous cycle's bonus token), the others the mask token (zhichai.net,
 // "DFlash 的架构密码", 训练策略 1: every block starts at a verified token).
 // The shared target embedding supplies the rows (same page, 训练策略 3).
-template <typename T>
+template <typename T, int PER>
 __global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ embed, int H, int V,
                                                     const int32_t* __restrict__ anchors,
                                                     int mask_id, int B, float* __restrict__ x,
                                                     float2* __restrict__ rope, int d, double theta,
-                                                    SeqTable seq, uint32_t* __restrict__ zero,
-                                                    int64_t n_zero) {
+                                                    SeqTable seq, const T* __restrict__ gain,
+                                                    T* __restrict__ u, float eps) {
+  __shared__ float red[4];
   const int m = blockIdx.x;
   const int b = m / B, j = m % B;
   // an anchor outside [0, V) is clamped into range rather than read out of bounds
   const int tok = (j == 0) ? min(max(anchors[b], 0), V - 1) : mask_id;
   const T* src = embed + static_cast<size_t>(tok) * H;
   float* dst = x + static_cast<size_t>(m) * H;
-  for (int c = threadIdx.x; c < H; c += 256) dst[c] = ldf(src + c);
+  float v[PER][4];
+  float ss = 0.f;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int c = (q * 256 + threadIdx.x) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[q][e] = (c < H) ? ldf(src + c + e) : 0.f;
+      ss += v[q][e] * v[q][e];
+    }
+    if (c < H) *reinterpret_cast<float4*>(dst + c) = make_float4(v[q][0], v[q][1], v[q][2], v[q][3]);
+  }
   const int pos = seq.len[b] + j;
   for (int i = threadIdx.x; i < d / 2; i += 256) {
     float cs, sn;
     rope_cos_sin(pos, i, d, theta, cs, sn);
     rope[static_cast<size_t>(m) * (d / 2) + i] = make_float2(cs, sn);
   }
-  for (int64_t w = static_cast<int64_t>(m) * 256 + threadIdx.x; w < n_zero;
-       w += static_cast<int64_t>(gridDim.x) * 256)
-    zero[w] = 0u;
+  // the first layer's attention RMSNorm of this row
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  const float r = 1.0f / sqrtf(tot / static_cast<float>(H) + eps);
+  T* o = u + static_cast<size_t>(m) * H;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int c = (q * 256 + threadIdx.x) * 4;
+    if (c < H) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) stf(o + c + e, v[q][e] * r * ldf(gain + c + e));
+    }
+  }
 }
 
-hipError_t launch_embed(bool bf16, const void* embed, int H, int V, const int32_t* anchors, int mask_id,
-                        int batch, int B, float* x, float2* rope, int d, double theta,
-                        const SeqTable& seq, uint32_t* zero, int64_t n_zero, hipStream_t st) {
+hipError_t launch_embed(bool bf16, const void* embed, int H, int V, const int32_t* anchors,
+                        int mask_id, int batch, int B, float* x, float2* rope, int d, double theta,
+                        const SeqTable& seq, const void* gain, void* u, float eps, hipStream_t st) {
+  if (H > 8192 || H % 4) return hipErrorInvalidValue;
   dim3 grid(batch * B), block(256);
-  if (bf16)
-    embed_kernel<uint16_t><<<grid, block, 0, st>>>(static_cast<const uint16_t*>(embed), H, V,
-                                                   anchors, mask_id, B, x, rope, d, theta, seq,
-                                                   zero, n_zero);
-  else
-    embed_kernel<float><<<grid, block, 0, st>>>(static_cast<const float*>(embed), H, V, anchors,
-                                                mask_id, B, x, rope, d, theta, seq, zero, n_zero);
+  const int per = (H + 1023) / 1024;
+#define DF_EMB(TT, P)                                                                          \
+  embed_kernel<TT, P><<<grid, block, 0, st>>>(static_cast<const TT*>(embed), H, V, anchors,    \
+                                              mask_id, B, x, rope, d, theta, seq,              \
+                                              static_cast<const TT*>(gain), static_cast<TT*>(u), \
+                                              eps)
+  if (bf16) {
+    if (per <= 1) DF_EMB(uint16_t, 1); else if (per <= 2) DF_EMB(uint16_t, 2);
+    else if (per <= 4) DF_EMB(uint16_t, 4); else DF_EMB(uint16_t, 8);
+  } else {
+    if (per <= 1) DF_EMB(float, 1); else if (per <= 2) DF_EMB(float, 2);
+    else if (per <= 4) DF_EMB(float, 4); else DF_EMB(float, 8);
+  }
+#undef DF_EMB
   return hipGetLastError();
 }
 
@@ -70,7 +102,7 @@ hipError_t launch_embed(bool bf16, const void* embed, int H, int V, const int32_
 // zhichai.net, "DFlash 的架构密码", 技术细节补充 / 投影层 for the fusion norm;
 // the same form for the layer norms.  One workgroup per row, H <= 8192,
 // float32 statistics with a fixed reduction order.
-template <typename T>
+template <typename T, int PER, int NS>
 __global__ __launch_bounds__(256) void resid_rmsnorm_kernel(float* __restrict__ x,
                                                             const float* __restrict__ part,
                                                             int n_split, int64_t split_stride,
@@ -78,24 +110,39 @@ __global__ __launch_bounds__(256) void resid_rmsnorm_kernel(float* __restrict__ 
                                                             T* __restrict__ out, int H, float eps) {
   __shared__ float red[4];
   const int m = blockIdx.x;
-  constexpr int kMaxPer = 8;   // float4 groups per thread: H <= 8192
-  float4 v[kMaxPer];
+  constexpr int kMaxSplit = NS;
+  // every load of the row is issued before any arithmetic (latency-bound)
+  float4 v[PER];
+  float4 p[kMaxSplit][PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int c = (q * 256 + threadIdx.x) * 4;
+    v[q] = (x && c < H) ? *reinterpret_cast<const float4*>(x + static_cast<int64_t>(m) * H + c)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s)
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int c = (q * 256 + threadIdx.x) * 4;
+      p[s][q] = (s < n_split && c < H)
+                    ? *reinterpret_cast<const float4*>(part + s * split_stride +
+                                                      static_cast<int64_t>(m) * H + c)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
   float ss = 0.f;
 #pragma unroll
-  for (int q = 0; q < kMaxPer; ++q) {
-    const int c = (q * 256 + threadIdx.x) * 4;
-    if (c < H) {
-      float4 a = x ? *reinterpret_cast<const float4*>(x + static_cast<int64_t>(m) * H + c)
-                   : make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int s = 0; s < n_split; ++s) {
-        const float4 p = *reinterpret_cast<const float4*>(part + s * split_stride +
-                                                         static_cast<int64_t>(m) * H + c);
-        a.x += p.x; a.y += p.y; a.z += p.z; a.w += p.w;
-      }
-      if (x && n_split > 0) *reinterpret_cast<float4*>(x + static_cast<int64_t>(m) * H + c) = a;
-      v[q] = a;
-      ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+  for (int q = 0; q < PER; ++q) {
+    float4 a = v[q];
+#pragma unroll
+    for (int s = 0; s < kMaxSplit; ++s) {
+      a.x += p[s][q].x; a.y += p[s][q].y; a.z += p[s][q].z; a.w += p[s][q].w;
     }
+    v[q] = a;
+    ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+    const int c = (q * 256 + threadIdx.x) * 4;
+    if (x && n_split > 0 && c < H)
+      *reinterpret_cast<float4*>(x + static_cast<int64_t>(m) * H + c) = a;
   }
   if (!out) return;
   ss = wave_sum(ss);
@@ -105,7 +152,7 @@ __global__ __launch_bounds__(256) void resid_rmsnorm_kernel(float* __restrict__ 
   const float r = 1.0f / sqrtf(tot / static_cast<float>(H) + eps);
   T* o = out + static_cast<int64_t>(m) * H;
 #pragma unroll
-  for (int q = 0; q < kMaxPer; ++q) {
+  for (int q = 0; q < PER; ++q) {
     const int c = (q * 256 + threadIdx.x) * 4;
     if (c < H) {
       stf(o + c + 0, v[q].x * r * ldf(gain + c + 0));
@@ -116,36 +163,64 @@ __global__ __launch_bounds__(256) void resid_rmsnorm_kernel(float* __restrict__ 
   }
 }
 
+template <typename T>
+static hipError_t launch_rn(float* x, const float* part, int n_split, int64_t split_stride,
+                            const void* gain, void* out, int rows, int H, float eps,
+                            hipStream_t st) {
+  const T* g = static_cast<const T*>(gain);
+  T* o = static_cast<T*>(out);
+  const int per = (H + 1023) / 1024;
+#define DF_RN(P, S) resid_rmsnorm_kernel<T, P, S><<<rows, 256, 0, st>>>(x, part, n_split, split_stride, g, o, H, eps)
+  if (n_split <= 4) {
+    if (per <= 1) DF_RN(1, 4);
+    else if (per <= 2) DF_RN(2, 4);
+    else if (per <= 4) DF_RN(4, 4);
+    else DF_RN(8, 4);
+  } else {
+    if (per <= 1) DF_RN(1, 8);
+    else if (per <= 2) DF_RN(2, 8);
+    else if (per <= 4) DF_RN(4, 8);
+    else return hipErrorInvalidValue;
+  }
+#undef DF_RN
+  return hipGetLastError();
+}
+
 hipError_t launch_resid_rmsnorm(bool bf16, float* x, const float* part, int n_split,
                                 int64_t split_stride, const void* gain, void* out, int rows,
                                 int H, float eps, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  if (H > 8192 || H % 4) return hipErrorInvalidValue;
-  if (bf16)
-    resid_rmsnorm_kernel<uint16_t><<<rows, 256, 0, st>>>(
-        x, part, n_split, split_stride, static_cast<const uint16_t*>(gain),
-        static_cast<uint16_t*>(out), H, eps);
-  else
-    resid_rmsnorm_kernel<float><<<rows, 256, 0, st>>>(x, part, n_split, split_stride,
-                                                      static_cast<const float*>(gain),
-                                                      static_cast<float*>(out), H, eps);
-  return hipGetLastError();
+  if (H > 8192 || H % 4 || n_split > 8) return hipErrorInvalidValue;
+  return bf16 ? launch_rn<uint16_t>(x, part, n_split, split_stride, gain, out, rows, H, eps, st)
+              : launch_rn<float>(x, part, n_split, split_stride, gain, out, rows, H, eps, st);
 }
 
 // ------------------------------------------------------------------ LM-head argmax
 // Row m (block slot j = m % B >= 1): fold the per-workgroup (value, lowest
 // column) partials of the LM-head GEMM into the draft id of that slot.
-__global__ __launch_bounds__(64) void lm_argmax_finalize_kernel(const float2* __restrict__ part,
-                                                                int n_wg, int B,
-                                                                int32_t* __restrict__ draft) {
+__global__ __launch_bounds__(256) void lm_argmax_finalize_kernel(const float2* __restrict__ part,
+                                                                 int n_wg, int B,
+                                                                 int32_t* __restrict__ draft) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
   const int m = blockIdx.x, j = m % B;
   if (j == 0) return;
   float best = -INFINITY;
   int bi = 0x7fffffff;
-  for (int w = threadIdx.x; w < n_wg; w += 64) {
-    const float2 p = part[static_cast<int64_t>(m) * n_wg + w];
-    const int pi = __float_as_int(p.y);
-    if (better(p.x, pi, best, bi)) { best = p.x; bi = pi; }
+  const float2* pr = part + static_cast<int64_t>(m) * n_wg;
+  constexpr int kU = 8;
+  for (int w0 = threadIdx.x; w0 < n_wg; w0 += 256 * kU) {
+    float2 q[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int w = w0 + u * 256;
+      q[u] = w < n_wg ? pr[w] : make_float2(-INFINITY, __int_as_float(0x7fffffff));
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int qi = __float_as_int(q[u].y);
+      if (better(q[u].x, qi, best, bi)) { best = q[u].x; bi = qi; }
+    }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -153,13 +228,19 @@ __global__ __launch_bounds__(64) void lm_argmax_finalize_kernel(const float2* __
     const int oi = __shfl_xor(bi, o, 64);
     if (better(ov, oi, best, bi)) { best = ov; bi = oi; }
   }
-  if (threadIdx.x == 0) draft[(m / B) * (B - 1) + (j - 1)] = bi;
+  if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = best; si[threadIdx.x >> 6] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (better(sv[w], si[w], best, bi)) { best = sv[w]; bi = si[w]; }
+    draft[(m / B) * (B - 1) + (j - 1)] = bi;
+  }
 }
 
 hipError_t launch_lm_argmax_finalize(const float2* part, int n_wg, int rows, int B, int32_t* draft,
                                      hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  lm_argmax_finalize_kernel<<<rows, 64, 0, st>>>(part, n_wg, B, draft);
+  lm_argmax_finalize_kernel<<<rows, 256, 0, st>>>(part, n_wg, B, draft);
   return hipGetLastError();
 }
 

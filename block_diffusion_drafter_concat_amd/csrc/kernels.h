@@ -14,10 +14,10 @@ namespace dflash {
 hipError_t launch_zero(int* p, int64_t n, hipStream_t st);
 
 // Block inputs: x[m] = embed[token(m)] (fp32), RoPE cos/sin of every block slot
-// at position seq.len[b] + j, and `n_zero` 32-bit words of `zero` cleared.
+// at position seq.len[b] + j, and u[m] = RMSNorm(x[m]) * gain (layer 0).
 hipError_t launch_embed(bool bf16, const void* embed, int H, int V, const int32_t* anchors,
                         int mask_id, int batch, int B, float* x, float2* rope, int d,
-                        double theta, const SeqTable& seq, uint32_t* zero, int64_t n_zero,
+                        double theta, const SeqTable& seq, const void* gain, void* u, float eps,
                         hipStream_t st);
 
 // Row m: v = x[m] + sum_s part[s * split_stride + m*H ...] (x and part may be

@@ -62,19 +62,34 @@ def synthetic_cache(shape, wid, lens, std=1.28):
 
 
 def draft_compare(shape, res, ids_gpu, hid_gpu, z_gpu, label=""):
-    """Draft ids bit-exact outside the top-2 gap exemption; floats within tol."""
+    """Floats within tolerance; draft ids bit-exact wherever the logits decide them.
+
+    A draft id is compared bit-exactly when the oracle's top-2 logit gap is at
+    least ``gate``: 1e-2 for float32 workloads; for bf16 workloads the larger
+    of 1e-2 and twice the measured max |logit difference|, because bf16
+    storage makes two correct implementations differ by up to that much.  An
+    exempt id must still be a near-argmax of the oracle's logits (within gate).
+    """
     t = tol(shape)
     e_h = rel_err(hid_gpu, res["final_hidden"].reshape(hid_gpu.shape))
     e_z = rel_err(z_gpu, res["logits"].reshape(z_gpu.shape))
+    zo = res["logits"]                                  # [N, B, V]
+    dz = float(np.max(np.abs(np.asarray(z_gpu, dtype=np.float64).reshape(zo.shape) - zo)))
+    gate = 1e-2 if shape.dtype == "f32" else max(1e-2, 2.0 * dz)
     want = res["draft_ids"]
-    ok = res["gap"] >= 1e-2
+    assert ids_gpu.min() >= 0 and ids_gpu.max() < shape.vocab, ids_gpu
+    ok = res["gap"] >= gate
     mism = (ids_gpu != want) & ok
-    info = (f"{label} final_hidden rel {e_h:.2e}, logits rel {e_z:.2e}, "
-            f"exempt {int((~ok).sum())}/{ok.size}, mismatches {int(mism.sum())}")
+    z1 = zo[:, 1:, :]
+    picked = np.take_along_axis(z1, ids_gpu[..., None].astype(np.int64), axis=2)[..., 0]
+    near = picked >= z1.max(axis=2) - gate
+    info = (f"{label} final_hidden rel {e_h:.2e}, logits rel {e_z:.2e} (max abs {dz:.3e}), "
+            f"gate {gate:.3e}, exempt {int((~ok).sum())}/{ok.size}, mismatches {int(mism.sum())}")
     print(info, flush=True)
     assert e_h <= t, info
     assert e_z <= t, info
     assert not mism.any(), info
+    assert near.all(), info
     return e_h, e_z
 
 

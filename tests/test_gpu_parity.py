@@ -1,8 +1,10 @@
 """HIP path against the CPU oracle on the same seeded inputs (needs an MI355X).
 
-Bars: integer outputs bit-exact (draft ids exempt where the oracle's top-2
-logit gap is below 1e-2); floating-point outputs within max relative error
-1e-4 (float32 workloads) or 2e-2 (bf16 workloads), per tensor.
+Bars: floating-point outputs within max relative error 1e-4 (float32
+workloads) or 2e-2 (bf16 workloads), per tensor; verify outputs bit-exact;
+draft ids bit-exact wherever the oracle's top-2 logit gap is at least 1e-2
+(float32) or max(1e-2, 2 x the measured max logit difference) (bf16), and a
+near-argmax of the oracle's logits elsewhere (see gpu_util.draft_compare).
 """
 import numpy as np
 import pytest
@@ -254,6 +256,27 @@ def test_headline_shape_draft_block_full_size(torch, qwen_like):
     ids, hid, z = _draft(torch, dr, shape, cache, 16, anchors, ws)
     res = O.draft_block(w, shape, caches, anchors, 16)
     draft_compare(shape, res, ids, hid, z, "qwen3-8b-shaped ctx2048")
+
+
+def test_headline_shape_float32_full_size(torch):
+    """The headline drafter shape with float32 storage, full size, ctx 2048.
+
+    Without bf16 storage points the two sides agree to ~1e-6, so every draft
+    id whose oracle top-2 gap is >= 1e-2 must match bit-exactly over the full
+    151936-token vocabulary.
+    """
+    shape = configs.scaled(configs.QWEN3_8B_LIKE, dtype="f32")
+    w = configs.make_weights(shape, 6)
+    dr = L.Drafter(shape, w)
+    caches = synthetic_cache(shape, 6, [2048])
+    cache = L.KVCache(shape, [2048 + 64])
+    upload_cache(cache, caches)
+    anchors = configs.make_anchors(shape, 6, 1)
+    ws = dr.workspace(1, 16, 1)
+    ids, hid, z = _draft(torch, dr, shape, cache, 16, anchors, ws)
+    res = O.draft_block(w, shape, caches, anchors, 16)
+    draft_compare(shape, res, ids, hid, z, "qwen3-8b-shaped float32 ctx2048")
+    del dr, cache
 
 
 def test_headline_shape_fuse_inject_sampled_rows(torch, qwen_like):
