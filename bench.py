@@ -47,7 +47,41 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-timing-pass", action="store_true",
+                    help="skip the per-section timing pass (for counter collection)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB, 5 times "
+                         "(scale reference for HBM byte counters) and exit")
     return ap.parse_args()
+
+
+def calibrate_copy(mib: int) -> None:
+    import torch
+    n = mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}), flush=True)
+
+
+def lm_head_traffic():
+    """HBM bytes per LM-head launch from the committed rocprofv3 counter record,
+    or None when the kernel's sources differ from the ones it was taken on."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "counters_lm_head.json")
+    try:
+        rec = json.load(open(path))
+        h = hashlib.sha256()
+        for f in rec["sources"]:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if h.hexdigest() != rec["sources_sha256"]:
+            return None
+        return int(rec["fetch_kib_per_launch"] * 1024 * rec["fetch_scale"] +
+                   rec["write_kib_per_launch"] * 1024 * rec["write_scale"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def step_bytes(shape, n_new: int) -> dict:
@@ -81,6 +115,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     L.load()
     shape = configs.QWEN3_8B_LIKE
     wid = 2
@@ -151,6 +188,9 @@ def main():
     log(f"timed: {K} steps, {ms_per_step:.3f} ms/step (wall {wall * 1e3 / K:.3f} ms/step)")
 
     # ---- kernel-timing pass: HIP events around each section, same steps
+    if args.no_timing_pass:
+        print(json.dumps({"value": round(blocks_per_s, 2), "ms_per_step": ms_per_step}))
+        return
     sections = [("lm_head", -1), ("fuse_gemm", -1), ("inject", -1), ("embed", -1),
                 ("final_norm", -1)]
     for l in range(shape.n_layers):
@@ -187,7 +227,7 @@ def main():
     lm_gbs = lm_bytes / (lm_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "kernel": "skinny_gemm_kernel<EpiLMHead> (LM head + argmax)",
                 "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": lm_head_traffic(),
                 "bytes_per_launch": lm_bytes, "avg_launch_us": round(lm_ms * 1e3, 2)}
 
     # per-kernel HBM fractions of the weight-streaming GEMMs (per launch)
