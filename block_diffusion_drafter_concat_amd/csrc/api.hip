@@ -345,6 +345,7 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
   aa.B = B;
   aa.G = D.G;
   aa.n_kv = D.Hkv;
+  aa.head_dim = D.d;
   aa.chunk = chunk;
   aa.max_chunks = (max_keys + chunk - 1) / chunk;
   aa.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(D.d)));

@@ -9,15 +9,18 @@
 // contiguous rows [0, len + B) of its slab.
 //
 // Work split (HBM-bound over the K/V stream): workgroup = (context chunk,
-// kv-head g, sequence b), 4 waves, each wave takes every 4th 32-key step.
-// All G*B queries of the kv-head (G = q heads per kv head) ride along as MFMA
-// columns, so each K/V byte is read once per workgroup:
+// kv-head g, sequence b) with one wave per 16-query tile; the G*B queries of
+// the kv head (G = q heads per kv head) are MFMA columns.  Every wave walks
+// the whole chunk in 32-key steps with the next step's K/V fragments in
+// flight; the waves of a workgroup read the same keys, so the repeats hit
+// L1/L2 and HBM sees each K/V byte once.  No cross-wave merge is needed.
 //   S^T[keys x queries] = K[keys x d] . Q^T   (K rows permuted so that the
 //                                             C layout equals the next B layout)
 //   O^T[d x queries]   += V^T[d x keys] . P^T (V^T straight from the transposed
 //                                             V cache, 16 contiguous bytes/lane)
 // Softmax is online in fp32 (base-2 with the scale folded in).  Chunks meet in
-// the workspace; a separate merge kernel combines them in chunk order.
+// the workspace in MFMA C-layout order; a merge kernel combines them in chunk
+// order.
 #include "kernels_attn.h"
 
 namespace dflash {
@@ -57,16 +60,28 @@ __device__ __forceinline__ void mask_tail(Frag8<float>& f, int first, int end) {
   pack8(f, w);
 }
 
+// Output element (query row r, head dim d) of a kv head's G*B x D block goes
+// to o[(b*B + j) * ldq + (g*G + h) * D + d] with r = h*B + j.
+template <typename T>
+__device__ __forceinline__ void store_out4(const AttnArgs& p, int b, int g, int r, int d,
+                                           const float* v) {
+  const int B = p.B, G = p.G, D = p.head_dim;
+  const int h = r / B, j = r % B;
+  T* o = static_cast<T*>(p.o) + static_cast<int64_t>(b * B + j) * p.ldq + (g * G + h) * D + d;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) stf(o + jj, v[jj]);
+}
+
+// Partial of chunk c of (b, g): O^T fragments in C-layout order
+// part_o[slot][qt][dt][lane] (float4 over jj) and (max, sum) per query row.
 template <typename T, int D, int NQ>
-__global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs p) {
+__global__ __launch_bounds__(NQ * 64) void block_attn_kernel(AttnArgs p) {
   constexpr int DS = D / 32;   // 32-wide k steps over the head dimension
   constexpr int DT = D / 16;   // 16-row tiles of O^T
   constexpr int QR = NQ * 16;  // query rows (padded)
-  __shared__ float s_m[4][QR], s_l[4][QR];
-  __shared__ float s_o[QR][D + 4];
 
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int qt = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r16 = lane & 15, kg = lane >> 4;
   const int B = p.B, G = p.G, GB = G * B;
   const int n_keys = p.seq.len[b] + B;
@@ -77,214 +92,181 @@ __global__ __launch_bounds__(256) void block_attn_kernel(AttnArgs p) {
   const int64_t base = p.seq.off[b];
   const T* Kg = static_cast<const T*>(p.kc) + static_cast<int64_t>(g) * p.cap * D;
   const T* Vg = static_cast<const T*>(p.vc) + static_cast<int64_t>(g) * D * p.cap;
-  const T* q = static_cast<const T*>(p.q);
+  const int r = qt * 16 + r16;   // this lane's query row (MFMA column)
 
-  Frag8<T> qf[NQ][DS];
+  Frag8<T> qf[DS];
+  if (r < GB) {
+    const int h = r / B, j = r % B;
+    const T* qrow = static_cast<const T*>(p.q) + static_cast<int64_t>(b * B + j) * p.ldq +
+                    (g * G + h) * D + kg * 8;
 #pragma unroll
-  for (int qt = 0; qt < NQ; ++qt) {
-    const int r = qt * 16 + r16;
-    if (r < GB) {
-      const int h = r / B, j = r % B;
-      const T* qrow = q + static_cast<int64_t>(b * B + j) * p.ldq + (g * G + h) * D;
+    for (int ds = 0; ds < DS; ++ds) ld_frag(qf[ds], qrow + ds * 32);
+  } else {
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) ld_frag(qf[qt][ds], qrow + ds * 32 + kg * 8);
-    } else {
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) zero_frag(qf[qt][ds]);
-    }
+    for (int ds = 0; ds < DS; ++ds) zero_frag(qf[ds]);
   }
 
-  float m_run[NQ], l_run[NQ];
-  f32x4 o[DT][NQ];
+  float m_run = -1e30f, l_run = 0.f;
+  f32x4 o[DT];
 #pragma unroll
-  for (int qt = 0; qt < NQ; ++qt) {
-    m_run[qt] = -1e30f;
-    l_run[qt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt][qt] = zero4();
-  }
+  for (int dt = 0; dt < DT; ++dt) o[dt] = zero4();
 
-  for (int kb = kbeg + wave * 32; kb < kend; kb += 128) {
-    Frag8<T> kf[2][DS];
+  // K fragment rows: tile t row rr <-> key kb + (rr/4)*8 + t*4 + rr%4, so the
+  // S^T C layout gives lane group kg the 8 consecutive keys kb + kg*8 .. +8.
+  Frag8<T> kf[2][2][DS], vf[2][DT];
+  auto load = [&](int buf, int kb) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int key = min(kb + (r16 >> 2) * 8 + t * 4 + (r16 & 3), n_keys - 1);
       const T* krow = Kg + (base + key) * D + kg * 8;
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) ld_frag(kf[t][ds], krow + ds * 32);
+      for (int ds = 0; ds < DS; ++ds) ld_frag(kf[buf][t][ds], krow + ds * 32);
     }
-    Frag8<T> vf[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
-      ld_frag(vf[dt], Vg + static_cast<int64_t>(dt * 16 + r16) * p.cap + base + kb + kg * 8);
+      ld_frag(vf[buf][dt], Vg + static_cast<int64_t>(dt * 16 + r16) * p.cap + base + kb + kg * 8);
+  };
+  auto step = [&](int buf, int kb) {
     if (kb + 32 > kend) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) mask_tail(vf[dt], kb + kg * 8, kend);
+      for (int dt = 0; dt < DT; ++dt) mask_tail(vf[buf][dt], kb + kg * 8, kend);
+    }
+    f32x4 s0 = zero4(), s1 = zero4();
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      s0 = mfma16(s0, kf[buf][0][ds], qf[ds]);
+      s1 = mfma16(s1, kf[buf][1][ds], qf[ds]);
+    }
+    float x[8];
+    float mx = m_run;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = (e < 4 ? s0[e] : s1[e - 4]) * p.scale_log2;
+      if (kb + kg * 8 + e >= kend) v = -INFINITY;
+      x[e] = v;
+      mx = fmaxf(mx, v);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float alpha = exp2f(m_run - mx);
+    m_run = mx;
+    float ls = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[e] = exp2f(x[e] - mx);
+      ls += x[e];
+    }
+    l_run = l_run * alpha + ls;
+    Frag8<T> pf;
+    pack8(pf, x);
+    constexpr bool kSplitP = sizeof(T) == 2;
+    Frag8<T> pl;
+    if (kSplitP) {
+      float lo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lo[e] = x[e] - Store<T>::load(Store<T>::make(x[e]));
+      pack8(pl, lo);
     }
 #pragma unroll
-    for (int qt = 0; qt < NQ; ++qt) {
-      f32x4 s0 = zero4(), s1 = zero4();
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        s0 = mfma16(s0, kf[0][ds], qf[qt][ds]);
-        s1 = mfma16(s1, kf[1][ds], qf[qt][ds]);
-      }
-      // this lane: query qt*16 + r16, keys kb + kg*8 + e, e = t*4 + jj
-      float x[8];
-      float mx = m_run[qt];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float v = (e < 4 ? s0[e] : s1[e - 4]) * p.scale_log2;
-        if (kb + kg * 8 + e >= kend) v = -INFINITY;
-        x[e] = v;
-        mx = fmaxf(mx, v);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float alpha = exp2f(m_run[qt] - mx);
-      m_run[qt] = mx;
-      float ls = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        x[e] = exp2f(x[e] - mx);
-        ls += x[e];
-      }
-      l_run[qt] = l_run[qt] * alpha + ls;
-      Frag8<T> pf;
-      pack8(pf, x);
-      constexpr bool kSplitP = sizeof(T) == 2;
-      Frag8<T> pl;
-      if (kSplitP) {
-        float lo[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) lo[e] = x[e] - Store<T>::load(Store<T>::make(x[e]));
-        pack8(pl, lo);
-      }
+    for (int dt = 0; dt < DT; ++dt) {
+      o[dt] = o[dt] * alpha;
+      o[dt] = mfma16(o[dt], vf[buf][dt], pf);
+      if (kSplitP) o[dt] = mfma16(o[dt], vf[buf][dt], pl);
+    }
+  };
+  load(0, kbeg);
+  int kb = kbeg;
+  for (; kb + 32 < kend; kb += 64) {
+    load(1, kb + 32);
+    step(0, kb);
+    if (kb + 64 < kend) load(0, kb + 64);
+    step(1, kb + 32);
+  }
+  if (kb < kend) step(0, kb);
+
+  float l = l_run;
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (n_chunks_b == 1) {
+    if (r < GB) {
+      const float inv = 1.0f / l;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        o[dt][qt] = o[dt][qt] * alpha;
-        o[dt][qt] = mfma16(o[dt][qt], vf[dt], pf);
-        if (kSplitP) o[dt][qt] = mfma16(o[dt][qt], vf[dt], pl);
+        const float v[4] = {o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv};
+        store_out4<T>(p, b, g, r, dt * 16 + kg * 4, v);
       }
-    }
-  }
-
-  // ---- waves of this workgroup meet in LDS
-#pragma unroll
-  for (int qt = 0; qt < NQ; ++qt) {
-    float l = l_run[qt];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    if (kg == 0) {
-      s_m[wave][qt * 16 + r16] = m_run[qt];
-      s_l[wave][qt * 16 + r16] = l;
-    }
-  }
-  __syncthreads();
-  float scale_w[NQ];
-#pragma unroll
-  for (int qt = 0; qt < NQ; ++qt) {
-    const int r = qt * 16 + r16;
-    const float M = fmaxf(fmaxf(s_m[0][r], s_m[1][r]), fmaxf(s_m[2][r], s_m[3][r]));
-    scale_w[qt] = exp2f(m_run[qt] - M);
-  }
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w) {
-#pragma unroll
-      for (int qt = 0; qt < NQ; ++qt)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            float& dst = s_o[qt * 16 + r16][dt * 16 + kg * 4 + jj];
-            const float v = o[dt][qt][jj] * scale_w[qt];
-            dst = (w == 0) ? v : dst + v;
-          }
-    }
-    __syncthreads();
-  }
-
-  const int t = threadIdx.x;
-  T* out = static_cast<T*>(p.o);
-  if (n_chunks_b == 1) {
-    for (int e = t; e < GB * D; e += 256) {
-      const int r = e / D, dd = e % D;
-      const float M = fmaxf(fmaxf(s_m[0][r], s_m[1][r]), fmaxf(s_m[2][r], s_m[3][r]));
-      const float L = s_l[0][r] * exp2f(s_m[0][r] - M) + s_l[1][r] * exp2f(s_m[1][r] - M) +
-                      s_l[2][r] * exp2f(s_m[2][r] - M) + s_l[3][r] * exp2f(s_m[3][r] - M);
-      const int h = r / B, j = r % B;
-      stf(out + static_cast<int64_t>(b * B + j) * p.ldq + (g * G + h) * D + dd, s_o[r][dd] / L);
     }
     return;
   }
-
-  // ---- several chunks: publish this chunk's (unnormalised O, max, sum); the
-  // merge kernel combines the chunks of a (sequence, kv head) in chunk order
-  const int64_t slot = (static_cast<int64_t>(b) * p.n_kv + g) * p.max_chunks;
-  float* po = p.part_o + (slot + c) * (QR * D);
-  float2* pml = p.part_ml + (slot + c) * QR;
-  for (int e = t; e < GB * D; e += 256) po[e] = s_o[e / D][e % D];
-  for (int r = t; r < GB; r += 256) {
-    const float M = fmaxf(fmaxf(s_m[0][r], s_m[1][r]), fmaxf(s_m[2][r], s_m[3][r]));
-    const float L = s_l[0][r] * exp2f(s_m[0][r] - M) + s_l[1][r] * exp2f(s_m[1][r] - M) +
-                    s_l[2][r] * exp2f(s_m[2][r] - M) + s_l[3][r] * exp2f(s_m[3][r] - M);
-    pml[r] = make_float2(M, L);
-  }
+  const int64_t slot = (static_cast<int64_t>(b) * p.n_kv + g) * p.max_chunks + c;
+  float4* po = reinterpret_cast<float4*>(p.part_o) + (slot * NQ + qt) * DT * 64 + lane;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) po[dt * 64] = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+  if (kg == 0) p.part_ml[slot * QR + r] = make_float2(m_run, l);
 }
 
-// One workgroup per (row block of 256 output elements, kv head, sequence):
-// o = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c over the sequence's chunks.
-template <typename T, int D, int QR>
+// One thread per (query tile, 16-row d tile, lane) of a (kv head, sequence):
+// o = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c over the sequence's chunks,
+// in chunk order, all loads of 8 chunks issued before they are combined.
+template <typename T, int D, int NQ>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p) {
+  constexpr int DT = D / 16, QR = NQ * 16;
   const int g = blockIdx.y, b = blockIdx.z;
   const int B = p.B, G = p.G, GB = G * B;
   const int n_keys = p.seq.len[b] + B;
   const int n_chunks_b = (n_keys + p.chunk - 1) / p.chunk;
   if (n_chunks_b <= 1) return;   // written directly by the attention kernel
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= GB * D) return;
-  const int r = e / D, dd = e % D;
-  const int64_t slot = (static_cast<int64_t>(b) * p.n_kv + g) * p.max_chunks;
-  const float2* ml = p.part_ml + slot * QR + r;
-  const float* po = p.part_o + slot * (QR * D) + e;
-  // all loads of a group of 8 chunks are issued before they are combined
+  const int e = blockIdx.x * 256 + threadIdx.x;   // (qt, dt, lane)
+  if (e >= NQ * DT * 64) return;
+  const int lane = e & 63, dt = (e >> 6) % DT, qt = (e >> 6) / DT;
+  const int r = qt * 16 + (lane & 15);
+  if (r >= GB) return;
+  const int64_t slot0 = (static_cast<int64_t>(b) * p.n_kv + g) * p.max_chunks;
+  const float2* ml = p.part_ml + slot0 * QR + r;
+  const float4* po = reinterpret_cast<const float4*>(p.part_o) + (slot0 * NQ + qt) * DT * 64 +
+                     dt * 64 + lane;
   constexpr int kU = 8;
-  float M = -1e30f, num = 0.f, den = 0.f;
+  float M = -1e30f, den = 0.f;
+  float num[4] = {0.f, 0.f, 0.f, 0.f};
   for (int c0 = 0; c0 < n_chunks_b; c0 += kU) {
     float2 v[kU];
-    float o[kU];
+    float4 w4[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const bool ok = c0 + u < n_chunks_b;
-      v[u] = ok ? ml[(c0 + u) * QR] : make_float2(-1e30f, 0.f);
-      o[u] = ok ? po[static_cast<int64_t>(c0 + u) * QR * D] : 0.f;
+      v[u] = ok ? ml[static_cast<int64_t>(c0 + u) * QR] : make_float2(-1e30f, 0.f);
+      w4[u] = ok ? po[static_cast<int64_t>(c0 + u) * NQ * DT * 64] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     float Mn = M;
 #pragma unroll
     for (int u = 0; u < kU; ++u) Mn = fmaxf(Mn, v[u].x);
     const float a = exp2f(M - Mn);
-    num *= a;
     den *= a;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) num[jj] *= a;
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const float w = exp2f(v[u].x - Mn);
-      num += w * o[u];
       den += w * v[u].y;
+      num[0] += w * w4[u].x;
+      num[1] += w * w4[u].y;
+      num[2] += w * w4[u].z;
+      num[3] += w * w4[u].w;
     }
     M = Mn;
   }
-  const int h = r / B, j = r % B;
-  stf(static_cast<T*>(p.o) + static_cast<int64_t>(b * B + j) * p.ldq + (g * G + h) * D + dd,
-      num / den);
+  const float inv = 1.0f / den;
+  const float out[4] = {num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv};
+  store_out4<T>(p, b, g, r, dt * 16 + (lane >> 4) * 4, out);
 }
 
 template <typename T, int D, int NQ>
 static hipError_t launch_attn_nq(const AttnArgs& a, dim3 grid, int batch, hipStream_t st) {
-  block_attn_kernel<T, D, NQ><<<grid, 256, 0, st>>>(a);
+  block_attn_kernel<T, D, NQ><<<grid, NQ * 64, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_chunks <= 1) return e;
-  dim3 mgrid((a.G * a.B * D + 255) / 256, a.n_kv, batch);
-  attn_merge_kernel<T, D, NQ * 16><<<mgrid, 256, 0, st>>>(a);
+  dim3 mgrid((NQ * (D / 16) * 64 + 255) / 256, a.n_kv, batch);
+  attn_merge_kernel<T, D, NQ><<<mgrid, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -12,9 +12,10 @@ struct AttnArgs {
   const void* vc;       // layer V cache [n_kv][D][cap]
   int64_t cap;
   void* o;              // [batch*B, n_q*D] attention output
-  float* part_o;        // [batch][n_kv][max_chunks][ceil16(G*B)][D]
+  float* part_o;        // [batch][n_kv][max_chunks][NQ][D/16][64 lanes][4] (C layout)
   float2* part_ml;      // [batch][n_kv][max_chunks][ceil16(G*B)]  (max, sum), base 2
   int B, G, n_kv;
+  int head_dim;
   int chunk;            // keys per workgroup, multiple of 128
   int max_chunks;       // grid.x
   float scale_log2;     // log2(e) / sqrt(D)
