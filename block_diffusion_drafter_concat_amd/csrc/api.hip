@@ -93,7 +93,7 @@ GemmPlan gemm_plan(const Dims& D) {
 // Every call lays out its own scratch from offset 0 with sizes that grow with
 // (batch, block, tokens); dflash_workspace_size takes the largest.
 struct Layout {
-  size_t rope_off, x_off, u_off, q_off, o_off, h_off, part_off, lm_off, ao_off, aml_off, ver_off;
+  size_t x_off, u_off, q_off, o_off, h_off, part_off, lm_off, ao_off, aml_off, ver_off;
   size_t total;
 };
 
@@ -105,8 +105,6 @@ Layout layout(const dflash_handle* h, int max_batch, int max_block, int64_t max_
   const GemmPlan g = gemm_plan(D);
   Layout L{};
   size_t off = 0;
-  const size_t rope_rows = M > T ? M : T;
-  L.rope_off = off; off += align_up(rope_rows * (D.d / 2) * 8);
   L.x_off = off;    off += align_up(M * D.H * 4);
   L.u_off = off;    off += align_up(M * D.H * es);
   L.q_off = off;    off += align_up(M * D.qd * es);
@@ -139,6 +137,15 @@ hipError_t mark(const dflash_handle* h, int section, int layer, bool stop, hipSt
   return hipSuccess;
 }
 #define DF_MARK(sec, layer, stop) DF_HIP(mark(h, sec, layer, stop, st))
+
+// RoPE inverse frequencies theta^(-2i/d) in double.
+RopeFreq rope_freq(const dflash_config& c) {
+  RopeFreq f{};
+  for (int i = 0; i < c.head_dim / 2 && i < 64; ++i)
+    f.inv[i] = pow(static_cast<double>(c.rope_theta),
+                   -2.0 * static_cast<double>(i) / static_cast<double>(c.head_dim));
+  return f;
+}
 
 template <typename P> P* at(void* ws, size_t off) {
   return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
@@ -174,12 +181,15 @@ hipError_t launch_skinny_nw(const AOperand<T>& A, int K, int n_tiles, int tiles_
 // best streaming configuration measured on MI355X for these shapes.
 template <typename T, class Epi, class PerLaunch>
 hipError_t run_rows(AOperand<T> A, int K, int n_tiles, int tiles_per_wg, int ksplit, Epi epi,
-                    hipStream_t st, PerLaunch per_launch) {
+                    hipStream_t st, PerLaunch per_launch, int nw = 4) {
+  if (nw == 8 && K % (8 * ksplit * 32) != 0) nw = 4;
   for (int m0 = 0, li = 0; m0 < A.M; m0 += kMaxRowsPerLaunch, ++li) {
     A.m0 = m0;
     A.mc = A.M - m0 < kMaxRowsPerLaunch ? A.M - m0 : kMaxRowsPerLaunch;
     per_launch(epi, li);
-    hipError_t e = launch_skinny_nw<T, 4, Epi>(A, K, n_tiles, tiles_per_wg, ksplit, epi, st);
+    hipError_t e = nw == 8
+                       ? launch_skinny_nw<T, 8, Epi>(A, K, n_tiles, tiles_per_wg, ksplit, epi, st)
+                       : launch_skinny_nw<T, 4, Epi>(A, K, n_tiles, tiles_per_wg, ksplit, epi, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -275,9 +285,7 @@ dflash_status inject_impl(dflash_handle* h, const void* ctx, const SeqTable& seq
   const Dims D = dims(h->cfg);
   const Layout L = layout(h, 1, 1, total);
   const GemmPlan g = gemm_plan(D);
-  float2* rope = at<float2>(ws, L.rope_off);
   DF_MARK(DFLASH_SEC_INJECT, -1, false);
-  DF_HIP(launch_rope_rows(rope, total, D.d, static_cast<double>(h->cfg.rope_theta), seq, st));
   EpiInject<T> epi{};
   for (int l = 0; l < D.L; ++l) {
     epi.wk[l] = static_cast<const T*>(h->layers[l].wk);
@@ -289,7 +297,7 @@ dflash_status inject_impl(dflash_handle* h, const void* ctx, const SeqTable& seq
   epi.d = D.d;
   epi.Hkv = D.Hkv;
   epi.cap = kv->cap_total;
-  epi.rope = rope;
+  epi.freq = rope_freq(h->cfg);
   epi.seq = seq;
   DF_HIP(run_rows<T>(a_single<T>(ctx, D.H, D.H, total), D.H, g.tiles_inj, 1, 1, epi, st,
                      NoPerLaunch{}));
@@ -315,7 +323,7 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
     seq.off[b] = kv->seq_off[b];
     max_keys = (kv->seq_len[b] + B > max_keys) ? kv->seq_len[b] + B : max_keys;
   }
-  float2* rope = at<float2>(ws, L.rope_off);
+  const RopeFreq freq = rope_freq(h->cfg);
   float* x = at<float>(ws, L.x_off);
   T* u = at<T>(ws, L.u_off);
   T* qb = at<T>(ws, L.q_off);
@@ -326,9 +334,8 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
 
   // block embedding fused with layer 0's attention RMSNorm
   DF_MARK(DFLASH_SEC_EMBED, -1, false);
-  DF_HIP(launch_embed(bf, h->w.embed, D.H, D.V, anchors, h->cfg.mask_token_id, nb, B, x, rope, D.d,
-                      static_cast<double>(h->cfg.rope_theta), seq, h->layers[0].attn_norm, u, eps,
-                      st));
+  DF_HIP(launch_embed(bf, h->w.embed, D.H, D.V, anchors, h->cfg.mask_token_id, nb, B, x,
+                      h->layers[0].attn_norm, u, eps, st));
   DF_MARK(DFLASH_SEC_EMBED, -1, true);
 
   // attention split: chunks of >= 128 keys (one 32-key step per wave), at most
@@ -371,10 +378,11 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
       e.kc = static_cast<T*>(kv->k[l]);
       e.vc = static_cast<T*>(kv->v[l]);
       e.cap = kv->cap_total;
-      e.rope = rope;
+      e.freq = freq;
       e.seq = seq;
+      // few tiles and no K-split (the epilogue needs whole sums): 8 waves each
       DF_HIP(run_rows<T>(a_single<T>(u, D.H, D.H, M), D.H, g.tiles_qkv, 1, 1, e, st,
-                         NoPerLaunch{}));
+                         NoPerLaunch{}, 8));
     }
     DF_MARK(DFLASH_SEC_QKV, l, true);
     aa.kc = kv->k[l];

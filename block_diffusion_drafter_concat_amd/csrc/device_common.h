@@ -113,15 +113,21 @@ __device__ __forceinline__ int argmax_key_index(unsigned long long k) {
   return static_cast<int>(0xffffffffu - static_cast<uint32_t>(k & 0xffffffffull));
 }
 
-// Cos/sin of RoPE angle pos * theta^(-2i/d), formed in double, stored float.
-__device__ __forceinline__ void rope_cos_sin(int pos, int i, int d, double theta, float& c,
+// RoPE inverse frequencies theta^(-2i/d), i < d/2, formed in double on the
+// host and passed by value.
+struct RopeFreq {
+  double inv[64];
+};
+
+// Cos/sin of the RoPE angle pos * inv[i]: the product and its reduction to
+// [-pi, pi] in double (positions reach ~10^5 radians), the sine and cosine of
+// the reduced angle in float.
+__device__ __forceinline__ void rope_cos_sin(int pos, int i, const RopeFreq& f, float& c,
                                              float& s) {
-  const double inv = pow(theta, -2.0 * static_cast<double>(i) / static_cast<double>(d));
-  const double ang = static_cast<double>(pos) * inv;
-  double sd, cd;
-  sincos(ang, &sd, &cd);
-  c = static_cast<float>(cd);
-  s = static_cast<float>(sd);
+  const double kTwoPi = 6.283185307179586476925286766559;
+  const double ang = static_cast<double>(pos) * f.inv[i];
+  const double r = fma(-rint(ang * (1.0 / kTwoPi)), kTwoPi, ang);
+  sincosf(static_cast<float>(r), &s, &c);
 }
 
 // Per-sequence bookkeeping passed by value to kernels.

@@ -85,7 +85,7 @@ struct EpiQKV {
   T* kc;
   T* vc;
   int64_t cap;
-  const float2* rope;   // [m][d/2]
+  RopeFreq freq;
   SeqTable seq;
   __device__ void init(State&) const {}
   __device__ int nq() const { return Hq * (d / 32); }
@@ -112,9 +112,10 @@ struct EpiQKV {
       const bool is_q = tile < nq();
       const RopePairTile pt = rope_pair_tile(is_q ? tile : tile - nq(), d);
       const int c = pt.i0 + i;
-      const float2 cs = rope[static_cast<int64_t>(m) * (d / 2) + c];
-      const float o0 = v0 * cs.x - v1 * cs.y;
-      const float o1 = v1 * cs.x + v0 * cs.y;
+      float cs, sn;
+      rope_cos_sin(seq.len[b] + j, c, freq, cs, sn);
+      const float o0 = v0 * cs - v1 * sn;
+      const float o1 = v1 * cs + v0 * sn;
       T* dst = is_q ? q + static_cast<int64_t>(m) * ldq + pt.head * d
                     : kc + (static_cast<int64_t>(pt.head) * cap + row) * d;
       stf(dst + c, o0);
@@ -139,7 +140,7 @@ struct EpiInject {
   T* vc[kMaxLayers];
   int K, d, Hkv;
   int64_t cap;
-  const float2* rope;   // [m][d/2] at each row's position
+  RopeFreq freq;
   SeqTable seq;
   __device__ void init(State&) const {}
   __device__ int kt() const { return Hkv * (d / 32); }
@@ -159,14 +160,16 @@ struct EpiInject {
     if (!valid) return;
     const int l = tile / (2 * kt()), t = tile % (2 * kt());
     const int b = seq_of_row(seq, m);
-    const int64_t row = seq.off[b] + seq.pos0[b] + (m - seq.row0[b]);
+    const int pos = seq.pos0[b] + (m - seq.row0[b]);
+    const int64_t row = seq.off[b] + pos;
     if (t < kt()) {
       const RopePairTile pt = rope_pair_tile(t, d);
       const int c = pt.i0 + i;
-      const float2 cs = rope[static_cast<int64_t>(m) * (d / 2) + c];
+      float cs, sn;
+      rope_cos_sin(pos, c, freq, cs, sn);
       T* dst = kc[l] + (static_cast<int64_t>(pt.head) * cap + row) * d;
-      stf(dst + c, v0 * cs.x - v1 * cs.y);
-      stf(dst + c + d / 2, v1 * cs.x + v0 * cs.y);
+      stf(dst + c, v0 * cs - v1 * sn);
+      stf(dst + c + d / 2, v1 * cs + v0 * sn);
     } else {
       const int ca = (t - kt()) * 32 + i, cb = ca + 16;
       stf(vc[l] + (static_cast<int64_t>(ca / d) * d + ca % d) * cap + row, v0);

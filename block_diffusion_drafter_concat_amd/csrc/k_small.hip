@@ -27,8 +27,7 @@ template <typename T, int PER>
 __global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ embed, int H, int V,
                                                     const int32_t* __restrict__ anchors,
                                                     int mask_id, int B, float* __restrict__ x,
-                                                    float2* __restrict__ rope, int d, double theta,
-                                                    SeqTable seq, const T* __restrict__ gain,
+                                                    const T* __restrict__ gain,
                                                     T* __restrict__ u, float eps) {
   __shared__ float red[4];
   const int m = blockIdx.x;
@@ -49,12 +48,6 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ embed,
     }
     if (c < H) *reinterpret_cast<float4*>(dst + c) = make_float4(v[q][0], v[q][1], v[q][2], v[q][3]);
   }
-  const int pos = seq.len[b] + j;
-  for (int i = threadIdx.x; i < d / 2; i += 256) {
-    float cs, sn;
-    rope_cos_sin(pos, i, d, theta, cs, sn);
-    rope[static_cast<size_t>(m) * (d / 2) + i] = make_float2(cs, sn);
-  }
   // the first layer's attention RMSNorm of this row
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
@@ -73,14 +66,14 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ embed,
 }
 
 hipError_t launch_embed(bool bf16, const void* embed, int H, int V, const int32_t* anchors,
-                        int mask_id, int batch, int B, float* x, float2* rope, int d, double theta,
-                        const SeqTable& seq, const void* gain, void* u, float eps, hipStream_t st) {
+                        int mask_id, int batch, int B, float* x, const void* gain, void* u,
+                        float eps, hipStream_t st) {
   if (H > 8192 || H % 4) return hipErrorInvalidValue;
   dim3 grid(batch * B), block(256);
   const int per = (H + 1023) / 1024;
 #define DF_EMB(TT, P)                                                                          \
   embed_kernel<TT, P><<<grid, block, 0, st>>>(static_cast<const TT*>(embed), H, V, anchors,    \
-                                              mask_id, B, x, rope, d, theta, seq,              \
+                                              mask_id, B, x,                                   \
                                               static_cast<const TT*>(gain), static_cast<TT*>(u), \
                                               eps)
   if (bf16) {
@@ -241,31 +234,6 @@ hipError_t launch_lm_argmax_finalize(const float2* part, int n_wg, int rows, int
                                      hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   lm_argmax_finalize_kernel<<<rows, 256, 0, st>>>(part, n_wg, B, draft);
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------------------ RoPE rows
-__global__ __launch_bounds__(256) void rope_rows_kernel(float2* __restrict__ rope, int rows, int d,
-                                                        double theta, SeqTable seq) {
-  const int half = d / 2;
-  const int64_t n = static_cast<int64_t>(rows) * half;
-  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
-       e += static_cast<int64_t>(gridDim.x) * 256) {
-    const int m = static_cast<int>(e / half), i = static_cast<int>(e % half);
-    const int b = seq_of_row(seq, m);
-    const int pos = seq.pos0[b] + (m - seq.row0[b]);
-    float cs, sn;
-    rope_cos_sin(pos, i, d, theta, cs, sn);
-    rope[e] = make_float2(cs, sn);
-  }
-}
-
-hipError_t launch_rope_rows(float2* rope, int rows, int d, double theta, const SeqTable& seq,
-                            hipStream_t st) {
-  if (rows <= 0) return hipSuccess;
-  const int64_t n = static_cast<int64_t>(rows) * (d / 2);
-  const int grid = static_cast<int>((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
-  rope_rows_kernel<<<grid, 256, 0, st>>>(rope, rows, d, theta, seq);
   return hipGetLastError();
 }
 

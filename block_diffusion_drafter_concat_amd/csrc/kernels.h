@@ -13,12 +13,11 @@ namespace dflash {
 // Clear n 32-bit words (a fill kernel, so the call stays graph-capturable).
 hipError_t launch_zero(int* p, int64_t n, hipStream_t st);
 
-// Block inputs: x[m] = embed[token(m)] (fp32), RoPE cos/sin of every block slot
-// at position seq.len[b] + j, and u[m] = RMSNorm(x[m]) * gain (layer 0).
+// Block inputs: x[m] = embed[token(m)] (fp32) and u[m] = RMSNorm(x[m]) * gain
+// (layer 0's attention norm), one workgroup per block slot.
 hipError_t launch_embed(bool bf16, const void* embed, int H, int V, const int32_t* anchors,
-                        int mask_id, int batch, int B, float* x, float2* rope, int d,
-                        double theta, const SeqTable& seq, const void* gain, void* u, float eps,
-                        hipStream_t st);
+                        int mask_id, int batch, int B, float* x, const void* gain, void* u,
+                        float eps, hipStream_t st);
 
 // Row m: v = x[m] + sum_s part[s * split_stride + m*H ...] (x and part may be
 // null); x[m] = v when x; out[m] = RMSNorm(v) * gain when out (handle type).
@@ -29,10 +28,6 @@ hipError_t launch_resid_rmsnorm(bool bf16, float* x, const float* part, int n_sp
 // Draft ids from the LM head's per-workgroup (value, index) partials [rows][n_wg].
 hipError_t launch_lm_argmax_finalize(const float2* part, int n_wg, int rows, int B, int32_t* draft,
                                      hipStream_t st);
-
-// RoPE cos/sin of inject rows: row m of sequence b sits at seq.pos0[b] + m - seq.row0[b].
-hipError_t launch_rope_rows(float2* rope, int rows, int d, double theta, const SeqTable& seq,
-                            hipStream_t st);
 
 // Greedy verify: per-chunk row argmax, then per-sequence prefix scan.
 size_t verify_ws_bytes(int batch, int B, int V);
