@@ -195,29 +195,40 @@ def block_attention(q, K, V) -> np.ndarray:
 # ------------------------------------------------- (a6) decoder layer
 
 def decoder_layer(x, positions, lw, k_ctx, v_ctx, shape, rb: bool) -> np.ndarray:
-    """One pre-norm drafter layer applied to one sequence's block.
+    """One pre-norm drafter layer applied to the blocks of one or more sequences.
 
-    x: [B, H] float64 residual stream; k_ctx, v_ctx: [L, Hkv, d] injected
-    context.  Attention half then SwiGLU feed-forward half, each with its own
-    RMSNorm and a residual add.
+    x: [B, H] (one sequence; k_ctx, v_ctx: [L, Hkv, d]) or [N, B, H] (N
+    sequences; k_ctx, v_ctx: lists of N such arrays); float64 residual stream.
+    Attention half then SwiGLU feed-forward half, each with its own RMSNorm and
+    a residual add.  The projections act on each row independently, so rows of
+    all sequences are stacked for them; attention runs per sequence.
     """
-    B = x.shape[0]
+    single = np.ndim(x) == 2
+    if single:
+        x, positions, k_ctx, v_ctx = x[None], np.asarray(positions)[None], [k_ctx], [v_ctx]
+    x = _f64(x)
+    N, B, H = x.shape
     Hq, Hkv, d = shape.n_q_heads, shape.n_kv_heads, shape.head_dim
     eps = shape.rms_eps
-    u = _maybe_round(rmsnorm(x, lw["attn_norm"], eps), rb)
-    q = (u @ _f64(lw["wq"]).T).reshape(B, Hq, d)
-    k = (u @ _f64(lw["wk"]).T).reshape(B, Hkv, d)
-    v = (u @ _f64(lw["wv"]).T).reshape(B, Hkv, d)
-    q = _maybe_round(rope(q, positions, shape.rope_theta), rb)
-    k = _maybe_round(rope(k, positions, shape.rope_theta), rb)
-    v = _maybe_round(v, rb)
-    K = np.concatenate([_f64(k_ctx), k], axis=0)
-    V = np.concatenate([_f64(v_ctx), v], axis=0)
-    o = _maybe_round(block_attention(q, K, V).reshape(B, Hq * d), rb)
-    x = x + o @ _f64(lw["wo"]).T
-    u = _maybe_round(rmsnorm(x, lw["ffn_norm"], eps), rb)
+    pos = np.asarray(positions).reshape(N * B)
+    rows = x.reshape(N * B, H)
+    u = _maybe_round(rmsnorm(rows, lw["attn_norm"], eps), rb)
+    q = (u @ _f64(lw["wq"]).T).reshape(N * B, Hq, d)
+    k = (u @ _f64(lw["wk"]).T).reshape(N * B, Hkv, d)
+    v = (u @ _f64(lw["wv"]).T).reshape(N * B, Hkv, d)
+    q = _maybe_round(rope(q, pos, shape.rope_theta), rb).reshape(N, B, Hq, d)
+    k = _maybe_round(rope(k, pos, shape.rope_theta), rb).reshape(N, B, Hkv, d)
+    v = _maybe_round(v, rb).reshape(N, B, Hkv, d)
+    o = np.stack([block_attention(q[n], np.concatenate([_f64(k_ctx[n]), k[n]], axis=0),
+                                  np.concatenate([_f64(v_ctx[n]), v[n]], axis=0))
+                  for n in range(N)])
+    o = _maybe_round(o.reshape(N * B, Hq * d), rb)
+    rows = rows + o @ _f64(lw["wo"]).T
+    u = _maybe_round(rmsnorm(rows, lw["ffn_norm"], eps), rb)
     h = _maybe_round(silu(u @ _f64(lw["wg"]).T) * (u @ _f64(lw["wu"]).T), rb)
-    return x + h @ _f64(lw["wd"]).T
+    rows = rows + h @ _f64(lw["wd"]).T
+    out = rows.reshape(N, B, H)
+    return out[0] if single else out
 
 
 # --------------------------------------- (a5, a6, a7) one block, one pass
@@ -239,18 +250,17 @@ def draft_block(weights, shape, caches, anchors, block_size: int) -> dict:
     rb = shape.dtype == "bf16"
     N, B = len(anchors), int(block_size)
     emb, lm = weights["embed"], weights["lm_head"]
-    final_h = np.empty((N, B, shape.hidden), dtype=np.float64)
-    logits = np.empty((N, B, shape.vocab), dtype=np.float64)
-    for b in range(N):
-        L = caches[b][0][0].shape[0]
-        tokens = [int(anchors[b])] + [shape.mask_token_id] * (B - 1)
-        positions = L + np.arange(B)
-        x = _f64(emb[tokens])                                   # [B, H]
-        for lw, (kc, vc) in zip(weights["layers"], caches[b]):
-            x = decoder_layer(x, positions, lw, kc, vc, shape, rb)
-        final_h[b] = x
-        u = _maybe_round(rmsnorm(x, weights["final_norm"], shape.rms_eps), rb)
-        logits[b] = u @ _f64(lm).T
+    tokens = np.array([[int(a)] + [shape.mask_token_id] * (B - 1) for a in anchors])
+    lens = np.array([caches[b][0][0].shape[0] for b in range(N)])
+    positions = lens[:, None] + np.arange(B)[None, :]
+    x = _f64(emb[tokens.reshape(-1)]).reshape(N, B, shape.hidden)
+    for l, lw in enumerate(weights["layers"]):
+        x = decoder_layer(x, positions, lw, [caches[b][l][0] for b in range(N)],
+                          [caches[b][l][1] for b in range(N)], shape, rb)
+    final_h = x
+    u = _maybe_round(rmsnorm(x.reshape(N * B, shape.hidden), weights["final_norm"],
+                             shape.rms_eps), rb)
+    logits = (u @ _f64(lm).T).reshape(N, B, shape.vocab)
     z = logits[:, 1:, :]
     draft_ids = argmax_lowest(z, axis=2).astype(np.int32)
     srt = np.sort(z, axis=2)
