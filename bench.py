@@ -84,6 +84,39 @@ def lm_head_traffic():
         return None
 
 
+def time_prefill(torch, dr, shape, feats_dev, ctx_all, cache, ws, reps: int = 5) -> dict:
+    """Fusion and injection GEMMs over the 2048-row prefill (MFMA-bound)."""
+    H, T = shape.hidden, CTX
+    fuse_flops = 2.0 * T * shape.n_feat * H * H
+    inj_flops = 2.0 * T * H * shape.n_layers * 2 * shape.kv_dim
+    sec = [("fuse_gemm", -1), ("inject", -1)]
+    evs = []
+    for _ in range(reps):
+        pts = []
+        for s_, l in sec:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            b.record()
+            pts.append((s_, l, a, b))
+        evs.append(pts)
+    torch.cuda.synchronize()
+    for pts in evs:
+        dr.set_timing(pts)
+        dr.fuse_context(feats_dev, ctx_all, ws)
+        dr.inject_kv(ctx_all, [CTX], cache, ws, pos_start=[0])
+    dr.set_timing([])
+    torch.cuda.synchronize()
+    f_us = float(np.mean([p[0][2].elapsed_time(p[0][3]) for p in evs])) * 1e3
+    i_us = float(np.mean([p[1][2].elapsed_time(p[1][3]) for p in evs])) * 1e3
+    out = {}
+    for name, us, fl in (("fusion_gemm", f_us, fuse_flops), ("injection_gemm", i_us, inj_flops)):
+        tf = fl / (us * 1e-6) / 1e12
+        out[name] = {"rows": T, "avg_us": round(us, 2), "TFLOP/s": round(tf, 1),
+                     "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+    return out
+
+
 def step_bytes(shape, n_new: int) -> dict:
     """Algorithmic HBM bytes of one step (each tensor read or written once)."""
     H, V, L = shape.hidden, shape.vocab, shape.n_layers
@@ -133,9 +166,11 @@ def main():
     cache = L.KVCache(shape, [CTX + 64])
     ws = dr.workspace(BATCH, BLOCK, CTX)
     ctx_all = torch.empty((CTX, shape.hidden), dtype=torch.bfloat16, device="cuda")
-    dr.fuse_context([L.to_device(f, "bf16") for f in feats], ctx_all, ws)
+    feats_dev = [L.to_device(f, "bf16") for f in feats]
+    dr.fuse_context(feats_dev, ctx_all, ws)
     dr.inject_kv(ctx_all, [CTX], cache, ws)
-    del ctx_all
+    prefill = time_prefill(torch, dr, shape, feats_dev, ctx_all, cache, ws)
+    del ctx_all, feats_dev
 
     # per-step inputs
     n_steps = W + K
@@ -274,6 +309,7 @@ def main():
         "roofline": roofline,
         "step_roofline": step_roof,
         "kernels": kernels,
+        "prefill_mfma": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -5,11 +5,14 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
+#include <atomic>
 #include <new>
 
 #include "../../include/dflash.h"
 #include "gemm_epilogues.h"
 #include "gemm_skinny.h"
+#include "gemm_tiled.h"
 #include "kernels.h"
 #include "kernels_attn.h"
 
@@ -68,10 +71,37 @@ int pick_ksplit(int n_tiles, int K) {
     ks *= 2;
   return ks;
 }
-// Fusion: K-split only for the short incremental calls (the partial slabs are
-// ks * T * H floats).
-int fuse_ksplit(const Dims& D, int64_t T) {
-  return T <= 64 ? pick_ksplit(D.H / 32, D.nf * D.H) : 1;
+// Rows from which bf16 fusion / injection use the LDS-tiled GEMM.
+constexpr int kTiledMinRows = 129;
+
+// Fusion K-split.  Weight-streaming path: only for short incremental calls.
+// Tiled path: split until the 256 x 256 tiles times the split fill the 256
+// compute units once (at most 8 partial slabs, whole 64-wide k stages).
+int fuse_ksplit(const dflash_handle* h, int64_t T) {
+  const Dims D = dims(h->cfg);
+  const int K = D.nf * D.H;
+  if (h->cfg.dtype == DFLASH_BF16 && T >= kTiledMinRows) {
+    const int64_t tiles = ((T + kTBM - 1) / kTBM) * ((D.H + kTBN - 1) / kTBN);
+    int ks = 1;
+    while (ks < 8 && 2 * ks * tiles <= 256 && K % (2 * ks * kTBK) == 0) ks *= 2;
+    return ks;
+  }
+  return T <= 64 ? pick_ksplit(D.H / 32, K) : 1;
+}
+
+// Largest ks * T over every call size T <= t_max (ks is constant where the
+// row-tile count is, so only the largest T of each such range matters).
+int64_t fuse_part_rows(const dflash_handle* h, int64_t t_max) {
+  int64_t best = 0;
+  auto consider = [&](int64_t T) {
+    T = T < t_max ? T : t_max;
+    if (T > 0) best = std::max(best, fuse_ksplit(h, T) * T);
+  };
+  consider(64);
+  consider(kTiledMinRows - 1);
+  for (int64_t tm = 1; (tm - 1) * kTBM < t_max; ++tm) consider(tm * kTBM);
+  consider(t_max);
+  return best;
 }
 
 GemmPlan gemm_plan(const Dims& D) {
@@ -112,7 +142,7 @@ Layout layout(const dflash_handle* h, int max_batch, int max_block, int64_t max_
   L.h_off = off;    off += align_up(M * D.F * es);
   // K-split partial slabs: O / down projections [ks][M][H], fusion [ks][T][H]
   size_t part = static_cast<size_t>(g.ks_o > g.ks_d ? g.ks_o : g.ks_d) * M * D.H * 4;
-  const size_t pf = static_cast<size_t>(fuse_ksplit(D, static_cast<int64_t>(T))) * T * D.H * 4;
+  const size_t pf = static_cast<size_t>(fuse_part_rows(h, static_cast<int64_t>(T))) * D.H * 4;
   part = pf > part ? pf : part;
   L.part_off = off; off += align_up(part);
   L.lm_off = off;   off += align_up(M * g.wg_lm * 8);
@@ -194,6 +224,23 @@ hipError_t run_rows(AOperand<T> A, int K, int n_tiles, int tiles_per_wg, int ksp
   }
   return hipSuccess;
 }
+template <class Epi>
+hipError_t launch_tiled(const AOperand<uint16_t>& A, int N, int K, int parts, int ksplit,
+                        const Epi& epi, hipStream_t st) {
+  static std::atomic<bool> attr_set{false};
+  if (!attr_set.load()) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&tiled_gemm_kernel<Epi>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(kTiledLds));
+    if (e != hipSuccess) return e;
+    attr_set.store(true);
+  }
+  const int tm = (A.M + kTBM - 1) / kTBM, tn = (N + kTBN - 1) / kTBN;
+  tiled_gemm_kernel<Epi><<<dim3(tm * tn, parts, ksplit), 256, kTiledLds, st>>>(A, N, K, tm, tn,
+                                                                                epi);
+  return hipGetLastError();
+}
+
 struct NoPerLaunch {
   template <class E> void operator()(E&, int) const {}
 };
@@ -265,11 +312,19 @@ dflash_status fuse_impl(dflash_handle* h, const void* const* feats, int64_t n_to
   A.slab_k = D.H;
   A.M = T_;
   const int K = D.nf * D.H;
-  const int ks = fuse_ksplit(D, n_tokens);
+  const int ks = fuse_ksplit(h, n_tokens);
   float* Y = at<float>(ws, L.part_off);
   DF_MARK(DFLASH_SEC_FUSE_GEMM, -1, false);
-  EpiPartialF32<T> epi{static_cast<const T*>(h->w.fc), K, Y, D.H, T_};
-  DF_HIP(run_rows<T>(A, K, g.tiles_fc, 1, ks, epi, st, NoPerLaunch{}));
+  if (sizeof(T) == 2 && T_ >= kTiledMinRows) {
+    AOperand<uint16_t> At{};
+    for (int i = 0; i < 6; ++i) At.slab[i] = reinterpret_cast<const uint16_t*>(A.slab[i]);
+    At.lda = A.lda; At.slab_k = A.slab_k; At.M = A.M; At.m0 = 0; At.mc = A.M;
+    TEpiStoreF32 te{static_cast<const uint16_t*>(h->w.fc), K, Y, D.H, T_};
+    DF_HIP(launch_tiled(At, D.H, K, 1, ks, te, st));
+  } else {
+    EpiPartialF32<T> epi{static_cast<const T*>(h->w.fc), K, Y, D.H, T_};
+    DF_HIP(run_rows<T>(A, K, g.tiles_fc, 1, ks, epi, st, NoPerLaunch{}));
+  }
   DF_MARK(DFLASH_SEC_FUSE_GEMM, -1, true);
   DF_MARK(DFLASH_SEC_FUSE_NORM, -1, false);
   DF_HIP(launch_resid_rmsnorm(h->cfg.dtype == DFLASH_BF16, nullptr, Y, ks,
@@ -299,8 +354,25 @@ dflash_status inject_impl(dflash_handle* h, const void* ctx, const SeqTable& seq
   epi.cap = kv->cap_total;
   epi.freq = rope_freq(h->cfg);
   epi.seq = seq;
-  DF_HIP(run_rows<T>(a_single<T>(ctx, D.H, D.H, total), D.H, g.tiles_inj, 1, 1, epi, st,
-                     NoPerLaunch{}));
+  if (sizeof(T) == 2 && total >= kTiledMinRows) {
+    TEpiInject te{};
+    for (int l = 0; l < D.L; ++l) {
+      te.wk[l] = reinterpret_cast<const uint16_t*>(epi.wk[l]);
+      te.wv[l] = reinterpret_cast<const uint16_t*>(epi.wv[l]);
+      te.kc[l] = reinterpret_cast<uint16_t*>(epi.kc[l]);
+      te.vc[l] = reinterpret_cast<uint16_t*>(epi.vc[l]);
+    }
+    te.K = D.H;
+    te.d = D.d;
+    te.cap = kv->cap_total;
+    te.freq = epi.freq;
+    te.seq = seq;
+    const AOperand<uint16_t> At = a_single<uint16_t>(ctx, D.H, D.H, total);
+    DF_HIP(launch_tiled(At, D.kvd, D.H, 2 * D.L, 1, te, st));
+  } else {
+    DF_HIP(run_rows<T>(a_single<T>(ctx, D.H, D.H, total), D.H, g.tiles_inj, 1, 1, epi, st,
+                       NoPerLaunch{}));
+  }
   DF_MARK(DFLASH_SEC_INJECT, -1, true);
   return DFLASH_OK;
 }

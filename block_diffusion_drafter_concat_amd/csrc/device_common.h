@@ -119,15 +119,18 @@ struct RopeFreq {
   double inv[64];
 };
 
-// Cos/sin of the RoPE angle pos * inv[i]: the product and its reduction to
+// Cos/sin of the RoPE angle pos * inv: the product and its reduction to
 // [-pi, pi] in double (positions reach ~10^5 radians), the sine and cosine of
 // the reduced angle in float.
-__device__ __forceinline__ void rope_cos_sin(int pos, int i, const RopeFreq& f, float& c,
-                                             float& s) {
+__device__ __forceinline__ void rope_cos_sin(int pos, double inv, float& c, float& s) {
   const double kTwoPi = 6.283185307179586476925286766559;
-  const double ang = static_cast<double>(pos) * f.inv[i];
+  const double ang = static_cast<double>(pos) * inv;
   const double r = fma(-rint(ang * (1.0 / kTwoPi)), kTwoPi, ang);
   sincosf(static_cast<float>(r), &s, &c);
+}
+__device__ __forceinline__ void rope_cos_sin(int pos, int i, const RopeFreq& f, float& c,
+                                             float& s) {
+  rope_cos_sin(pos, f.inv[i], c, s);
 }
 
 // Per-sequence bookkeeping passed by value to kernels.
