@@ -224,20 +224,24 @@ hipError_t run_rows(AOperand<T> A, int K, int n_tiles, int tiles_per_wg, int ksp
   }
   return hipSuccess;
 }
+// 8 waves (2 x 4) per 256 x 256 tile: two waves per SIMD, 128 accumulators each.
+constexpr int kTiledWM = 2, kTiledWN = 4;
+
 template <class Epi>
 hipError_t launch_tiled(const AOperand<uint16_t>& A, int N, int K, int parts, int ksplit,
                         const Epi& epi, hipStream_t st) {
+  auto kern = &tiled_gemm_kernel<kTiledWM, kTiledWN, Epi>;
   static std::atomic<bool> attr_set{false};
   if (!attr_set.load()) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&tiled_gemm_kernel<Epi>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(kTiledLds));
     if (e != hipSuccess) return e;
     attr_set.store(true);
   }
   const int tm = (A.M + kTBM - 1) / kTBM, tn = (N + kTBN - 1) / kTBN;
-  tiled_gemm_kernel<Epi><<<dim3(tm * tn, parts, ksplit), 256, kTiledLds, st>>>(A, N, K, tm, tn,
-                                                                                epi);
+  kern<<<dim3(tm * tn, parts, ksplit), kTiledWM * kTiledWN * 64, kTiledLds, st>>>(A, N, K, tm,
+                                                                                  tn, epi);
   return hipGetLastError();
 }
 

@@ -6,7 +6,8 @@
 //     grid, each wave 128 x 128 = 8 x 8 MFMA tiles of 16 x 16 (fp32
 //     accumulators, 256 per lane, held in AGPRs);
 //   - K in stages of 64: both operand tiles (2 x 32 KB) go through LDS, double
-//     buffered; the next stage is loaded into registers while the current one
+//     buffered; the next stage is loaded straight into LDS (buffer loads with
+//     the LDS-destination bit, no staging registers) while the current one
 //     feeds the MFMAs.  16-byte chunks are XOR-swizzled by row so that the
 //     fragment reads (16 rows x 16 bytes per instruction) hit distinct banks;
 //   - tiles are walked in an XCD-aware order: workgroup w runs on XCD w % 8,
@@ -31,27 +32,46 @@ constexpr int kTBM = 256, kTBN = 256, kTBK = 64;
 __device__ __forceinline__ int swz(int r, int c) { return r * 64 + ((c ^ (r & 7)) << 3); }
 
 // One 64-row slice of a finished 256 x 256 tile in LDS, as the epilogue sees
-// it: local row lr < 32 is output row mA + lr, lr >= 32 is mB + lr - 32;
-// column c is output column n0 + c.
+// it.  Local rows come in runs of `run` rows, one run per wave row; run r
+// starts at output row m_base + r * wave_rows.  Column c is output column
+// n0 + c.
 constexpr int kCtStride = kTBN + 4;   // padded fp32 row stride (no bank conflicts)
 constexpr int kTiledEpiLds = 1024;
 struct TiledSlice {
   const float* c;
-  int mA, mB, M, n0, N, part, split;
-  __device__ int row(int lr) const { return lr < 32 ? mA + lr : mB + lr - 32; }
+  int m_base, run, wave_rows, M, n0, N, part, split;
+  __device__ int row(int lr) const { return m_base + (lr / run) * wave_rows + lr % run; }
   __device__ float at(int lr, int col) const { return c[lr * kCtStride + col]; }
 };
 static_assert(64 * kCtStride * 4 + kTiledEpiLds <= 2 * 2 * kTBM * kTBK * 2, "slice fits in LDS");
 
-template <class Epi>
-__global__ __launch_bounds__(256) void tiled_gemm_kernel(AOperand<uint16_t> A, int N, int K,
-                                                         int tiles_m, int tiles_n, Epi epi) {
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+// Raw buffer resource over [base, base + bytes): loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes > 0xffffffffull ? 0xffffffffu : static_cast<uint32_t>(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(n),
+                                           0x00020000);
+}
+
+// WM x WN waves; wave (wm, wn) owns rows wm * 256/WM and columns
+// wn * 256/WN of the tile as MI x NJ MFMA tiles of 16 x 16.
+template <int WM, int WN, class Epi>
+__global__ __launch_bounds__(WM * WN * 64) void tiled_gemm_kernel(AOperand<uint16_t> A, int N,
+                                                                  int K, int tiles_m,
+                                                                  int tiles_n, Epi epi) {
+  constexpr int NWAVES = WM * WN, NT = NWAVES * 64;
+  constexpr int RW = kTBM / WM, CW = kTBN / WN;   // wave tile
+  constexpr int MI = RW / 16, NJ = CW / 16;
+  constexpr int LI = 32 / NWAVES;                 // loads per wave per operand
+  static_assert(MI % 4 == 0, "four epilogue slices per wave row");
   const int part = blockIdx.y;    // output part (uniform per workgroup)
   const int split = blockIdx.z;   // K split
   extern __shared__ __align__(16) uint16_t lds[];   // [2][A 256x64 | W 256x64]
-  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int r16 = lane & 15, kg = lane >> 4;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
 
   // ---- XCD-aware tile order: workgroup w runs on XCD w % 8; XCD x owns the
   // contiguous tile range [start(x), start(x) + count(x)) (a bijection)
@@ -73,121 +93,104 @@ __global__ __launch_bounds__(256) void tiled_gemm_kernel(AOperand<uint16_t> A, i
   const int kper = K / gridDim.z;
   const int kbeg = split * kper;
 
-  // ---- global -> register staging: thread t moves chunks (row t/8 + 32 i,
-  // chunk t%8) of both operand tiles; row offsets and W row pointers are fixed
-  // for the whole K loop.
-  const int srow = t >> 3, schunk = t & 7;
-  int64_t aoff[8];
-  const uint16_t* wp[8];
+  // ---- global -> LDS without registers (buffer_load ... lds).  One wave
+  // instruction fills 1 KB of LDS: 8 tile rows of 8 16-byte chunks, lane l
+  // landing at chunk l of the run.  Instruction i of wave w covers tile rows
+  // 8 (w LI + i) .. +8; lane l takes row 8 (w LI + i) + l / 8 and, so that the
+  // XOR swizzle holds, global chunk (l % 8) ^ (l / 8).  Rows past M or N
+  // read as zero through the buffer range check.
+  const int lrow = 8 * LI * wave + (lane >> 3);
+  const int gchunk = (lane & 7) ^ (lane >> 3);
+  const uint32_t a_voff = static_cast<uint32_t>(lrow * A.lda * 2 + gchunk * 16);
+  const uint32_t w_voff = static_cast<uint32_t>(lrow * K * 2 + gchunk * 16);
+  const uint32_t a_istep = static_cast<uint32_t>(8 * A.lda * 2);
+  const uint32_t w_istep = static_cast<uint32_t>(8 * K * 2);
+  const __amdgpu_buffer_rsrc_t wrs =
+      tile_rsrc(epi.wbase(part) + static_cast<int64_t>(n0) * K,
+                static_cast<uint64_t>(N - n0) * static_cast<uint64_t>(K) * 2);
+  const uint64_t a_bytes = static_cast<uint64_t>(A.M - m0) * static_cast<uint64_t>(A.lda) * 2;
+  auto issue = [&](int k0, int buf) {
+    const int s = k0 / A.slab_k;
+    const int col = k0 - s * A.slab_k;
+    const __amdgpu_buffer_rsrc_t ars =
+        tile_rsrc(A.slab[s] + static_cast<int64_t>(m0) * A.lda, a_bytes);
+    lds_u16* la = (lds_u16*)(lds) + buf * (2 * kTBM * kTBK) + wave * (LI * 512);
+    lds_u16* lw = la + kTBM * kTBK;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    aoff[i] = static_cast<int64_t>(min(m0 + srow + 32 * i, A.M - 1)) * A.lda + schunk * 8;
-    wp[i] = epi.wrow(part, min(n0 + srow + 32 * i, N - 1)) + schunk * 8;
-  }
-  int lw_off[8];
+    for (int i = 0; i < LI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, la + i * 512, 16, a_voff,
+                                               i * a_istep + col * 2, 0, 0);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) lw_off[i] = swz(srow + 32 * i, schunk);
+    for (int i = 0; i < LI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, lw + i * 512, 16, w_voff,
+                                               i * w_istep + k0 * 2, 0, 0);
+  };
 
-  f32x4 acc[8][8];
+  f32x4 acc[MI][NJ];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = zero4();
+    for (int j = 0; j < NJ; ++j) acc[i][j] = zero4();
 
-  const int n_stages = kper / kTBK;
-  uint4 ra0, ra1, ra2, ra3, ra4, ra5, ra6, ra7;
-  uint4 rw0, rw1, rw2, rw3, rw4, rw5, rw6, rw7;
-#define DF_GLOAD(k0)                                                                      \
-  {                                                                                       \
-    const int s_ = (k0) / A.slab_k;                                                       \
-    const uint16_t* ab_ = A.slab[s_] + ((k0) - s_ * A.slab_k);                            \
-    ra0 = *reinterpret_cast<const uint4*>(ab_ + aoff[0]);                                 \
-    ra1 = *reinterpret_cast<const uint4*>(ab_ + aoff[1]);                                 \
-    ra2 = *reinterpret_cast<const uint4*>(ab_ + aoff[2]);                                 \
-    ra3 = *reinterpret_cast<const uint4*>(ab_ + aoff[3]);                                 \
-    ra4 = *reinterpret_cast<const uint4*>(ab_ + aoff[4]);                                 \
-    ra5 = *reinterpret_cast<const uint4*>(ab_ + aoff[5]);                                 \
-    ra6 = *reinterpret_cast<const uint4*>(ab_ + aoff[6]);                                 \
-    ra7 = *reinterpret_cast<const uint4*>(ab_ + aoff[7]);                                 \
-    rw0 = *reinterpret_cast<const uint4*>(wp[0] + (k0));                                  \
-    rw1 = *reinterpret_cast<const uint4*>(wp[1] + (k0));                                  \
-    rw2 = *reinterpret_cast<const uint4*>(wp[2] + (k0));                                  \
-    rw3 = *reinterpret_cast<const uint4*>(wp[3] + (k0));                                  \
-    rw4 = *reinterpret_cast<const uint4*>(wp[4] + (k0));                                  \
-    rw5 = *reinterpret_cast<const uint4*>(wp[5] + (k0));                                  \
-    rw6 = *reinterpret_cast<const uint4*>(wp[6] + (k0));                                  \
-    rw7 = *reinterpret_cast<const uint4*>(wp[7] + (k0));                                  \
-  }
-#define DF_LSTORE(buf)                                                                    \
-  {                                                                                       \
-    uint16_t* la_ = lds + (buf) * (2 * kTBM * kTBK);                                      \
-    uint16_t* lw_ = la_ + kTBM * kTBK;                                                    \
-    *reinterpret_cast<uint4*>(la_ + lw_off[0]) = ra0;                                     \
-    *reinterpret_cast<uint4*>(la_ + lw_off[1]) = ra1;                                     \
-    *reinterpret_cast<uint4*>(la_ + lw_off[2]) = ra2;                                     \
-    *reinterpret_cast<uint4*>(la_ + lw_off[3]) = ra3;                                     \
-    *reinterpret_cast<uint4*>(la_ + lw_off[4]) = ra4;                                     \
-    *reinterpret_cast<uint4*>(la_ + lw_off[5]) = ra5;                                     \
-    *reinterpret_cast<uint4*>(la_ + lw_off[6]) = ra6;                                     \
-    *reinterpret_cast<uint4*>(la_ + lw_off[7]) = ra7;                                     \
-    *reinterpret_cast<uint4*>(lw_ + lw_off[0]) = rw0;                                     \
-    *reinterpret_cast<uint4*>(lw_ + lw_off[1]) = rw1;                                     \
-    *reinterpret_cast<uint4*>(lw_ + lw_off[2]) = rw2;                                     \
-    *reinterpret_cast<uint4*>(lw_ + lw_off[3]) = rw3;                                     \
-    *reinterpret_cast<uint4*>(lw_ + lw_off[4]) = rw4;                                     \
-    *reinterpret_cast<uint4*>(lw_ + lw_off[5]) = rw5;                                     \
-    *reinterpret_cast<uint4*>(lw_ + lw_off[6]) = rw6;                                     \
-    *reinterpret_cast<uint4*>(lw_ + lw_off[7]) = rw7;                                     \
-  }
-  DF_GLOAD(kbeg);
-  DF_LSTORE(0);
-  __syncthreads();
-  for (int st = 0; st < n_stages; ++st) {
-    const int buf = st & 1;
-    const bool more = st + 1 < n_stages;
-    if (more) DF_GLOAD(kbeg + (st + 1) * kTBK);
+  // One stage: read this wave's fragments of both k halves, then (when there
+  // is a next stage) start its loads into the other buffer -- after the reads
+  // in program order, so no LDS read waits on them -- then the MFMAs.  The
+  // other buffer was last read in the previous stage, which every thread
+  // finished before the previous barrier.
+  auto stage = [&](int buf, bool next, int k_next) {
     const uint16_t* la = lds + buf * (2 * kTBM * kTBK);
     const uint16_t* lw = la + kTBM * kTBK;
+    Frag8<uint16_t> af[2][MI], bf[2][NJ];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      Frag8<uint16_t> af[8], bf[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        af[i].v = *reinterpret_cast<const uint4*>(la + swz(wm * 128 + i * 16 + r16, kk * 4 + kg));
+      for (int i = 0; i < MI; ++i)
+        af[kk][i].v =
+            *reinterpret_cast<const uint4*>(la + swz(wm * RW + i * 16 + r16, kk * 4 + kg));
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        bf[j].v = *reinterpret_cast<const uint4*>(lw + swz(wn * 128 + j * 16 + r16, kk * 4 + kg));
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = mfma16(acc[i][j], af[i], bf[j]);
+      for (int j = 0; j < NJ; ++j)
+        bf[kk][j].v =
+            *reinterpret_cast<const uint4*>(lw + swz(wn * CW + j * 16 + r16, kk * 4 + kg));
     }
-    // the other buffer was last read in the previous stage, which every
-    // thread finished before the previous barrier
-    if (more) DF_LSTORE(buf ^ 1);
+    if (next) issue(k_next, buf ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16(acc[i][j], af[kk][i], bf[kk][j]);
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's next-stage loads
     __syncthreads();
-  }
-#undef DF_GLOAD
-#undef DF_LSTORE
+  };
 
-  // ---- epilogue: slice q holds rows {32 q + r, 128 + 32 q + r : r < 32} of
-  // the tile as C[64][kCtStride] fp32 (local row lr = wm * 32 + r).  C tile
+  const int n_stages = kper / kTBK;
+  issue(kbeg, 0);
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+  __syncthreads();
+  for (int st = 0; st + 1 < n_stages; ++st) stage(st & 1, true, kbeg + (st + 1) * kTBK);
+  stage((n_stages - 1) & 1, false, 0);
+
+  // ---- epilogue: four slices of 64 rows.  Slice q takes MFMA rows
+  // i in [q MI/4, (q+1) MI/4) of every wave: local row lr = wm * 4 MI +
+  // (i - q MI/4) * 16 + kg * 4 + jj, stored as C[64][kCtStride] fp32.  C tile
   // (i, j) lane holds rows i*16 + kg*4 + jj, column j*16 + r16.
+  constexpr int QI = MI / 4, RUN = 16 * QI;
   float* ct = reinterpret_cast<float*>(lds);
   void* ext = ct + 64 * kCtStride;   // epilogue's own LDS (kTiledEpiLds bytes)
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
+    for (int ii = 0; ii < QI; ++ii)
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
-          ct[(wm * 32 + ii * 16 + kg * 4 + jj) * kCtStride + wn * 128 + j * 16 + r16] =
-              acc[2 * q + ii][j][jj];
+          ct[(wm * RUN + ii * 16 + kg * 4 + jj) * kCtStride + wn * CW + j * 16 + r16] =
+              acc[q * QI + ii][j][jj];
     __syncthreads();
-    const TiledSlice sl{ct, m0 + 32 * q, m0 + 128 + 32 * q, A.M, n0, N, part, split};
-    epi.store(sl, ext, t);
+    const TiledSlice sl{ct, m0 + q * RUN, RUN, RW, A.M, n0, N, part, split};
+    epi.store(sl, ext, t, NT);
     __syncthreads();
   }
 }
@@ -202,11 +205,11 @@ struct TEpiStoreF32 {
   int K;
   float* out;
   int64_t ldo, slab_rows;
-  __device__ const uint16_t* wrow(int, int n) const { return W + static_cast<int64_t>(n) * K; }
-  __device__ void store(const TiledSlice& s, void*, int t) const {
+  __device__ const uint16_t* wbase(int) const { return W; }
+  __device__ void store(const TiledSlice& s, void*, int t, int nt) const {
     const int c4 = (t & 63) * 4;
     if (s.n0 + c4 >= s.N) return;
-    for (int lr = t >> 6; lr < 64; lr += 4) {
+    for (int lr = t >> 6; lr < 64; lr += nt >> 6) {
       const int m = s.row(lr);
       if (m >= s.M) continue;
       const float4 v = *reinterpret_cast<const float4*>(s.c + lr * kCtStride + c4);
@@ -228,11 +231,10 @@ struct TEpiInject {
   int64_t cap;
   RopeFreq freq;
   SeqTable seq;
-  __device__ const uint16_t* wrow(int part, int n) const {
-    const uint16_t* w = (part & 1) ? wv[part >> 1] : wk[part >> 1];
-    return w + static_cast<int64_t>(n) * K;
+  __device__ const uint16_t* wbase(int part) const {
+    return (part & 1) ? wv[part >> 1] : wk[part >> 1];
   }
-  __device__ void store(const TiledSlice& s, void* ext, int t) const {
+  __device__ void store(const TiledSlice& s, void* ext, int t, int nt) const {
     // per local row: position and cache row (rows are grouped by sequence)
     int* pos_t = static_cast<int*>(ext);
     int64_t* row_t = reinterpret_cast<int64_t*>(pos_t + 64);
@@ -258,7 +260,7 @@ struct TEpiInject {
       const int head = (s.n0 + col) / d;
       if (s.n0 + col >= s.N) return;
       const double inv = freq.inv[c];
-      for (int lr = t >> 7; lr < 64; lr += 2) {
+      for (int lr = t >> 7; lr < 64; lr += nt >> 7) {
         if (s.row(lr) >= s.M) continue;
         float cs, sn;
         rope_cos_sin(pos_t[lr], inv, cs, sn);
@@ -272,7 +274,7 @@ struct TEpiInject {
       const int lr = t & 63;
       if (s.row(lr) >= s.M) return;
       const int64_t r = row_t[lr];
-      for (int col = t >> 6; col < kTBN && s.n0 + col < s.N; col += 4)
+      for (int col = t >> 6; col < kTBN && s.n0 + col < s.N; col += nt >> 6)
         stf(vt + static_cast<int64_t>(s.n0 + col) * cap + r, s.at(lr, col));
     }
   }
