@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-timing-pass", action="store_true",
                     help="skip the per-section timing pass (for counter collection)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the batch-16 / long-context / 27B-shaped kernel measurements")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, 5 times "
                          "(scale reference for HBM byte counters) and exit")
@@ -114,6 +116,247 @@ def time_prefill(torch, dr, shape, feats_dev, ctx_all, cache, ws, reps: int = 5)
         tf = fl / (us * 1e-6) / 1e12
         out[name] = {"rows": T, "avg_us": round(us, 2), "TFLOP/s": round(tf, 1),
                      "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+    return out
+
+
+def section_times(torch, dr, fn, sections, reps: int) -> dict:
+    """Mean duration (ms) per section name over every layer and repetition,
+    from HIP events the library records around each section of ``fn()``."""
+    runs = []
+    for _ in range(reps):
+        pts = []
+        for s_, l in sections:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            b.record()
+            pts.append((s_, l, a, b))
+        runs.append(pts)
+    torch.cuda.synchronize()
+    for pts in runs:
+        dr.set_timing(pts)
+        fn()
+    dr.set_timing([])
+    torch.cuda.synchronize()
+    acc = {}
+    for pts in runs:
+        for s_, l, a, b in pts:
+            acc.setdefault(s_, []).append(a.elapsed_time(b))
+    return {k: float(np.mean(v)) for k, v in acc.items()}
+
+
+def event_time_ms(torch, fn, reps: int, warm: int = 2) -> float:
+    """Mean ms per call of ``fn`` over ``reps`` back-to-back calls."""
+    for _ in range(warm):
+        fn()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def layer_sections(n_layers: int) -> list:
+    out = [("lm_head", -1), ("embed", -1), ("final_norm", -1)]
+    for l in range(n_layers):
+        out += [("qkv", l), ("attention", l), ("o_proj", l), ("gate_up", l), ("down", l)]
+    return out
+
+
+def kernel_report(shape, kern_ms: dict, M: int, kv_rows: int) -> dict:
+    """HBM fraction per kernel: weight bytes (+ the M activation rows) for the
+    GEMMs, K and V rows for attention (per layer, per launch)."""
+    H, F, qd, kvd, V = shape.hidden, shape.ffn, shape.q_dim, shape.kv_dim, shape.vocab
+    s = 2
+    kb = {"qkv": (qd + 2 * kvd) * H * s + M * H * s, "o_proj": H * qd * s + M * qd * s,
+          "gate_up": 2 * F * H * s + M * H * s, "down": H * F * s + M * F * s,
+          "lm_head": V * H * s + M * H * s, "attention": kv_rows * kvd * 2 * s}
+    out = {}
+    for k, ms in kern_ms.items():
+        e = {"avg_us": round(ms * 1e3, 2)}
+        if k in kb:
+            gbs = kb[k] / (ms * 1e-3) / 1e9
+            e.update({"bytes": kb[k], "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+        out[k] = e
+    return out
+
+
+def device_weights(torch, shape, seed: int) -> dict:
+    """Seeded random-init weights generated on the device (same distributions
+    as configs.make_weights: matrices N(0, 0.02^2), gains 1 + N(0, 0.02^2))."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    bf = torch.bfloat16
+
+    def mat(r, c):
+        return (torch.randn((r, c), generator=g, device="cuda") * 0.02).to(bf)
+
+    def gain():
+        return (1.0 + 0.02 * torch.randn((shape.hidden,), generator=g, device="cuda")).to(bf)
+
+    H = shape.hidden
+    w = {"fc": mat(H, shape.n_feat * H), "fc_norm": gain(), "final_norm": gain(),
+         "embed": mat(shape.vocab, H), "lm_head": mat(shape.vocab, H), "layers": []}
+    for _ in range(shape.n_layers):
+        w["layers"].append({"attn_norm": gain(), "wq": mat(shape.q_dim, H),
+                            "wk": mat(shape.kv_dim, H), "wv": mat(shape.kv_dim, H),
+                            "wo": mat(H, shape.q_dim), "ffn_norm": gain(),
+                            "wg": mat(shape.ffn, H), "wu": mat(shape.ffn, H),
+                            "wd": mat(H, shape.ffn)})
+    return w
+
+
+def fill_cache(torch, cache, lens, seed: int, std: float = 1.28) -> None:
+    """Context K/V drawn on the device (seeded), committed lengths set."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    for t in cache.k + cache.v:
+        t.copy_(torch.randn(t.shape, generator=g, device="cuda") * std)
+    cache.seq_len[:] = np.asarray(lens, dtype=np.int32)
+
+
+def graph_vs_eager(torch, dr, cache, anchor, draft, ws, reps: int) -> dict:
+    """The per-block launch sequence (one draft_block call) eager and as a
+    replayed HIP graph, same inputs."""
+    dr.set_timing([])
+    eager = event_time_ms(torch, lambda: dr.draft_block(cache, BLOCK, anchor, draft, ws), reps)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            dr.draft_block(cache, BLOCK, anchor, draft, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dr.draft_block(cache, BLOCK, anchor, draft, ws)
+    graph = event_time_ms(torch, g.replay, reps)
+    del g
+    return {"draft_block_eager_us": round(eager * 1e3, 2),
+            "draft_block_graph_us": round(graph * 1e3, 2),
+            "graph_blocks_per_s": round(1e3 / graph, 2)}
+
+
+def workload_batch16(torch, L, configs, synth, dr, shape, reps: int) -> dict:
+    """Batch 16, ragged contexts 512..8192 (M = 256 block rows)."""
+    wl = configs.qwen3_8b_b16_ragged()
+    lens = list(wl.ctx)
+    cache = L.KVCache(shape, [n + 64 for n in lens])
+    fill_cache(torch, cache, lens, 3001)
+    anchors = torch.from_numpy(configs.make_anchors(shape, wl.wid, wl.batch)).cuda()
+    draft = torch.empty((wl.batch, BLOCK - 1), dtype=torch.int32, device="cuda")
+    ws = dr.workspace(wl.batch, BLOCK, 1)
+    fn = lambda: dr.draft_block(cache, BLOCK, anchors, draft, ws)
+    ms = event_time_ms(torch, fn, reps)
+    M = wl.batch * BLOCK
+    kern = section_times(torch, dr, fn, layer_sections(shape.n_layers), max(3, reps // 4))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3002)
+    logits = torch.randn((wl.batch, BLOCK, shape.vocab), generator=g, device="cuda").to(torch.bfloat16)
+    acc = torch.empty(wl.batch, dtype=torch.int32, device="cuda")
+    bon = torch.empty(wl.batch, dtype=torch.int32, device="cuda")
+    vws = torch.empty(L.verify_workspace_size(wl.batch, BLOCK, shape.vocab), dtype=torch.uint8,
+                      device="cuda")
+    v_ms = event_time_ms(torch, lambda: L.verify_greedy(logits, draft, acc, bon, vws), reps)
+    v_bytes = wl.batch * BLOCK * shape.vocab * 2
+    out = {"workload": wl.name, "ctx_sum": int(sum(lens)), "draft_block_ms": round(ms, 4),
+           "blocks_per_s": round(wl.batch / (ms * 1e-3), 1),
+           "kernels": kernel_report(shape, kern, M, sum(lens) + wl.batch * BLOCK),
+           "verify": {"avg_us": round(v_ms * 1e3, 2), "bytes": v_bytes,
+                      "hbm_frac": round(v_bytes / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+    del cache
+    return out
+
+
+def workload_long(torch, L, configs, dr, shape, repeats: int = 3) -> dict:
+    """Batch 1: one 32768-token prefill (fuse + inject), then 256 steps that
+    each append n ~ U{1..16} fresh feature rows and draft a 16-slot block."""
+    wl = configs.qwen3_8b_long_incremental()
+    from block_diffusion_drafter_concat_amd import synth
+    T, steps, cap = wl.ctx[0], wl.extra["steps"], wl.extra["capacity"]
+    H = shape.hidden
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4001)
+    feats = [torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16)
+             for _ in range(shape.n_feat)]
+    ctx = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    cache = L.KVCache(shape, [cap])
+    ws = dr.workspace(1, BLOCK, T)
+    sec = section_times(torch, dr, lambda: (dr.fuse_context(feats, ctx, ws),
+                                            dr.inject_kv(ctx, [T], cache, ws, pos_start=[0])),
+                        [("fuse_gemm", -1), ("inject", -1)], 2)
+    pre = {}
+    for name, key, fl in (("fusion_gemm", "fuse_gemm", 2.0 * T * shape.n_feat * H * H),
+                          ("injection_gemm", "inject", 2.0 * T * H * shape.n_layers * 2 * shape.kv_dim)):
+        tf = fl / (sec[key] * 1e-3) / 1e12
+        pre[name] = {"rows": T, "avg_us": round(sec[key] * 1e3, 1), "TFLOP/s": round(tf, 1),
+                     "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+    del feats
+    n_new = synth.integers((steps,), 1, 16, wl.wid, synth.STREAM_INDICES, "n_new")
+    pool = [torch.randn((steps * BLOCK, H), generator=g, device="cuda").to(torch.bfloat16)
+            for _ in range(shape.n_feat)]
+    ctx_new = torch.empty((BLOCK, H), dtype=torch.bfloat16, device="cuda")
+    anchor = torch.from_numpy(configs.make_anchors(shape, wl.wid, 1)).cuda()
+    draft = torch.empty((1, BLOCK - 1), dtype=torch.int32, device="cuda")
+
+    def loop():
+        for i in range(steps):
+            n = int(n_new[i])
+            dr.fuse_context([p[i * BLOCK:i * BLOCK + n] for p in pool], ctx_new, ws)
+            dr.inject_kv(ctx_new, [n], cache, ws)
+            dr.draft_block(cache, BLOCK, anchor, draft, ws)
+
+    times = []
+    for _ in range(repeats):
+        cache.seq_len[:] = T          # restore the post-prefill snapshot
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        loop()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    end_len = int(cache.seq_len[0])
+    # per-kernel figures at the end of the loop (context ~ end_len)
+    kern = section_times(torch, dr, lambda: dr.draft_block(cache, BLOCK, anchor, draft, ws),
+                         layer_sections(shape.n_layers), 4)
+    out = {"workload": wl.name, "prefill": pre, "loop_ms": round(float(np.median(times)), 3),
+           "loop_ms_all": [round(t, 3) for t in times],
+           "mean_step_ms": round(float(np.median(times)) / steps, 4),
+           "ctx_after_loop": end_len,
+           "kernels_at_end": kernel_report(shape, kern, BLOCK, end_len + BLOCK)}
+    del cache, pool
+    return out
+
+
+def workload_27b(torch, L, configs, reps: int) -> dict:
+    """27B-target-shaped drafter (H 5120, 40/8 heads, FFN 17408), batch 8,
+    context 4096 each, blocks of 8 and 16 slots."""
+    shape = configs.TARGET_27B_LIKE
+    w = device_weights(torch, shape, 5001)
+    dr = L.Drafter(shape, w)
+    wl = configs.target27b_b8()
+    lens = list(wl.ctx)
+    cache = L.KVCache(shape, [n + 64 for n in lens])
+    fill_cache(torch, cache, lens, 5002)
+    anchors = torch.from_numpy(configs.make_anchors(shape, wl.wid, wl.batch)).cuda()
+    out = {"workload": "27b-target-shaped 5-layer bf16, batch 8, ctx 4096"}
+    for B in (8, 16):
+        draft = torch.empty((wl.batch, B - 1), dtype=torch.int32, device="cuda")
+        ws = dr.workspace(wl.batch, B, 1)
+        fn = lambda: dr.draft_block(cache, B, anchors, draft, ws)
+        ms = event_time_ms(torch, fn, reps)
+        kern = section_times(torch, dr, fn, layer_sections(shape.n_layers), max(3, reps // 4))
+        out[f"B{B}"] = {"draft_block_ms": round(ms, 4),
+                        "blocks_per_s": round(wl.batch / (ms * 1e-3), 1),
+                        "kernels": kernel_report(shape, kern, wl.batch * B,
+                                                 sum(lens) + wl.batch * B)}
+    dr.close()
+    del cache, w
     return out
 
 
@@ -287,6 +530,25 @@ def main():
     step_roof = {"bytes_per_step": tot, "roofline_ms": tot / (HBM_PEAK_GBS * 1e9) * 1e3,
                  "frac": round(tot / (HBM_PEAK_GBS * 1e9) / (ms_per_step * 1e-3), 4)}
 
+    # ---- the per-block launch sequence as a HIP graph, then other workloads
+    graph = graph_vs_eager(torch, dr, cache, anchor, draft, ws, K)
+    log(f"graph: {graph}")
+    workloads = None
+    if not args.no_workloads:
+        workloads = {}
+        t1 = time.time()
+        workloads["batch16_ragged"] = workload_batch16(torch, L, configs, synth, dr, shape, 20)
+        log(f"batch-16 ragged done ({time.time() - t1:.1f}s)")
+        t1 = time.time()
+        workloads["long_ctx_incremental"] = workload_long(torch, L, configs, dr, shape)
+        log(f"long-context loop done ({time.time() - t1:.1f}s)")
+        dr.close()
+        del dr
+        torch.cuda.empty_cache()
+        t1 = time.time()
+        workloads["target27b_batch8"] = workload_27b(torch, L, configs, 20)
+        log(f"27b-shaped done ({time.time() - t1:.1f}s)")
+
     # ---- CPU oracle on a bounded sample of the same workload
     cpu = None
     if not args.no_cpu_baseline:
@@ -310,6 +572,8 @@ def main():
         "step_roofline": step_roof,
         "kernels": kernels,
         "prefill_mfma": prefill,
+        "graph": graph,
+        "workloads": workloads,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
