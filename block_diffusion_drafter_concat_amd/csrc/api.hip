@@ -71,8 +71,39 @@ int pick_ksplit(int n_tiles, int K) {
     ks *= 2;
   return ks;
 }
-// Rows from which bf16 fusion / injection use the LDS-tiled GEMM.
+// Rows from which bf16 fusion / injection use the LDS-tiled GEMM, and its
+// tile for them (8 waves, 2 x 4: two per SIMD, 128 accumulators each).
 constexpr int kTiledMinRows = 129;
+constexpr int kPreBM = 256, kPreBN = 256;
+// Block rows (batch x slots) from which a bf16 draft runs its layer GEMMs and
+// LM head on the LDS-tiled GEMM instead of the weight-streaming one.
+constexpr int kMidMinRows = 64;
+
+// Mid-M plan: K splits of the partial-slab GEMMs.  A split is taken while the
+// workgroups stay under ~1.25 per compute unit and the fp32 partial slabs it
+// adds stay under half the weight bytes.
+struct MidPlan {
+  int ks_qkv, ks_o, ks_d;
+};
+int mid_ksplit(int64_t tiles, int K, int64_t w_bytes, int64_t slab_bytes, int max_ks = 8) {
+  int ks = 1;
+  while (ks < max_ks && tiles * ks * 2 <= 320 && K % (ks * 2 * kTBK) == 0 &&
+         ks * 2 * slab_bytes <= w_bytes / 2)
+    ks *= 2;
+  return ks;
+}
+MidPlan mid_plan(const Dims& D, int M) {
+  const int64_t nq = D.qd + 2 * D.kvd;
+  MidPlan p;
+  p.ks_qkv = mid_ksplit((nq + 127) / 128, D.H, nq * D.H * 2, static_cast<int64_t>(M) * nq * 4);
+  // the residual-norm kernel sums up to 8 slabs for H <= 4096, 4 above
+  const int max_rn = D.H <= 4096 ? 8 : 4;
+  p.ks_o = mid_ksplit((D.H + 127) / 128, D.qd, static_cast<int64_t>(D.H) * D.qd * 2,
+                      static_cast<int64_t>(M) * D.H * 4, max_rn);
+  p.ks_d = mid_ksplit((D.H + 127) / 128, D.F, static_cast<int64_t>(D.H) * D.F * 2,
+                      static_cast<int64_t>(M) * D.H * 4, max_rn);
+  return p;
+}
 
 // Fusion K-split.  Weight-streaming path: only for short incremental calls.
 // Tiled path: split until the 256 x 256 tiles times the split fill the 256
@@ -81,9 +112,10 @@ int fuse_ksplit(const dflash_handle* h, int64_t T) {
   const Dims D = dims(h->cfg);
   const int K = D.nf * D.H;
   if (h->cfg.dtype == DFLASH_BF16 && T >= kTiledMinRows) {
-    const int64_t tiles = ((T + kTBM - 1) / kTBM) * ((D.H + kTBN - 1) / kTBN);
+    const int64_t tiles = ((T + kPreBM - 1) / kPreBM) * ((D.H + kPreBN - 1) / kPreBN);
+    const int max_ks = D.H <= 4096 ? 8 : 4;   // partial slabs the norm kernel sums
     int ks = 1;
-    while (ks < 8 && 2 * ks * tiles <= 256 && K % (2 * ks * kTBK) == 0) ks *= 2;
+    while (ks < max_ks && 2 * ks * tiles <= 256 && K % (2 * ks * kTBK) == 0) ks *= 2;
     return ks;
   }
   return T <= 64 ? pick_ksplit(D.H / 32, K) : 1;
@@ -99,7 +131,7 @@ int64_t fuse_part_rows(const dflash_handle* h, int64_t t_max) {
   };
   consider(64);
   consider(kTiledMinRows - 1);
-  for (int64_t tm = 1; (tm - 1) * kTBM < t_max; ++tm) consider(tm * kTBM);
+  for (int64_t tm = 1; (tm - 1) * kPreBM < t_max; ++tm) consider(tm * kPreBM);
   consider(t_max);
   return best;
 }
@@ -123,7 +155,7 @@ GemmPlan gemm_plan(const Dims& D) {
 // Every call lays out its own scratch from offset 0 with sizes that grow with
 // (batch, block, tokens); dflash_workspace_size takes the largest.
 struct Layout {
-  size_t x_off, u_off, q_off, o_off, h_off, part_off, lm_off, ao_off, aml_off, ver_off;
+  size_t x_off, u_off, q_off, o_off, h_off, part_off, qkvp_off, lm_off, ao_off, aml_off, ver_off;
   size_t total;
 };
 
@@ -144,7 +176,17 @@ Layout layout(const dflash_handle* h, int max_batch, int max_block, int64_t max_
   size_t part = static_cast<size_t>(g.ks_o > g.ks_d ? g.ks_o : g.ks_d) * M * D.H * 4;
   const size_t pf = static_cast<size_t>(fuse_part_rows(h, static_cast<int64_t>(T))) * D.H * 4;
   part = pf > part ? pf : part;
+  size_t qkvp = 0;
+  if (h->cfg.dtype == DFLASH_BF16 && M >= static_cast<size_t>(kMidMinRows)) {
+    // the mid-M path at every row count up to M (splits shrink as M grows)
+    for (size_t m = kMidMinRows; m <= M; ++m) {
+      const MidPlan mp = mid_plan(D, static_cast<int>(m));
+      part = std::max(part, static_cast<size_t>(std::max(mp.ks_o, mp.ks_d)) * m * D.H * 4);
+      qkvp = std::max(qkvp, static_cast<size_t>(mp.ks_qkv) * m * (D.qd + 2 * D.kvd) * 4);
+    }
+  }
   L.part_off = off; off += align_up(part);
+  L.qkvp_off = off; off += align_up(qkvp);
   L.lm_off = off;   off += align_up(M * g.wg_lm * 8);
   const size_t qr = static_cast<size_t>((D.G * max_block + 15) / 16 * 16);
   const size_t slots = static_cast<size_t>(max_batch) * D.Hkv * kMaxAttnChunks;
@@ -224,25 +266,38 @@ hipError_t run_rows(AOperand<T> A, int K, int n_tiles, int tiles_per_wg, int ksp
   }
   return hipSuccess;
 }
-// 8 waves (2 x 4) per 256 x 256 tile: two waves per SIMD, 128 accumulators each.
-constexpr int kTiledWM = 2, kTiledWN = 4;
-
-template <class Epi>
-hipError_t launch_tiled(const AOperand<uint16_t>& A, int N, int K, int parts, int ksplit,
-                        const Epi& epi, hipStream_t st) {
-  auto kern = &tiled_gemm_kernel<kTiledWM, kTiledWN, Epi>;
+template <int BM, int BN, int WM, int WN, class Epi>
+hipError_t launch_tiled_cfg(const AOperand<uint16_t>& A, int N, int K, int parts, int ksplit,
+                            const Epi& epi, hipStream_t st) {
+  auto kern = &tiled_gemm_kernel<BM, BN, WM, WN, Epi>;
+  constexpr size_t lds = tiled_lds_bytes(BM, BN);
   static std::atomic<bool> attr_set{false};
   if (!attr_set.load()) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(kTiledLds));
+                                       static_cast<int>(lds));
     if (e != hipSuccess) return e;
     attr_set.store(true);
   }
-  const int tm = (A.M + kTBM - 1) / kTBM, tn = (N + kTBN - 1) / kTBN;
-  kern<<<dim3(tm * tn, parts, ksplit), kTiledWM * kTiledWN * 64, kTiledLds, st>>>(A, N, K, tm,
-                                                                                  tn, epi);
+  const int tm = (A.M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  kern<<<dim3(tm * tn, parts, ksplit), WM * WN * 64, lds, st>>>(A, N, K, tm, tn, epi);
   return hipGetLastError();
+}
+
+// Prefill fusion / injection: 256 x 256 tiles.
+template <class Epi>
+hipError_t launch_tiled(const AOperand<uint16_t>& A, int N, int K, int parts, int ksplit,
+                        const Epi& epi, hipStream_t st) {
+  return launch_tiled_cfg<kPreBM, kPreBN, 2, 4>(A, N, K, parts, ksplit, epi, st);
+}
+
+// A batch of blocks (M = 64 .. 256 rows): the row tile covers M.
+template <int BN, class Epi>
+hipError_t launch_mid(const AOperand<uint16_t>& A, int N, int K, int ksplit, const Epi& epi,
+                      hipStream_t st) {
+  if (A.M <= 64) return launch_tiled_cfg<64, BN, 1, 4>(A, N, K, 1, ksplit, epi, st);
+  if (A.M <= 128) return launch_tiled_cfg<128, BN, 2, 4>(A, N, K, 1, ksplit, epi, st);
+  return launch_tiled_cfg<256, BN, 2, 4>(A, N, K, 1, ksplit, epi, st);
 }
 
 struct NoPerLaunch {
@@ -407,6 +462,14 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
   T* hb = at<T>(ws, L.h_off);
   float* part = at<float>(ws, L.part_off);
   const int64_t pstride = static_cast<int64_t>(M) * D.H;   // one K-split slab
+  // batches of blocks: the layer GEMMs and the LM head on the LDS-tiled GEMM
+  const bool mid = bf && M >= kMidMinRows;
+  const MidPlan mp = mid_plan(D, M);
+  const int ks_o = mid ? mp.ks_o : g.ks_o, ks_d = mid ? mp.ks_d : g.ks_d;
+  float* qkvp = at<float>(ws, L.qkvp_off);
+  auto a16 = [&](const void* p, int K) {
+    return a_single<uint16_t>(p, K, K, M);
+  };
 
   // block embedding fused with layer 0's attention RMSNorm
   DF_MARK(DFLASH_SEC_EMBED, -1, false);
@@ -444,7 +507,15 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
       DF_MARK(DFLASH_SEC_ATTN_NORM, l, true);
     }
     DF_MARK(DFLASH_SEC_QKV, l, false);
-    {
+    if (mid) {
+      const int nq = D.qd + 2 * D.kvd;
+      TEpiQKVParts e{static_cast<const uint16_t*>(w.wq), static_cast<const uint16_t*>(w.wk),
+                     static_cast<const uint16_t*>(w.wv), D.H, D.qd, D.kvd, qkvp, nq, M};
+      DF_HIP(launch_mid<128>(a16(u, D.H), nq, D.H, mp.ks_qkv, e, st));
+      DF_HIP(launch_qkv_finish(true, qkvp, mp.ks_qkv, static_cast<int64_t>(M) * nq, M, D.qd,
+                               D.kvd, D.d, B, qb, D.qd, kv->k[l], kv->v[l], kv->cap_total, freq,
+                               seq, st));
+    } else {
       EpiQKV<T> e{};
       e.wq = static_cast<const T*>(w.wq);
       e.wk = static_cast<const T*>(w.wk);
@@ -467,7 +538,10 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
     DF_HIP(launch_block_attention(bf, D.d, aa, nb, st));
     DF_MARK(DFLASH_SEC_ATTENTION, l, true);
     DF_MARK(DFLASH_SEC_O_PROJ, l, false);
-    {
+    if (mid) {
+      TEpiStoreF32 e{static_cast<const uint16_t*>(w.wo), D.qd, part, D.H, M};
+      DF_HIP(launch_mid<128>(a16(ob, D.qd), D.H, D.qd, ks_o, e, st));
+    } else {
       EpiPartialF32<T> e{static_cast<const T*>(w.wo), D.qd, part, D.H, M};
       DF_HIP(run_rows<T>(a_single<T>(ob, D.qd, D.qd, M), D.qd, g.tiles_o, 1, g.ks_o, e, st,
                          NoPerLaunch{}));
@@ -475,23 +549,30 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
     DF_MARK(DFLASH_SEC_O_PROJ, l, true);
     // feed-forward half: x += O partials; u = RMSNorm(x)
     DF_MARK(DFLASH_SEC_FFN_NORM, l, false);
-    DF_HIP(launch_resid_rmsnorm(bf, x, part, g.ks_o, pstride, w.ffn_norm, u, M, D.H, eps, st));
+    DF_HIP(launch_resid_rmsnorm(bf, x, part, ks_o, pstride, w.ffn_norm, u, M, D.H, eps, st));
     DF_MARK(DFLASH_SEC_FFN_NORM, l, true);
     DF_MARK(DFLASH_SEC_GATE_UP, l, false);
-    {
+    if (mid) {
+      TEpiSwiGLUPair e{static_cast<const uint16_t*>(w.wg), static_cast<const uint16_t*>(w.wu),
+                       D.H, D.F, 128, reinterpret_cast<uint16_t*>(hb), D.F};
+      DF_HIP(launch_mid<128>(a16(u, D.H), 2 * D.F, D.H, 1, e, st));
+    } else {
       EpiSwiGLU<T> e{static_cast<const T*>(w.wg), static_cast<const T*>(w.wu), D.H, hb, D.F};
       DF_HIP(run_rows<T>(a_single<T>(u, D.H, D.H, M), D.H, g.tiles_gu, 1, 1, e, st,
                          NoPerLaunch{}));
     }
     DF_MARK(DFLASH_SEC_GATE_UP, l, true);
     DF_MARK(DFLASH_SEC_DOWN, l, false);
-    {
+    if (mid) {
+      TEpiStoreF32 e{static_cast<const uint16_t*>(w.wd), D.F, part, D.H, M};
+      DF_HIP(launch_mid<128>(a16(hb, D.F), D.H, D.F, ks_d, e, st));
+    } else {
       EpiPartialF32<T> e{static_cast<const T*>(w.wd), D.F, part, D.H, M};
       DF_HIP(run_rows<T>(a_single<T>(hb, D.F, D.F, M), D.F, g.tiles_d, 1, g.ks_d, e, st,
                          NoPerLaunch{}));
     }
     DF_MARK(DFLASH_SEC_DOWN, l, true);
-    pending = g.ks_d;
+    pending = ks_d;
   }
   // x += down partials of the last layer; u = RMSNorm(x)
   DF_MARK(DFLASH_SEC_FINAL_NORM, -1, false);
@@ -507,7 +588,13 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
     EpiLMHead<T, 4> e4{static_cast<const T*>(h->w.lm_head), D.H, D.V, g.wg_lm, lm_part, dbg_z};
     EpiLMHead<T, 8> e8{static_cast<const T*>(h->w.lm_head), D.H, D.V, g.wg_lm, lm_part, dbg_z};
     const AOperand<T> A = a_single<T>(u, D.H, D.H, M);
-    for (int m0 = 0; m0 < M; m0 += kMaxRowsPerLaunch) {
+    if (mid) {
+      const int n_parts = (D.V + 255) / 256;
+      TEpiArgmax e{static_cast<const uint16_t*>(h->w.lm_head), D.H, D.V, n_parts, lm_part, dbg_z};
+      DF_HIP(launch_mid<256>(a16(u, D.H), D.V, D.H, 1, e, st));
+      DF_HIP(launch_lm_argmax_finalize(lm_part, n_parts, M, B, draft, st));
+    }
+    for (int m0 = 0; !mid && m0 < M; m0 += kMaxRowsPerLaunch) {
       AOperand<T> Ai = A;
       Ai.m0 = m0;
       Ai.mc = M - m0 < kMaxRowsPerLaunch ? M - m0 : kMaxRowsPerLaunch;
@@ -519,7 +606,7 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
       else e = launch_skinny_nw<T, 4>(Ai, D.H, g.tiles_lm, kLmTilesPerWg, 1, e8, st);
       DF_HIP(e);
     }
-    DF_HIP(launch_lm_argmax_finalize(lm_part, g.wg_lm, M, B, draft, st));
+    if (!mid) DF_HIP(launch_lm_argmax_finalize(lm_part, g.wg_lm, M, B, draft, st));
   }
   DF_MARK(DFLASH_SEC_LM_HEAD, -1, true);
   return DFLASH_OK;

@@ -1,24 +1,27 @@
-// LDS-tiled bf16 MFMA GEMM for many rows: out[m, n] = sum_k A[m, k] * W[n, k].
+// LDS-tiled bf16 MFMA GEMM: out[m, n] = sum_k A[m, k] * W[n, k].
 //
-// Used where M is large enough that the problem is compute-bound (fusion and
-// injection over a prefill of T context rows).  Design for CDNA4 (gfx950):
-//   - workgroup tile 256 x 256 (rows of A x rows of W), 4 waves in a 2 x 2
-//     grid, each wave 128 x 128 = 8 x 8 MFMA tiles of 16 x 16 (fp32
-//     accumulators, 256 per lane, held in AGPRs);
-//   - K in stages of 64: both operand tiles (2 x 32 KB) go through LDS, double
-//     buffered; the next stage is loaded straight into LDS (buffer loads with
-//     the LDS-destination bit, no staging registers) while the current one
-//     feeds the MFMAs.  16-byte chunks are XOR-swizzled by row so that the
-//     fragment reads (16 rows x 16 bytes per instruction) hit distinct banks;
+// Used wherever the rows are many enough for the MFMA units to matter: the
+// fusion and injection GEMMs over a prefill, and the layer GEMMs and LM head
+// of a batch of blocks (M = 64 .. 256 rows).  Design for CDNA4 (gfx950):
+//   - workgroup tile BM x BN (rows of A x rows of W), WM x WN waves, each wave
+//     (BM/WM) x (BN/WN) as 16 x 16 MFMA tiles with fp32 accumulators;
+//   - K in stages of 64: both operand tiles go through LDS, double buffered.
+//     The next stage is loaded straight into LDS (buffer loads with the
+//     LDS-destination bit, no staging registers) while the current one feeds
+//     the MFMAs.  16-byte chunks are XOR-swizzled by row so that the fragment
+//     reads (16 rows x 16 bytes per instruction) hit distinct banks;
+//   - every 8-row load instruction of the W tile has its own buffer resource,
+//     from the epilogue's W-row map, so one tile can draw rows from several
+//     matrices (q/k/v, gate/up pairs) and rows past a matrix's end read zero;
 //   - tiles are walked in an XCD-aware order: workgroup w runs on XCD w % 8,
 //     so consecutive tile indices are given to the same XCD, and inside an
 //     XCD's range tiles go in groups of 4 row-tiles, so the A and W tiles a
 //     group shares stay in that XCD's L2;
 //   - grid.y selects an output part (e.g. a layer's K or V projection), grid.z
 //     a K split whose fp32 partial the consumer sums;
-//   - the accumulators leave through LDS in four 64-row slices, so the
-//     epilogue sees whole rows of the 256-column tile and can store them
-//     coalesced (and RoPE pairs (c, c + d/2) of a head are both at hand).
+//   - the accumulators leave through LDS in 64-row slices, so the epilogue
+//     sees whole rows of the tile and can store them coalesced (and RoPE
+//     pairs (c, c + d/2) of a head are both at hand).
 #pragma once
 
 #include "device_common.h"
@@ -26,24 +29,33 @@
 
 namespace dflash {
 
-constexpr int kTBM = 256, kTBN = 256, kTBK = 64;
+constexpr int kTBK = 64;
+constexpr int kTiledEpiLds = 1024;   // epilogue's own LDS after the C slice
 
-// Row r, 16-byte chunk c (of 8 per 64-element row) of a 256 x 64 LDS tile.
+// Row r, 16-byte chunk c (of 8 per 64-element row) of an LDS operand tile.
 __device__ __forceinline__ int swz(int r, int c) { return r * 64 + ((c ^ (r & 7)) << 3); }
 
-// One 64-row slice of a finished 256 x 256 tile in LDS, as the epilogue sees
-// it.  Local rows come in runs of `run` rows, one run per wave row; run r
-// starts at output row m_base + r * wave_rows.  Column c is output column
-// n0 + c.
-constexpr int kCtStride = kTBN + 4;   // padded fp32 row stride (no bank conflicts)
-constexpr int kTiledEpiLds = 1024;
+// Dynamic LDS of one launch: two stages of both operand tiles.
+constexpr size_t tiled_lds_bytes(int BM, int BN) {
+  return static_cast<size_t>(2) * (BM + BN) * kTBK * sizeof(uint16_t);
+}
+
+// One 64-row slice of a finished tile in LDS, as the epilogue sees it.  Local
+// rows come in runs of `run` rows, one run per wave row; run r starts at
+// output row m_base + r * wave_rows.  Column c < bn is output column n0 + c.
 struct TiledSlice {
   const float* c;
-  int m_base, run, wave_rows, M, n0, N, part, split;
+  int ld;   // fp32 row stride of c
+  int m_base, run, wave_rows, M, n0, N, bn, part, split, tile_n;
   __device__ int row(int lr) const { return m_base + (lr / run) * wave_rows + lr % run; }
-  __device__ float at(int lr, int col) const { return c[lr * kCtStride + col]; }
+  __device__ float at(int lr, int col) const { return c[lr * ld + col]; }
 };
-static_assert(64 * kCtStride * 4 + kTiledEpiLds <= 2 * 2 * kTBM * kTBK * 2, "slice fits in LDS");
+
+// W rows [n, n + 8) of part p: where they start and how many are real.
+struct WRows {
+  const uint16_t* p;
+  int valid;
+};
 
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
@@ -54,20 +66,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, ui
                                            0x00020000);
 }
 
-// WM x WN waves; wave (wm, wn) owns rows wm * 256/WM and columns
-// wn * 256/WN of the tile as MI x NJ MFMA tiles of 16 x 16.
-template <int WM, int WN, class Epi>
+template <int BM, int BN, int WM, int WN, class Epi>
 __global__ __launch_bounds__(WM * WN * 64) void tiled_gemm_kernel(AOperand<uint16_t> A, int N,
                                                                   int K, int tiles_m,
                                                                   int tiles_n, Epi epi) {
   constexpr int NWAVES = WM * WN, NT = NWAVES * 64;
-  constexpr int RW = kTBM / WM, CW = kTBN / WN;   // wave tile
+  constexpr int RW = BM / WM, CW = BN / WN;   // wave tile
   constexpr int MI = RW / 16, NJ = CW / 16;
-  constexpr int LI = 32 / NWAVES;                 // loads per wave per operand
-  static_assert(MI % 4 == 0, "four epilogue slices per wave row");
+  constexpr int LA = BM / 8 / NWAVES, LW = BN / 8 / NWAVES;   // load instructions per wave
+  constexpr int NSL = BM / 64, RUN = RW / NSL, QI = RUN / 16;  // epilogue slices
+  constexpr int CT_LD = BN + 4;               // padded fp32 row stride of a C slice
+  static_assert(LA * 8 * NWAVES == BM && LW * 8 * NWAVES == BN, "whole load instructions");
+  static_assert(BM % 64 == 0 && RUN % 16 == 0 && RUN * WM == 64, "64-row slices");
+  static_assert(64 * CT_LD * 4 + kTiledEpiLds <= tiled_lds_bytes(BM, BN), "slice fits in LDS");
+
   const int part = blockIdx.y;    // output part (uniform per workgroup)
   const int split = blockIdx.z;   // K split
-  extern __shared__ __align__(16) uint16_t lds[];   // [2][A 256x64 | W 256x64]
+  extern __shared__ __align__(16) uint16_t lds[];   // [2][A BMx64 | W BNx64]
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int r16 = lane & 15, kg = lane >> 4;
@@ -88,42 +103,56 @@ __global__ __launch_bounds__(WM * WN * 64) void tiled_gemm_kernel(AOperand<uint1
   const int in_g = tile % group_size;
   const int tm = g0 + in_g % gm;
   const int tn = in_g / gm;
-  const int m0 = tm * kTBM, n0 = tn * kTBN;
+  const int m0 = tm * BM, n0 = tn * BN;
 
   const int kper = K / gridDim.z;
   const int kbeg = split * kper;
 
   // ---- global -> LDS without registers (buffer_load ... lds).  One wave
   // instruction fills 1 KB of LDS: 8 tile rows of 8 16-byte chunks, lane l
-  // landing at chunk l of the run.  Instruction i of wave w covers tile rows
-  // 8 (w LI + i) .. +8; lane l takes row 8 (w LI + i) + l / 8 and, so that the
-  // XOR swizzle holds, global chunk (l % 8) ^ (l / 8).  Rows past M or N
-  // read as zero through the buffer range check.
-  const int lrow = 8 * LI * wave + (lane >> 3);
+  // landing at chunk l of the run.  Lane l takes row l / 8 of the run and,
+  // so that the XOR swizzle holds, global chunk (l % 8) ^ (l / 8).  Each
+  // instruction has its own buffer resource starting at its first row and
+  // covering its rows that exist; the range check covers the VGPR (row,
+  // chunk) and SGPR (k) offsets together, so rows past M (or past a W
+  // matrix's end) read as zero.
+  const int lrow = lane >> 3;
   const int gchunk = (lane & 7) ^ (lane >> 3);
   const uint32_t a_voff = static_cast<uint32_t>(lrow * A.lda * 2 + gchunk * 16);
   const uint32_t w_voff = static_cast<uint32_t>(lrow * K * 2 + gchunk * 16);
-  const uint32_t a_istep = static_cast<uint32_t>(8 * A.lda * 2);
-  const uint32_t w_istep = static_cast<uint32_t>(8 * K * 2);
-  const __amdgpu_buffer_rsrc_t wrs =
-      tile_rsrc(epi.wbase(part) + static_cast<int64_t>(n0) * K,
-                static_cast<uint64_t>(N - n0) * static_cast<uint64_t>(K) * 2);
-  const uint64_t a_bytes = static_cast<uint64_t>(A.M - m0) * static_cast<uint64_t>(A.lda) * 2;
+  // bytes of rows [0, valid) of an 8-row run (valid <= 8)
+  auto run_bytes = [](int valid, int ld) -> uint64_t {
+    valid = valid < 8 ? valid : 8;
+    return valid > 0 ? static_cast<uint64_t>(valid) * ld * 2 : 0;
+  };
+  const int a_row0 = m0 + 8 * LA * wave;   // rows of A this wave loads
+  const uint16_t* wptr[LW];   // first W row of each load instruction
+  uint64_t wbytes[LW];
+#pragma unroll
+  for (int i = 0; i < LW; ++i) {
+    const WRows wr = epi.wrows(part, n0 + 8 * (wave * LW + i), N);
+    wptr[i] = wr.p;
+    wbytes[i] = run_bytes(wr.valid, K);
+  }
   auto issue = [&](int k0, int buf) {
     const int s = k0 / A.slab_k;
     const int col = k0 - s * A.slab_k;
-    const __amdgpu_buffer_rsrc_t ars =
-        tile_rsrc(A.slab[s] + static_cast<int64_t>(m0) * A.lda, a_bytes);
-    lds_u16* la = (lds_u16*)(lds) + buf * (2 * kTBM * kTBK) + wave * (LI * 512);
-    lds_u16* lw = la + kTBM * kTBK;
+    lds_u16* la = (lds_u16*)(lds) + buf * ((BM + BN) * kTBK) + wave * (LA * 512);
+    lds_u16* lw = (lds_u16*)(lds) + buf * ((BM + BN) * kTBK) + BM * kTBK + wave * (LW * 512);
 #pragma unroll
-    for (int i = 0; i < LI; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, la + i * 512, 16, a_voff,
-                                               i * a_istep + col * 2, 0, 0);
+    for (int i = 0; i < LA; ++i) {
+      const int r0 = a_row0 + 8 * i;
+      const __amdgpu_buffer_rsrc_t ars = tile_rsrc(
+          A.slab[s] + static_cast<int64_t>(min(r0, A.M)) * A.lda, run_bytes(A.M - r0, A.lda));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, la + i * 512, 16, a_voff, col * 2, 0, 0);
+    }
 #pragma unroll
-    for (int i = 0; i < LI; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, lw + i * 512, 16, w_voff,
-                                               i * w_istep + k0 * 2, 0, 0);
+    for (int i = 0; i < LW; ++i) {
+      // (bound to a local: a resource temporary passed straight to the builtin
+      // makes the host pass drop the kernel's launch stub)
+      const __amdgpu_buffer_rsrc_t wrs = tile_rsrc(wptr[i], wbytes[i]);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, lw + i * 512, 16, w_voff, k0 * 2, 0, 0);
+    }
   };
 
   f32x4 acc[MI][NJ];
@@ -138,8 +167,8 @@ __global__ __launch_bounds__(WM * WN * 64) void tiled_gemm_kernel(AOperand<uint1
   // other buffer was last read in the previous stage, which every thread
   // finished before the previous barrier.
   auto stage = [&](int buf, bool next, int k_next) {
-    const uint16_t* la = lds + buf * (2 * kTBM * kTBK);
-    const uint16_t* lw = la + kTBM * kTBK;
+    const uint16_t* la = lds + buf * ((BM + BN) * kTBK);
+    const uint16_t* lw = la + BM * kTBK;
     Frag8<uint16_t> af[2][MI], bf[2][NJ];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -171,49 +200,141 @@ __global__ __launch_bounds__(WM * WN * 64) void tiled_gemm_kernel(AOperand<uint1
   for (int st = 0; st + 1 < n_stages; ++st) stage(st & 1, true, kbeg + (st + 1) * kTBK);
   stage((n_stages - 1) & 1, false, 0);
 
-  // ---- epilogue: four slices of 64 rows.  Slice q takes MFMA rows
-  // i in [q MI/4, (q+1) MI/4) of every wave: local row lr = wm * 4 MI +
-  // (i - q MI/4) * 16 + kg * 4 + jj, stored as C[64][kCtStride] fp32.  C tile
+  // ---- epilogue: NSL slices of 64 rows.  Slice q takes MFMA rows
+  // i in [q QI, (q+1) QI) of every wave: local row lr = wm * RUN +
+  // (i - q QI) * 16 + kg * 4 + jj, stored as C[64][CT_LD] fp32.  C tile
   // (i, j) lane holds rows i*16 + kg*4 + jj, column j*16 + r16.
-  constexpr int QI = MI / 4, RUN = 16 * QI;
   float* ct = reinterpret_cast<float*>(lds);
-  void* ext = ct + 64 * kCtStride;   // epilogue's own LDS (kTiledEpiLds bytes)
+  void* ext = ct + 64 * CT_LD;   // epilogue's own LDS (kTiledEpiLds bytes)
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < NSL; ++q) {
 #pragma unroll
     for (int ii = 0; ii < QI; ++ii)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
-          ct[(wm * RUN + ii * 16 + kg * 4 + jj) * kCtStride + wn * CW + j * 16 + r16] =
+          ct[(wm * RUN + ii * 16 + kg * 4 + jj) * CT_LD + wn * CW + j * 16 + r16] =
               acc[q * QI + ii][j][jj];
     __syncthreads();
-    const TiledSlice sl{ct, m0 + q * RUN, RUN, RW, A.M, n0, N, part, split};
+    const TiledSlice sl{ct, CT_LD, m0 + q * RUN, RUN, RW, A.M, n0, N, BN, part, split, tn};
     epi.store(sl, ext, t, NT);
     __syncthreads();
   }
 }
 
-constexpr size_t kTiledLds = 2 * 2 * kTBM * kTBK * sizeof(uint16_t);   // 128 KB
-
 // ------------------------------------------------------------- epilogues
+// Each epilogue maps W rows (wrows) and stores one slice (store); store is
+// called by every thread of the workgroup and may use __syncthreads.
 
-// out[split][m][n] (float32 partial sums) over W rows 0..N-1; N % 4 == 0.
+// One W matrix [N, K] (row n at W + n K).
+__device__ __forceinline__ WRows wrows_single(const uint16_t* W, int K, int n, int N) {
+  return WRows{W + static_cast<int64_t>(min(n, N)) * K, max(N - n, 0)};
+}
+
+// Coalesced fp32 store of a slice: out[row][n0 + c], 4 columns per thread.
+__device__ __forceinline__ void store_slice_f32(const TiledSlice& s, float* out, int64_t ldo,
+                                                int t, int nt) {
+  const int tpr = s.bn / 4;   // threads per row
+  const int c4 = (t % tpr) * 4;
+  if (s.n0 + c4 >= s.N) return;
+  for (int lr = t / tpr; lr < 64; lr += nt / tpr) {
+    const int m = s.row(lr);
+    if (m >= s.M) continue;
+    const float4 v = *reinterpret_cast<const float4*>(s.c + lr * s.ld + c4);
+    *reinterpret_cast<float4*>(out + static_cast<int64_t>(m) * ldo + s.n0 + c4) = v;
+  }
+}
+
+// out[split][m][n] (float32 partial sums, slabs of slab_rows rows); N % 4 == 0.
 struct TEpiStoreF32 {
   const uint16_t* W;
   int K;
   float* out;
   int64_t ldo, slab_rows;
-  __device__ const uint16_t* wbase(int) const { return W; }
+  __device__ WRows wrows(int, int n, int N) const { return wrows_single(W, K, n, N); }
   __device__ void store(const TiledSlice& s, void*, int t, int nt) const {
-    const int c4 = (t & 63) * 4;
-    if (s.n0 + c4 >= s.N) return;
-    for (int lr = t >> 6; lr < 64; lr += nt >> 6) {
+    store_slice_f32(s, out + s.split * slab_rows * ldo, ldo, t, nt);
+  }
+};
+
+// The rows of q, k and v stacked ([qd | kvd | kvd]): the QKV projection of a
+// batch of blocks as fp32 partial slabs out[split][m][qd + 2 kvd].
+struct TEpiQKVParts {
+  const uint16_t* wq;
+  const uint16_t* wk;
+  const uint16_t* wv;
+  int K, qd, kvd;
+  float* out;
+  int64_t ldo, slab_rows;
+  __device__ WRows wrows(int, int n, int) const {
+    if (n < qd) return wrows_single(wq, K, n, qd);
+    if (n < qd + kvd) return wrows_single(wk, K, n - qd, kvd);
+    return wrows_single(wv, K, n - qd - kvd, kvd);
+  }
+  __device__ void store(const TiledSlice& s, void*, int t, int nt) const {
+    store_slice_f32(s, out + s.split * slab_rows * ldo, ldo, t, nt);
+  }
+};
+
+// SwiGLU of a batch of blocks: the columns [0, bn/2) of tile tn are gate rows
+// tn*bn/2 .. +bn/2, the columns [bn/2, bn) the up rows with the same indices;
+// the epilogue writes h[m][tn*bn/2 + c] = silu(g) * u in bf16.
+struct TEpiSwiGLUPair {
+  const uint16_t* wg;
+  const uint16_t* wu;
+  int K, F, bn;
+  uint16_t* h;
+  int64_t ldh;
+  __device__ WRows wrows(int, int n, int) const {
+    const int half = bn / 2, tn = n / bn, r = n % bn;
+    const int f = tn * half + (r < half ? r : r - half);
+    return wrows_single(r < half ? wg : wu, K, f, F);
+  }
+  __device__ void store(const TiledSlice& s, void*, int t, int nt) const {
+    const int half = s.bn / 2, f0 = s.tile_n * half;
+    const int c = t % half;
+    if (f0 + c >= F) return;
+    for (int lr = t / half; lr < 64; lr += nt / half) {
       const int m = s.row(lr);
       if (m >= s.M) continue;
-      const float4 v = *reinterpret_cast<const float4*>(s.c + lr * kCtStride + c4);
-      *reinterpret_cast<float4*>(out + (s.split * slab_rows + m) * ldo + s.n0 + c4) = v;
+      const float g = s.at(lr, c), u = s.at(lr, c + half);
+      stf(h + static_cast<int64_t>(m) * ldh + f0 + c, g / (1.0f + expf(-g)) * u);
+    }
+  }
+};
+
+// LM head of a batch of blocks: per row, the largest logit among the tile's
+// columns and its lowest column index -> part[m][tile] (value, index bits),
+// reduced over tiles by the finalize kernel; optionally every logit.
+struct TEpiArgmax {
+  const uint16_t* W;
+  int K, V, n_parts;
+  float2* part;
+  float* dbg;   // [M][V] or null
+  __device__ WRows wrows(int, int n, int) const { return wrows_single(W, K, n, V); }
+  __device__ void store(const TiledSlice& s, void*, int t, int nt) const {
+    const int lane = t & 63, wave = t >> 6, nw = nt >> 6;
+    for (int lr = wave; lr < 64; lr += nw) {   // one wave per row
+      const int m = s.row(lr);
+      if (m >= s.M) continue;
+      float best = -INFINITY;
+      int bi = 0x7fffffff;
+      for (int c = lane; c < s.bn; c += 64) {
+        const int n = s.n0 + c;
+        if (n >= V) break;
+        const float v = s.at(lr, c);
+        if (dbg) dbg[static_cast<int64_t>(m) * V + n] = v;
+        if (v > best) { best = v; bi = n; }   // columns grow: ">" keeps the lowest
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(best, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (better(ov, oi, best, bi)) { best = ov; bi = oi; }
+      }
+      if (lane == 0)
+        part[static_cast<int64_t>(m) * n_parts + s.tile_n] = make_float2(best, __int_as_float(bi));
     }
   }
 };
@@ -221,7 +342,7 @@ struct TEpiStoreF32 {
 // KV injection over rows of context features.  Part p = 2 * layer + (0: K,
 // 1: V); its N = Hkv * d columns are that layer's k (or v) projection.  K
 // gets RoPE at the row's position (the pair partner of column c is c + d/2);
-// V is stored transposed.  A tile's 256 columns hold whole heads.
+// V is stored transposed.  A tile's columns hold whole heads (bn % d == 0).
 struct TEpiInject {
   const uint16_t* wk[kMaxLayers];
   const uint16_t* wv[kMaxLayers];
@@ -231,8 +352,8 @@ struct TEpiInject {
   int64_t cap;
   RopeFreq freq;
   SeqTable seq;
-  __device__ const uint16_t* wbase(int part) const {
-    return (part & 1) ? wv[part >> 1] : wk[part >> 1];
+  __device__ WRows wrows(int part, int n, int N) const {
+    return wrows_single((part & 1) ? wv[part >> 1] : wk[part >> 1], K, n, N);
   }
   __device__ void store(const TiledSlice& s, void* ext, int t, int nt) const {
     // per local row: position and cache row (rows are grouped by sequence)
@@ -253,14 +374,14 @@ struct TEpiInject {
     __syncthreads();
     if ((s.part & 1) == 0) {
       uint16_t* kd = kc[s.part >> 1];
-      const int half = d / 2;
-      const int q = t & 127;                    // RoPE pair of the tile
+      const int half = d / 2, pairs = s.bn / 2;
+      const int q = t % pairs;                  // RoPE pair of the tile
       const int hl = q / half, c = q % half;    // head inside the tile, pair index
       const int col = hl * d + c;
       const int head = (s.n0 + col) / d;
       if (s.n0 + col >= s.N) return;
       const double inv = freq.inv[c];
-      for (int lr = t >> 7; lr < 64; lr += nt >> 7) {
+      for (int lr = t / pairs; lr < 64; lr += nt / pairs) {
         if (s.row(lr) >= s.M) continue;
         float cs, sn;
         rope_cos_sin(pos_t[lr], inv, cs, sn);
@@ -274,7 +395,7 @@ struct TEpiInject {
       const int lr = t & 63;
       if (s.row(lr) >= s.M) return;
       const int64_t r = row_t[lr];
-      for (int col = t >> 6; col < kTBN && s.n0 + col < s.N; col += nt >> 6)
+      for (int col = t >> 6; col < s.bn && s.n0 + col < s.N; col += nt >> 6)
         stf(vt + static_cast<int64_t>(s.n0 + col) * cap + r, s.at(lr, col));
     }
   }

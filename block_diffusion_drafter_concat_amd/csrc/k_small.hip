@@ -230,6 +230,60 @@ __global__ __launch_bounds__(256) void lm_argmax_finalize_kernel(const float2* _
   }
 }
 
+// ------------------------------------------------------------ QKV finish
+// Block row m = b * B + j of a batch whose QKV projection left ks fp32
+// partial slabs [ks][M][qd + 2 kvd]: sum the slabs, rotate q and k at the
+// block position len[b] + j (pairs (c, c + d/2) of a head), store q to its
+// buffer and k, v to the layer's cache at row off[b] + len[b] + j (V
+// transposed).  One workgroup per row.
+template <typename T>
+__global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict__ part, int ks,
+                                                         int64_t slab, int qd, int kvd, int d,
+                                                         int B, T* __restrict__ q, int64_t ldq,
+                                                         T* __restrict__ kc, T* __restrict__ vc,
+                                                         int64_t cap, RopeFreq freq, SeqTable seq) {
+  const int m = blockIdx.x, b = m / B, j = m % B;
+  const int pos = seq.len[b] + j;
+  const int64_t row = seq.off[b] + pos;
+  const int nq = qd + 2 * kvd, half = d / 2;
+  const float* pr = part + static_cast<int64_t>(m) * nq;
+  for (int p = threadIdx.x; p < (qd + kvd) / 2; p += 256) {
+    const int c = p % half, col = (p / half) * d + c;   // [q heads | k heads] columns
+    float x0 = 0.f, x1 = 0.f;
+    for (int s = 0; s < ks; ++s) {
+      x0 += pr[s * slab + col];
+      x1 += pr[s * slab + col + half];
+    }
+    float cs, sn;
+    rope_cos_sin(pos, c, freq, cs, sn);
+    T* dst = col < qd ? q + static_cast<int64_t>(m) * ldq + col
+                      : kc + (static_cast<int64_t>((col - qd) / d) * cap + row) * d + c;
+    stf(dst, x0 * cs - x1 * sn);
+    stf(dst + half, x1 * cs + x0 * sn);
+  }
+  for (int cv = threadIdx.x; cv < kvd; cv += 256) {
+    float x = 0.f;
+    for (int s = 0; s < ks; ++s) x += pr[s * slab + qd + kvd + cv];
+    stf(vc + static_cast<int64_t>(cv) * cap + row, x);
+  }
+}
+
+hipError_t launch_qkv_finish(bool bf16, const float* part, int ks, int64_t slab, int rows, int qd,
+                             int kvd, int d, int B, void* q, int64_t ldq, void* kc, void* vc,
+                             int64_t cap, const RopeFreq& freq, const SeqTable& seq,
+                             hipStream_t st) {
+  if (bf16)
+    qkv_finish_kernel<uint16_t><<<rows, 256, 0, st>>>(
+        part, ks, slab, qd, kvd, d, B, static_cast<uint16_t*>(q), ldq,
+        static_cast<uint16_t*>(kc), static_cast<uint16_t*>(vc), cap, freq, seq);
+  else
+    qkv_finish_kernel<float><<<rows, 256, 0, st>>>(part, ks, slab, qd, kvd, d, B,
+                                                   static_cast<float*>(q), ldq,
+                                                   static_cast<float*>(kc),
+                                                   static_cast<float*>(vc), cap, freq, seq);
+  return hipGetLastError();
+}
+
 hipError_t launch_lm_argmax_finalize(const float2* part, int n_wg, int rows, int B, int32_t* draft,
                                      hipStream_t st) {
   if (rows <= 0) return hipSuccess;

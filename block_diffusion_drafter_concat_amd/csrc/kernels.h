@@ -25,6 +25,14 @@ hipError_t launch_resid_rmsnorm(bool bf16, float* x, const float* part, int n_sp
                                 int64_t split_stride, const void* gain, void* out, int rows,
                                 int H, float eps, hipStream_t st);
 
+// QKV of a batch of blocks from ks fp32 partial slabs [ks][rows][qd + 2 kvd]
+// (slab = rows * (qd + 2 kvd)): sum, RoPE on q and k at the block positions,
+// q -> q[rows][ldq], k -> K cache rows, v -> transposed V cache.
+hipError_t launch_qkv_finish(bool bf16, const float* part, int ks, int64_t slab, int rows, int qd,
+                             int kvd, int d, int B, void* q, int64_t ldq, void* kc, void* vc,
+                             int64_t cap, const RopeFreq& freq, const SeqTable& seq,
+                             hipStream_t st);
+
 // Draft ids from the LM head's per-workgroup (value, index) partials [rows][n_wg].
 hipError_t launch_lm_argmax_finalize(const float2* part, int n_wg, int rows, int B, int32_t* draft,
                                      hipStream_t st);

@@ -31,10 +31,12 @@ def feats_dev(feats, dtype):
     return [dev(f, dtype) for f in feats]
 
 
-def upload_cache(cache: "L.KVCache", caches_np):
-    """Write per-sequence (K, V) [L_b, Hkv, d] into the device cache layout."""
+def upload_cache(cache: "L.KVCache", caches_np, seqs=None):
+    """Write per-sequence (K, V) [L_b, Hkv, d] into the device cache layout
+    (entry i goes to sequence seqs[i], default i)."""
     import torch
-    for b, per_layer in enumerate(caches_np):
+    for i, per_layer in enumerate(caches_np):
+        b = i if seqs is None else int(seqs[i])
         o = int(cache.offs[b])
         for l, (k, v) in enumerate(per_layer):
             n = k.shape[0]

@@ -217,6 +217,28 @@ def test_small_bf16_ragged_batch_end_to_end(torch, B):
     draft_compare(shape, res, ids, hid, z, f"small-bf16 B={B}")
 
 
+@pytest.mark.parametrize("nb,B", [(4, 16), (13, 5), (5, 16), (9, 16), (16, 16)])
+def test_small_bf16_batch_of_blocks(torch, nb, B):
+    """Batches of M = nb * B >= 64 block rows (64, 65, 80, 144, 256): the
+    layer GEMMs and the LM head run on the LDS-tiled MFMA GEMM with row tiles
+    of 64, 128 and 256, ragged M, split-K partials, and a vocabulary (5003)
+    that ends inside a tile."""
+    shape = small_bf16_shape()
+    w = configs.make_weights(shape, 51)
+    dr = L.Drafter(shape, w)
+    lens = [int(v) for v in synth.integers((nb,), 0, 400, 51, synth.STREAM_INDICES,
+                                           f"mid_lens{nb}")]
+    lens[0] = 0
+    caches = synthetic_cache(shape, 51, lens)
+    cache = L.KVCache(shape, [n + 32 for n in lens])
+    upload_cache(cache, caches)
+    anchors = configs.make_anchors(shape, 51, nb)
+    ws = dr.workspace(nb, B, 1)
+    ids, hid, z = _draft(torch, dr, shape, cache, B, anchors, ws)
+    res = O.draft_block(w, shape, caches, anchors, B)
+    draft_compare(shape, res, ids, hid, z, f"small-bf16 batch {nb} x B{B}")
+
+
 def test_draft_is_deterministic(torch):
     shape = small_bf16_shape()
     w = configs.make_weights(shape, 32)
@@ -256,6 +278,32 @@ def test_headline_shape_draft_block_full_size(torch, qwen_like):
     ids, hid, z = _draft(torch, dr, shape, cache, 16, anchors, ws)
     res = O.draft_block(w, shape, caches, anchors, 16)
     draft_compare(shape, res, ids, hid, z, "qwen3-8b-shaped ctx2048")
+
+
+def test_batch16_ragged_full_size_sampled(torch, qwen_like):
+    """Qwen3-8B-shaped drafter, batch 16, contexts 512..8192 (the ragged
+    batch workload), B = 16: M = 256 block rows on the tiled path.  Three
+    sequences take their context from the shared generator and are checked
+    against the oracle; the other thirteen get device draws (sequences never
+    exchange anything, so they only have to exist)."""
+    shape, w, dr = qwen_like
+    wl = configs.qwen3_8b_b16_ragged()
+    lens = list(wl.ctx)
+    sample = [0, 7, 15]
+    cache = L.KVCache(shape, [n + 64 for n in lens])
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3003)
+    for t in cache.k + cache.v:
+        t.copy_(torch.randn(t.shape, generator=g, device="cuda") * 1.28)
+    cache.seq_len[:] = np.asarray(lens, dtype=np.int32)
+    sub = synthetic_cache(shape, wl.wid, [lens[b] for b in sample])
+    upload_cache(cache, sub, seqs=sample)
+    anchors = configs.make_anchors(shape, wl.wid, wl.batch)
+    ws = dr.workspace(wl.batch, 16, 1)
+    ids, hid, z = _draft(torch, dr, shape, cache, 16, anchors, ws)
+    rows = np.concatenate([np.arange(b * 16, b * 16 + 16) for b in sample])
+    res = O.draft_block(w, shape, sub, anchors[sample], 16)
+    draft_compare(shape, res, ids[sample], hid[rows], z[rows], "batch-16 ragged, sampled")
 
 
 def test_headline_shape_float32_full_size(torch):
