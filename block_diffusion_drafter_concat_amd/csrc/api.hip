@@ -39,8 +39,17 @@ inline dflash_status hip_status(hipError_t e) { return e == hipSuccess ? DFLASH_
     if (e_ != hipSuccess) return DFLASH_ERR_HIP;         \
   } while (0)
 
-// Largest attention chunk count per (sequence, kv head).
-constexpr int kMaxAttnChunks = 32;
+// Attention split: chunks per (sequence, kv head) at most kMaxAttnChunks, and
+// at most kAttnSlotBudget partial slots over the whole batch (or one chunk
+// per (sequence, kv head) if the batch is larger); chunk sizes aim at about
+// kAttnTargetWgs workgroups (two per compute unit).
+constexpr int kMaxAttnChunks = 64;
+constexpr int kAttnSlotBudget = 2048;
+constexpr int kAttnTargetWgs = 512;
+int64_t attn_slots(int batch, int n_kv) {
+  const int64_t all = static_cast<int64_t>(batch) * n_kv;
+  return std::min<int64_t>(all * kMaxAttnChunks, std::max<int64_t>(kAttnSlotBudget, all));
+}
 // Rows per launch of the weight-streaming GEMM.
 constexpr int kMaxRowsPerLaunch = 128;
 // LM-head tiles (32 vocabulary rows each) walked by one workgroup.
@@ -189,7 +198,7 @@ Layout layout(const dflash_handle* h, int max_batch, int max_block, int64_t max_
   L.qkvp_off = off; off += align_up(qkvp);
   L.lm_off = off;   off += align_up(M * g.wg_lm * 8);
   const size_t qr = static_cast<size_t>((D.G * max_block + 15) / 16 * 16);
-  const size_t slots = static_cast<size_t>(max_batch) * D.Hkv * kMaxAttnChunks;
+  const size_t slots = static_cast<size_t>(attn_slots(max_batch, D.Hkv));
   L.ao_off = off;  off += align_up(slots * qr * D.d * 4);
   L.aml_off = off; off += align_up(slots * qr * 8);
   L.ver_off = off; off += align_up(verify_ws_bytes(max_batch, max_block, D.V));
@@ -477,10 +486,14 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
                       h->layers[0].attn_norm, u, eps, st));
   DF_MARK(DFLASH_SEC_EMBED, -1, true);
 
-  // attention split: chunks of >= 128 keys (one 32-key step per wave), at most
-  // kMaxAttnChunks per sequence
-  int chunk = 128;
-  while ((max_keys + chunk - 1) / chunk > kMaxAttnChunks) chunk += 128;
+  // attention split (see kAttnTargetWgs): multiples of 128 keys
+  int64_t total_keys = 0;
+  for (int b = 0; b < nb; ++b) total_keys += seq.len[b] + B;
+  const int max_c = static_cast<int>(
+      std::max<int64_t>(1, std::min<int64_t>(kMaxAttnChunks, attn_slots(nb, D.Hkv) / (nb * D.Hkv))));
+  int chunk = static_cast<int>(
+      std::max<int64_t>(128, (total_keys * D.Hkv / kAttnTargetWgs + 127) / 128 * 128));
+  while ((max_keys + chunk - 1) / chunk > max_c) chunk += 128;
   AttnArgs aa{};
   aa.q = qb;
   aa.ldq = D.qd;

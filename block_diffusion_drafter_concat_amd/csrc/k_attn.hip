@@ -33,10 +33,10 @@ template <typename T>
 __device__ __forceinline__ void pack8(Frag8<T>& f, const float* x);
 template <>
 __device__ __forceinline__ void pack8(Frag8<uint16_t>& f, const float* x) {
-  f.v.x = static_cast<uint32_t>(f32_to_bf16(x[0])) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
-  f.v.y = static_cast<uint32_t>(f32_to_bf16(x[2])) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16);
-  f.v.z = static_cast<uint32_t>(f32_to_bf16(x[4])) | (static_cast<uint32_t>(f32_to_bf16(x[5])) << 16);
-  f.v.w = static_cast<uint32_t>(f32_to_bf16(x[6])) | (static_cast<uint32_t>(f32_to_bf16(x[7])) << 16);
+  f.v.x = f32x2_to_bf16x2(x[0], x[1]);
+  f.v.y = f32x2_to_bf16x2(x[2], x[3]);
+  f.v.z = f32x2_to_bf16x2(x[4], x[5]);
+  f.v.w = f32x2_to_bf16x2(x[6], x[7]);
 }
 template <>
 __device__ __forceinline__ void pack8(Frag8<float>& f, const float* x) {
@@ -205,6 +205,246 @@ __global__ __launch_bounds__(NQ * 64) void block_attn_kernel(AttnArgs p) {
   if (kg == 0) p.part_ml[slot * QR + r] = make_float2(m_run, l);
 }
 
+// bf16 variant with the K/V stream staged through LDS.  The workgroup's
+// threads load each 32-key step once (K rows and V^T rows, 16-byte chunks)
+// P steps ahead into registers, write it into one of two LDS slots, and the
+// waves read their MFMA fragments from there.  P steps of 16 KB (head dim
+// 128) per workgroup are in flight at once.  The loads go to registers and
+// the slot is published with an explicit LDS wait and a plain s_barrier: the
+// compiler's waits on the loads stay exact (a workgroup fence here would
+// also drain every prefetch in flight).
+//
+// LDS slot: K [32 keys][D] with 16-byte chunk c of key k at c ^ kswz(k), and
+// V^T [D][32 keys] with chunk c of row d at c ^ ((d >> 2) & 3): the 16 lanes
+// of an MFMA fragment read (16 keys or 16 d-rows at one chunk) then hit
+// distinct banks.
+template <int KCH>
+__device__ __forceinline__ int kswz(int k) {
+  return ((((k >> 3) & 3) << 2) | (k & 3)) & (KCH - 1);
+}
+
+template <int D, int NQ, int P>
+__global__ __launch_bounds__(NQ * 64) void block_attn_lds_kernel(AttnArgs p) {
+  using T = uint16_t;
+  constexpr int DS = D / 32;   // 32-wide k steps over the head dimension
+  constexpr int DT = D / 16;   // 16-row tiles of O^T
+  constexpr int QR = NQ * 16;  // query rows (padded)
+  constexpr int NT = NQ * 64;
+  constexpr int KCH = D / 8;                   // 16-byte chunks per K row
+  constexpr int SLOT_K = 32 * D;               // elements of the K part of a slot
+  constexpr int SLOT = 2 * 32 * D;             // K + V^T elements per slot
+  constexpr int CH = SLOT / 8;                 // 16-byte chunks per step
+  constexpr int PER = (CH + NT - 1) / NT;      // chunks per thread per step
+  __shared__ __align__(16) T lds[2 * SLOT];
+
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int t = threadIdx.x, qt = t >> 6, lane = t & 63;
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int B = p.B, G = p.G, GB = G * B;
+  const int n_keys = p.seq.len[b] + B;
+  const int kbeg = c * p.chunk;
+  if (kbeg >= n_keys) return;
+  const int kend = min(kbeg + p.chunk, n_keys);
+  const int n_steps = (kend - kbeg + 31) / 32;
+  const int n_chunks_b = (n_keys + p.chunk - 1) / p.chunk;
+  const int64_t base = p.seq.off[b];
+  const T* Kg = static_cast<const T*>(p.kc) + static_cast<int64_t>(g) * p.cap * D;
+  const T* Vg = static_cast<const T*>(p.vc) + static_cast<int64_t>(g) * D * p.cap;
+  const int r = qt * 16 + r16;   // this lane's query row (MFMA column)
+
+  Frag8<T> qf[DS];
+  if (r < GB) {
+    const int h = r / B, j = r % B;
+    const T* qrow = static_cast<const T*>(p.q) + static_cast<int64_t>(b * B + j) * p.ldq +
+                    (g * G + h) * D + kg * 8;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) ld_frag(qf[ds], qrow + ds * 32);
+  } else {
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) zero_frag(qf[ds]);
+  }
+
+  // chunk i of a step: K (key i / KCH, chunk i % KCH) for i < 32 KCH, else
+  // V^T (row d = j / 4, keys (j % 4) * 8 .. +8) with j = i - 32 KCH.  K rows
+  // past the sequence's keys are clamped (their scores are masked); V^T reads
+  // stay inside the sequence's slab (capacities are multiples of 32).
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  struct StepRegs {
+    u32x4 v[PER];
+  };
+  static_assert(P == 1 || P == 2 || P == 4, "prefetch depth");
+  StepRegs R0, R1, R2, R3;   // step s lives in R(s % P) (named: no stack array)
+  // Every thread issues the same PER loads at every refill (chunk indices past
+  // the step are clamped, and so is the step), so the compiler's count of
+  // loads in flight is the same on every path and its waits stay exact.
+  auto gload = [&](StepRegs& dst, int kb) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = min(t + u * NT, CH - 1);
+      const T* src;
+      if (i < 32 * KCH) {
+        const int key = min(kb + i / KCH, n_keys - 1);
+        src = Kg + (base + key) * D + (i % KCH) * 8;
+      } else {
+        const int jj = i - 32 * KCH;
+        src = Vg + static_cast<int64_t>(jj >> 2) * p.cap + base + kb + (jj & 3) * 8;
+      }
+      dst.v[u] = *reinterpret_cast<const u32x4*>(src);
+    }
+  };
+  // (a clamped chunk index rewrites the last chunk with the same data)
+  auto lstore = [&](const StepRegs& src, int slot) {
+    T* sl = lds + slot * SLOT;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = min(t + u * NT, CH - 1);
+      int off;
+      if (i < 32 * KCH) {
+        const int k = i / KCH, ch = i % KCH;
+        off = k * D + ((ch ^ kswz<KCH>(k)) << 3);
+      } else {
+        const int jj = i - 32 * KCH, d = jj >> 2, ch = jj & 3;
+        off = SLOT_K + d * 32 + ((ch ^ ((d >> 2) & 3)) << 3);
+      }
+      *reinterpret_cast<u32x4*>(sl + off) = src.v[u];
+    }
+  };
+
+  float m_run = -1e30f, l_run = 0.f;
+  f32x4 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = zero4();
+
+  // K fragment rows: tile t2 row rr <-> key (rr/4)*8 + t2*4 + rr%4 of the
+  // step, so the S^T C layout gives lane group kg the 8 consecutive keys
+  // kg*8 .. +8 (the V^T fragment's keys).
+  auto compute = [&](int slot, int kb) {
+    const T* sl = lds + slot * SLOT;
+    Frag8<T> kf[2][DS], vf[DT];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int k = (r16 >> 2) * 8 + t2 * 4 + (r16 & 3);
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds)
+        kf[t2][ds].v = *reinterpret_cast<const uint4*>(
+            sl + k * D + (((ds * 4 + kg) ^ kswz<KCH>(k)) << 3));
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = dt * 16 + r16;
+      vf[dt].v = *reinterpret_cast<const uint4*>(sl + SLOT_K + d * 32 +
+                                                 ((kg ^ ((d >> 2) & 3)) << 3));
+    }
+    const bool tail = kb + 32 > kend;   // uniform: the chunk's last, partial step
+    if (tail) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) mask_tail(vf[dt], kb + kg * 8, kend);
+    }
+    f32x4 s0 = zero4(), s1 = zero4();
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      s0 = mfma16(s0, kf[0][ds], qf[ds]);
+      s1 = mfma16(s1, kf[1][ds], qf[ds]);
+    }
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (e < 4 ? s0[e] : s1[e - 4]) * p.scale_log2;
+    if (tail) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (kb + kg * 8 + e >= kend) x[e] = -INFINITY;
+    }
+    float mx = m_run;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, x[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // exponents are <= 0 (2^x of -inf is 0); the hardware 2^x is used as is
+    float ls = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[e] = __builtin_amdgcn_exp2f(x[e] - mx);
+      ls += x[e];
+    }
+    // rescale only when some query's running max moved (else alpha == 1)
+    if (__any(mx != m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mx);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] = o[dt] * alpha;
+    }
+    m_run = mx;
+    l_run += ls;
+    // P = hi + lo in bf16 (see pack8)
+    Frag8<T> pf, pl;
+    pack8(pf, x);
+    const uint32_t hw[4] = {pf.v.x, pf.v.y, pf.v.z, pf.v.w};
+    float lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      lo[e] = x[e] - __uint_as_float((e & 1) ? (hw[e >> 1] & 0xffff0000u) : (hw[e >> 1] << 16));
+    pack8(pl, lo);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      o[dt] = mfma16(o[dt], vf[dt], pf);
+      o[dt] = mfma16(o[dt], vf[dt], pl);
+    }
+  };
+
+  auto step_kb = [&](int s) { return kbeg + 32 * min(s, n_steps - 1); };
+  gload(R0, step_kb(0));
+  if constexpr (P > 1) gload(R1, step_kb(1));
+  if constexpr (P > 2) {
+    gload(R2, step_kb(2));
+    gload(R3, step_kb(3));
+  }
+  // one step: publish its slot, refill its registers P steps ahead, compute
+  auto one = [&](StepRegs& rq, int s) {
+    const int kb = kbeg + 32 * s;
+    lstore(rq, s & 1);
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this thread's slot writes
+    __builtin_amdgcn_s_barrier();          // slot s & 1 complete; slot (s+1) & 1 free
+    gload(rq, step_kb(s + P));
+    compute(s & 1, kb);
+  };
+
+  // whole groups of P steps (no branch between the refills, so the waits on
+  // each step's registers leave the later steps' loads in flight), then the
+  // last n_steps % P steps
+  int s0 = 0;
+  for (; s0 + P <= n_steps; s0 += P) {
+    one(R0, s0);
+    if constexpr (P > 1) one(R1, s0 + 1);
+    if constexpr (P > 2) {
+      one(R2, s0 + 2);
+      one(R3, s0 + 3);
+    }
+  }
+  if (s0 < n_steps) one(R0, s0);
+  if constexpr (P > 1) if (s0 + 1 < n_steps) one(R1, s0 + 1);
+  if constexpr (P > 2) if (s0 + 2 < n_steps) one(R2, s0 + 2);
+
+  float l = l_run;
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (n_chunks_b == 1) {
+    if (r < GB) {
+      const float inv = 1.0f / l;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const float v[4] = {o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv};
+        store_out4<T>(p, b, g, r, dt * 16 + kg * 4, v);
+      }
+    }
+    return;
+  }
+  const int64_t slot = (static_cast<int64_t>(b) * p.n_kv + g) * p.max_chunks + c;
+  float4* po = reinterpret_cast<float4*>(p.part_o) + (slot * NQ + qt) * DT * 64 + lane;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) po[dt * 64] = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+  if (kg == 0) p.part_ml[slot * QR + r] = make_float2(m_run, l);
+}
+
 // One thread per (query tile, 16-row d tile, lane) of a (kv head, sequence):
 // o = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c over the sequence's chunks,
 // in chunk order, all loads of 8 chunks issued before they are combined.
@@ -260,9 +500,20 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p) {
   store_out4<T>(p, b, g, r, dt * 16 + (lane >> 4) * 4, out);
 }
 
+// 32-key steps in flight per workgroup (bf16): at most 16 staged 16-byte
+// chunks per thread (64 VGPRs), so narrower workgroups prefetch fewer steps.
+template <int D, int NQ>
+constexpr int attn_prefetch() {
+  constexpr int per = (2 * 32 * D / 8 + NQ * 64 - 1) / (NQ * 64);
+  return 16 / per < 1 ? 1 : (16 / per > 4 ? 4 : 16 / per);
+}
+
 template <typename T, int D, int NQ>
 static hipError_t launch_attn_nq(const AttnArgs& a, dim3 grid, int batch, hipStream_t st) {
-  block_attn_kernel<T, D, NQ><<<grid, NQ * 64, 0, st>>>(a);
+  if constexpr (sizeof(T) == 2)
+    block_attn_lds_kernel<D, NQ, attn_prefetch<D, NQ>()><<<grid, NQ * 64, 0, st>>>(a);
+  else
+    block_attn_kernel<T, D, NQ><<<grid, NQ * 64, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_chunks <= 1) return e;
   dim3 mgrid((NQ * (D / 16) * 64 + 255) / 256, a.n_kv, batch);
