@@ -1,22 +1,9 @@
-// Small memory-bound kernels of the drafter pass: block embedding, RMSNorm,
-// RoPE tables and greedy verification.
+// Small memory-bound kernels of the drafter pass: block embedding, residual
+// RMSNorm, the QKV finish of batched blocks, LM-head argmax finalize and
+// greedy verification.
 #include "kernels.h"
 
 namespace dflash {
-
-// ------------------------------------------------------------------ zero
-__global__ __launch_bounds__(256) void zero_kernel(int* __restrict__ p, int64_t n) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
-       i += static_cast<int64_t>(gridDim.x) * 256)
-    p[i] = 0;
-}
-
-hipError_t launch_zero(int* p, int64_t n, hipStream_t st) {
-  if (n <= 0) return hipSuccess;
-  const int64_t g = (n + 255) / 256;
-  zero_kernel<<<static_cast<int>(g < 1024 ? g : 1024), 256, 0, st>>>(p, n);
-  return hipGetLastError();
-}
 
 // ------------------------------------------------------------------ embed
 // One workgroup per block slot m = b*B + j.  Slot 0 of a block holds the anchor

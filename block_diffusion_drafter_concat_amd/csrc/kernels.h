@@ -10,9 +10,6 @@
 namespace dflash {
 
 // ---------------------------------------------------------------- small kernels
-// Clear n 32-bit words (a fill kernel, so the call stays graph-capturable).
-hipError_t launch_zero(int* p, int64_t n, hipStream_t st);
-
 // Block inputs: x[m] = embed[token(m)] (fp32) and u[m] = RMSNorm(x[m]) * gain
 // (layer 0's attention norm), one workgroup per block slot.
 hipError_t launch_embed(bool bf16, const void* embed, int H, int V, const int32_t* anchors,

@@ -205,7 +205,7 @@ size_t dflash_verify_workspace_size(int32_t batch, int32_t block_size, int32_t v
 typedef enum {
   DFLASH_SEC_FUSE_GEMM = 1,   /* dflash_fuse_context: the fusion GEMM launches */
   DFLASH_SEC_FUSE_NORM = 2,   /* dflash_fuse_context: the RMSNorm launch */
-  DFLASH_SEC_INJECT = 3,      /* dflash_inject_kv: RoPE table and injection GEMM launches */
+  DFLASH_SEC_INJECT = 3,      /* dflash_inject_kv: the injection GEMM (RoPE in its epilogue) */
   DFLASH_SEC_EMBED = 4,       /* dflash_draft_block: block embedding */
   DFLASH_SEC_ATTN_NORM = 5,   /* per layer: attention RMSNorm */
   DFLASH_SEC_QKV = 6,         /* per layer: QKV projection (+RoPE, cache write) */
