@@ -24,20 +24,50 @@
 //     pairs (c, c + d/2) of a head are both at hand).
 #pragma once
 
+#include <utility>
+
 #include "device_common.h"
 #include "gemm_skinny.h"
 
 namespace dflash {
 
-constexpr int kTBK = 64;
+constexpr int kTBK = 32;             // k per stage
+constexpr int kTStages = 4;          // LDS ring: 3 stages in flight + the one read
 constexpr int kTiledEpiLds = 1024;   // epilogue's own LDS after the C slice
 
-// Row r, 16-byte chunk c (of 8 per 64-element row) of an LDS operand tile.
-__device__ __forceinline__ int swz(int r, int c) { return r * 64 + ((c ^ (r & 7)) << 3); }
+// Row r, 16-byte chunk c (of 4 per 32-element row) of an LDS operand tile, in
+// elements: chunk c sits at c ^ ((r >> 2) & 3), so the 16 rows of an MFMA
+// fragment read (one chunk each) cover all 64 banks.
+__device__ __forceinline__ int swz(int r, int c) { return r * 32 + ((c ^ ((r >> 2) & 3)) << 3); }
 
-// Dynamic LDS of one launch: two stages of both operand tiles.
+// Dynamic LDS of one launch: the stage ring of both operand tiles.
 constexpr size_t tiled_lds_bytes(int BM, int BN) {
-  return static_cast<size_t>(2) * (BM + BN) * kTBK * sizeof(uint16_t);
+  return static_cast<size_t>(kTStages) * (BM + BN) * kTBK * sizeof(uint16_t);
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// LDS fragment read issued as an instruction the compiler does not track:
+// the LDS-destination loads of later stages are then never waited for here
+// (the compiler would otherwise drain them before every LDS read).  The
+// caller waits for the result explicitly (tile_lgkm_wait).
+template <int OFF>
+__device__ __forceinline__ u32x4_t tile_ds_read(uint32_t addr) {
+  u32x4_t v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+  return v;
+}
+// Fragment reads at 1 KB strides from one address (fragment i at i KB).
+template <int... I>
+__device__ __forceinline__ void tile_read_frags(u32x4_t* dst, uint32_t addr,
+                                                std::integer_sequence<int, I...>) {
+  ((dst[I] = tile_ds_read<I * 1024>(addr)), ...);
+}
+// An empty asm that claims to modify x: no use of x can move above it.
+__device__ __forceinline__ void tile_tie(u32x4_t& x) { asm volatile("" : "+v"(x)); }
+template <int... I>
+__device__ __forceinline__ void tile_tie_all(u32x4_t* r, std::integer_sequence<int, I...>) {
+  (tile_tie(r[I]), ...);
 }
 
 // One 64-row slice of a finished tile in LDS, as the epilogue sees it.  Local
@@ -73,10 +103,8 @@ __global__ __launch_bounds__(WM * WN * 64) void tiled_gemm_kernel(AOperand<uint1
   constexpr int NWAVES = WM * WN, NT = NWAVES * 64;
   constexpr int RW = BM / WM, CW = BN / WN;   // wave tile
   constexpr int MI = RW / 16, NJ = CW / 16;
-  constexpr int LA = BM / 8 / NWAVES, LW = BN / 8 / NWAVES;   // load instructions per wave
   constexpr int NSL = BM / 64, RUN = RW / NSL, QI = RUN / 16;  // epilogue slices
   constexpr int CT_LD = BN + 4;               // padded fp32 row stride of a C slice
-  static_assert(LA * 8 * NWAVES == BM && LW * 8 * NWAVES == BN, "whole load instructions");
   static_assert(BM % 64 == 0 && RUN % 16 == 0 && RUN * WM == 64, "64-row slices");
   static_assert(64 * CT_LD * 4 + kTiledEpiLds <= tiled_lds_bytes(BM, BN), "slice fits in LDS");
 
@@ -109,39 +137,48 @@ __global__ __launch_bounds__(WM * WN * 64) void tiled_gemm_kernel(AOperand<uint1
   const int kbeg = split * kper;
 
   // ---- global -> LDS without registers (buffer_load ... lds).  One wave
-  // instruction fills 1 KB of LDS: 8 tile rows of 8 16-byte chunks, lane l
-  // landing at chunk l of the run.  Lane l takes row l / 8 of the run and,
-  // so that the XOR swizzle holds, global chunk (l % 8) ^ (l / 8).  Each
+  // instruction fills 1 KB of LDS: 16 tile rows of 4 16-byte chunks, lane l
+  // landing at chunk l of the run.  Lane l takes row l / 4 of the run and,
+  // so that the swizzle holds, global chunk (l % 4) ^ ((l / 16) & 3).  Each
   // instruction has its own buffer resource starting at its first row and
   // covering its rows that exist; the range check covers the VGPR (row,
   // chunk) and SGPR (k) offsets together, so rows past M (or past a W
   // matrix's end) read as zero.
-  const int lrow = lane >> 3;
-  const int gchunk = (lane & 7) ^ (lane >> 3);
+  constexpr int LA = BM / 16 / NWAVES, LW = BN / 16 / NWAVES;   // loads per wave per stage
+  static_assert(LA * 16 * NWAVES == BM && LW * 16 * NWAVES == BN, "whole load instructions");
+  constexpr int STAGE = (BM + BN) * kTBK;   // elements of one ring slot
+  const int lrow = lane >> 2;
+  const int gchunk = (lane & 3) ^ ((lane >> 4) & 3);
   const uint32_t a_voff = static_cast<uint32_t>(lrow * A.lda * 2 + gchunk * 16);
   const uint32_t w_voff = static_cast<uint32_t>(lrow * K * 2 + gchunk * 16);
-  // bytes of rows [0, valid) of an 8-row run (valid <= 8)
+  // bytes of rows [0, valid) of a 16-row run (valid <= 16)
   auto run_bytes = [](int valid, int ld) -> uint64_t {
-    valid = valid < 8 ? valid : 8;
+    valid = valid < 16 ? valid : 16;
     return valid > 0 ? static_cast<uint64_t>(valid) * ld * 2 : 0;
   };
-  const int a_row0 = m0 + 8 * LA * wave;   // rows of A this wave loads
+  const int a_row0 = m0 + 16 * LA * wave;   // rows of A this wave loads
   const uint16_t* wptr[LW];   // first W row of each load instruction
   uint64_t wbytes[LW];
 #pragma unroll
   for (int i = 0; i < LW; ++i) {
-    const WRows wr = epi.wrows(part, n0 + 8 * (wave * LW + i), N);
+    const WRows wr = epi.wrows(part, n0 + 16 * (wave * LW + i), N);
     wptr[i] = wr.p;
     wbytes[i] = run_bytes(wr.valid, K);
   }
-  auto issue = [&](int k0, int buf) {
+  const int n_stages = kper / kTBK;
+  // stage st -> ring slot st % kTStages; stages past the last re-load the last
+  // one (never read), so every step issues the same loads
+  auto issue = [&](int st) {
+    st = min(st, n_stages - 1);
+    const int k0 = kbeg + st * kTBK;
     const int s = k0 / A.slab_k;
     const int col = k0 - s * A.slab_k;
-    lds_u16* la = (lds_u16*)(lds) + buf * ((BM + BN) * kTBK) + wave * (LA * 512);
-    lds_u16* lw = (lds_u16*)(lds) + buf * ((BM + BN) * kTBK) + BM * kTBK + wave * (LW * 512);
+    lds_u16* slot = (lds_u16*)(lds) + (st % kTStages) * STAGE;
+    lds_u16* la = slot + wave * (LA * 512);
+    lds_u16* lw = slot + BM * kTBK + wave * (LW * 512);
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
-      const int r0 = a_row0 + 8 * i;
+      const int r0 = a_row0 + 16 * i;
       const __amdgpu_buffer_rsrc_t ars = tile_rsrc(
           A.slab[s] + static_cast<int64_t>(min(r0, A.M)) * A.lda, run_bytes(A.M - r0, A.lda));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, la + i * 512, 16, a_voff, col * 2, 0, 0);
@@ -161,44 +198,79 @@ __global__ __launch_bounds__(WM * WN * 64) void tiled_gemm_kernel(AOperand<uint1
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = zero4();
 
-  // One stage: read this wave's fragments of both k halves, then (when there
-  // is a next stage) start its loads into the other buffer -- after the reads
-  // in program order, so no LDS read waits on them -- then the MFMAs.  The
-  // other buffer was last read in the previous stage, which every thread
-  // finished before the previous barrier.
-  auto stage = [&](int buf, bool next, int k_next) {
-    const uint16_t* la = lds + buf * ((BM + BN) * kTBK);
-    const uint16_t* lw = la + BM * kTBK;
-    Frag8<uint16_t> af[2][MI], bf[2][NJ];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-        af[kk][i].v =
-            *reinterpret_cast<const uint4*>(la + swz(wm * RW + i * 16 + r16, kk * 4 + kg));
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        bf[kk][j].v =
-            *reinterpret_cast<const uint4*>(lw + swz(wn * CW + j * 16 + r16, kk * 4 + kg));
-    }
-    if (next) issue(k_next, buf ^ 1);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16(acc[i][j], af[kk][i], bf[kk][j]);
-    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's next-stage loads
-    __syncthreads();
+  // Fragments of one stage: A rows wm*RW + i*16 + r16, W rows wn*CW + j*16 +
+  // r16, chunk kg.  Fragment i sits 1 KB after fragment i - 1 (16 rows of
+  // 64 bytes; the swizzle depends on r16 only), so each operand needs one
+  // address and immediate offsets.
+  struct Frags {
+    u32x4_t a[MI], b[NJ];
   };
+  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u16*)(lds)));
+  const uint32_t fa_off = lds_base + 2 * swz(wm * RW + r16, kg);
+  const uint32_t fb_off = lds_base + 2 * (BM * kTBK + swz(wn * CW + r16, kg));
+  auto read_frags = [&](Frags& f, int st) {
+    const uint32_t sb = static_cast<uint32_t>((min(st, n_stages - 1) % kTStages) * STAGE * 2);
+    const uint32_t aa = fa_off + sb, ba = fb_off + sb;
+    tile_read_frags(f.a, aa, std::make_integer_sequence<int, MI>{});
+    tile_read_frags(f.b, ba, std::make_integer_sequence<int, NJ>{});
+  };
+  // wait for this wave's fragment reads; the fragments are operands, so no
+  // use of them can be placed before the wait
+  auto lgkm_wait = [&](Frags& f) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    tile_tie_all(f.a, std::make_integer_sequence<int, MI>{});
+    tile_tie_all(f.b, std::make_integer_sequence<int, NJ>{});
+  };
+  auto mfmas = [&](const Frags& f) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        Frag8<uint16_t> fa, fb;
+        fa.v = __builtin_bit_cast(uint4, f.a[i]);
+        fb.v = __builtin_bit_cast(uint4, f.b[j]);
+        acc[i][j] = mfma16(acc[i][j], fa, fb);
+      }
+  };
+  // vmcnt(n) for n < 64 (lgkmcnt and expcnt not waited)
+  constexpr int kVm = LA + LW;   // this wave's loads per stage
+  static_assert(kVm < 16, "vmcnt field");
 
-  const int n_stages = kper / kTBK;
-  issue(kbeg, 0);
-  __builtin_amdgcn_s_waitcnt(0x0f70);
+  // Pipeline.  Before step st: stages st+1, st+2 in flight, fragments of st
+  // in registers.  Step st: wait for stage st+1 (stage st+2 stays in
+  // flight), barrier (stage st+1 complete; every wave is past its reads of
+  // slot (st-1) % 4), load stage st+3 into that slot, read the fragments of
+  // st+1, run the MFMAs of st, then wait for the fragment reads -- so values
+  // that cross the loop edge are always complete.
+  issue(0);
+  issue(1);
+  issue(2);
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * kVm));   // vmcnt(2 kVm): stage 0 landed
+  __builtin_amdgcn_s_barrier();
+  Frags f0, f1;
+  read_frags(f0, 0);
+  lgkm_wait(f0);
+  int st = 0;
+  for (; st + 2 <= n_stages; st += 2) {
+    __builtin_amdgcn_s_waitcnt(0x0f70 | kVm);
+    __builtin_amdgcn_s_barrier();
+    issue(st + 3);
+    read_frags(f1, st + 1);
+    __builtin_amdgcn_sched_barrier(0);   // reads go out before the MFMAs
+    mfmas(f0);
+    lgkm_wait(f1);
+    __builtin_amdgcn_s_waitcnt(0x0f70 | kVm);
+    __builtin_amdgcn_s_barrier();
+    issue(st + 4);
+    read_frags(f0, st + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(f1);
+    lgkm_wait(f0);
+  }
+  if (st < n_stages) mfmas(f0);   // odd stage count: the last stage
+  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): no load may land in the epilogue's LDS
   __syncthreads();
-  for (int st = 0; st + 1 < n_stages; ++st) stage(st & 1, true, kbeg + (st + 1) * kTBK);
-  stage((n_stages - 1) & 1, false, 0);
 
   // ---- epilogue: NSL slices of 64 rows.  Slice q takes MFMA rows
   // i in [q QI, (q+1) QI) of every wave: local row lr = wm * RUN +
