@@ -32,8 +32,14 @@
 namespace dflash {
 
 constexpr int kTBK = 32;             // k per stage
-constexpr int kTStages = 4;          // LDS ring: 3 stages in flight + the one read
 constexpr int kTiledEpiLds = 1024;   // epilogue's own LDS after the C slice
+constexpr int kLdsMax = 160 * 1024;  // LDS of one gfx950 workgroup
+
+// LDS ring slots: 5 when they fit in the workgroup's LDS (3 stages in
+// flight ahead of the one being read), else 4.
+constexpr int tiled_stages(int BM, int BN) {
+  return 5 * (BM + BN) * kTBK * 2 <= kLdsMax ? 5 : 4;
+}
 
 // Row r, 16-byte chunk c (of 4 per 32-element row) of an LDS operand tile, in
 // elements: chunk c sits at c ^ ((r >> 2) & 3), so the 16 rows of an MFMA
@@ -42,10 +48,14 @@ __device__ __forceinline__ int swz(int r, int c) { return r * 32 + ((c ^ ((r >> 
 
 // Dynamic LDS of one launch: the stage ring of both operand tiles.
 constexpr size_t tiled_lds_bytes(int BM, int BN) {
-  return static_cast<size_t>(kTStages) * (BM + BN) * kTBK * sizeof(uint16_t);
+  return static_cast<size_t>(tiled_stages(BM, BN)) * (BM + BN) * kTBK * sizeof(uint16_t);
 }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// s_waitcnt immediate that waits for vmcnt <= n (n < 64) and nothing else
+// (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0f70; }
 
 // LDS fragment read issued as an instruction the compiler does not track:
 // the LDS-destination loads of later stages are then never waited for here
@@ -147,6 +157,7 @@ __global__ __launch_bounds__(WM * WN * 64) void tiled_gemm_kernel(AOperand<uint1
   constexpr int LA = BM / 16 / NWAVES, LW = BN / 16 / NWAVES;   // loads per wave per stage
   static_assert(LA * 16 * NWAVES == BM && LW * 16 * NWAVES == BN, "whole load instructions");
   constexpr int STAGE = (BM + BN) * kTBK;   // elements of one ring slot
+  constexpr int NS = tiled_stages(BM, BN);  // ring slots; NS - 2 stages in flight
   const int lrow = lane >> 2;
   const int gchunk = (lane & 3) ^ ((lane >> 4) & 3);
   const uint32_t a_voff = static_cast<uint32_t>(lrow * A.lda * 2 + gchunk * 16);
@@ -166,29 +177,42 @@ __global__ __launch_bounds__(WM * WN * 64) void tiled_gemm_kernel(AOperand<uint1
     wbytes[i] = run_bytes(wr.valid, K);
   }
   const int n_stages = kper / kTBK;
-  // stage st -> ring slot st % kTStages; stages past the last re-load the last
-  // one (never read), so every step issues the same loads
-  auto issue = [&](int st) {
-    st = min(st, n_stages - 1);
-    const int k0 = kbeg + st * kTBK;
-    const int s = k0 / A.slab_k;
-    const int col = k0 - s * A.slab_k;
-    lds_u16* slot = (lds_u16*)(lds) + (st % kTStages) * STAGE;
+  // Loads are issued for stages 0, 1, 2, ... in order; the next stage's slab,
+  // column and ring slot advance incrementally (stages past the last re-load
+  // the last one, never read, so every step issues the same loads).  The
+  // division below runs on the vector ALU: its results are marked uniform.
+  int nx_stage = 0, nx_slot = 0, nx_k = kbeg;
+  int nx_slab = __builtin_amdgcn_readfirstlane(kbeg / A.slab_k);
+  int nx_col = __builtin_amdgcn_readfirstlane(kbeg - nx_slab * A.slab_k);
+  const uint16_t* nx_sp = A.slab[nx_slab];   // reloaded only when the slab changes
+  auto issue = [&]() {
+    const uint16_t* sp = nx_sp;
+    lds_u16* slot = (lds_u16*)(lds) + nx_slot * STAGE;
     lds_u16* la = slot + wave * (LA * 512);
     lds_u16* lw = slot + BM * kTBK + wave * (LW * 512);
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
       const int r0 = a_row0 + 16 * i;
       const __amdgpu_buffer_rsrc_t ars = tile_rsrc(
-          A.slab[s] + static_cast<int64_t>(min(r0, A.M)) * A.lda, run_bytes(A.M - r0, A.lda));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, la + i * 512, 16, a_voff, col * 2, 0, 0);
+          sp + static_cast<int64_t>(min(r0, A.M)) * A.lda, run_bytes(A.M - r0, A.lda));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, la + i * 512, 16, a_voff, nx_col * 2, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < LW; ++i) {
       // (bound to a local: a resource temporary passed straight to the builtin
       // makes the host pass drop the kernel's launch stub)
       const __amdgpu_buffer_rsrc_t wrs = tile_rsrc(wptr[i], wbytes[i]);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, lw + i * 512, 16, w_voff, k0 * 2, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, lw + i * 512, 16, w_voff, nx_k * 2, 0, 0);
+    }
+    nx_slot = nx_slot + 1 == NS ? 0 : nx_slot + 1;
+    if (++nx_stage < n_stages) {
+      nx_k += kTBK;
+      nx_col += kTBK;
+      if (nx_col == A.slab_k) {
+        nx_col = 0;
+        ++nx_slab;
+        nx_sp = A.slab[nx_slab];
+      }
     }
   };
 
@@ -208,8 +232,8 @@ __global__ __launch_bounds__(WM * WN * 64) void tiled_gemm_kernel(AOperand<uint1
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u16*)(lds)));
   const uint32_t fa_off = lds_base + 2 * swz(wm * RW + r16, kg);
   const uint32_t fb_off = lds_base + 2 * (BM * kTBK + swz(wn * CW + r16, kg));
-  auto read_frags = [&](Frags& f, int st) {
-    const uint32_t sb = static_cast<uint32_t>((min(st, n_stages - 1) % kTStages) * STAGE * 2);
+  auto read_frags = [&](Frags& f, int slot) {
+    const uint32_t sb = static_cast<uint32_t>(slot * STAGE * 2);
     const uint32_t aa = fa_off + sb, ba = fb_off + sb;
     tile_read_frags(f.a, aa, std::make_integer_sequence<int, MI>{});
     tile_read_frags(f.b, ba, std::make_integer_sequence<int, NJ>{});
@@ -235,41 +259,51 @@ __global__ __launch_bounds__(WM * WN * 64) void tiled_gemm_kernel(AOperand<uint1
   };
   // vmcnt(n) for n < 64 (lgkmcnt and expcnt not waited)
   constexpr int kVm = LA + LW;   // this wave's loads per stage
-  static_assert(kVm < 16, "vmcnt field");
+  static_assert(kVm * (tiled_stages(BM, BN) - 2) < 64, "vmcnt field");
 
-  // Pipeline.  Before step st: stages st+1, st+2 in flight, fragments of st
-  // in registers.  Step st: wait for stage st+1 (stage st+2 stays in
+  // Pipeline.  Before step st: stages st+1 .. st+NS-2 in flight, fragments
+  // of st in registers.  Step st: wait for stage st+1 (the later ones stay in
   // flight), barrier (stage st+1 complete; every wave is past its reads of
-  // slot (st-1) % 4), load stage st+3 into that slot, read the fragments of
-  // st+1, run the MFMAs of st, then wait for the fragment reads -- so values
-  // that cross the loop edge are always complete.
-  issue(0);
-  issue(1);
-  issue(2);
-  __builtin_amdgcn_s_waitcnt(0x0f70 | (2 * kVm));   // vmcnt(2 kVm): stage 0 landed
+  // slot (st-1) % NS), load stage st+NS-1 into that slot, read the fragments
+  // of st+1, run the MFMAs of st, then wait for the fragment reads -- so
+  // values that cross the loop edge are always complete.
+  constexpr int kAhead = NS - 2;                     // stages in flight after a wait
+#pragma unroll
+  for (int q = 0; q < NS - 1; ++q) issue();
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * kVm));   // stage 0 landed
   __builtin_amdgcn_s_barrier();
   Frags f0, f1;
-  read_frags(f0, 0);
+  // ring slot of the stage whose fragments are read next (stays on the last
+  // stage's slot once past it)
+  int rd_slot = 0, rd_stage = 0;
+  auto next_read = [&]() {
+    if (rd_stage + 1 < n_stages) {
+      ++rd_stage;
+      rd_slot = rd_slot + 1 == NS ? 0 : rd_slot + 1;
+    }
+    return rd_slot;
+  };
+  read_frags(f0, rd_slot);
   lgkm_wait(f0);
   int st = 0;
   for (; st + 2 <= n_stages; st += 2) {
-    __builtin_amdgcn_s_waitcnt(0x0f70 | kVm);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kAhead - 1) * kVm));
     __builtin_amdgcn_s_barrier();
-    issue(st + 3);
-    read_frags(f1, st + 1);
+    issue();
+    read_frags(f1, next_read());
     __builtin_amdgcn_sched_barrier(0);   // reads go out before the MFMAs
     mfmas(f0);
     lgkm_wait(f1);
-    __builtin_amdgcn_s_waitcnt(0x0f70 | kVm);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kAhead - 1) * kVm));
     __builtin_amdgcn_s_barrier();
-    issue(st + 4);
-    read_frags(f0, st + 2);
+    issue();
+    read_frags(f0, next_read());
     __builtin_amdgcn_sched_barrier(0);
     mfmas(f1);
     lgkm_wait(f0);
   }
   if (st < n_stages) mfmas(f0);   // odd stage count: the last stage
-  __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): no load may land in the epilogue's LDS
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // no load may land in the epilogue's LDS
   __syncthreads();
 
   // ---- epilogue: NSL slices of 64 rows.  Slice q takes MFMA rows
