@@ -215,9 +215,9 @@ __global__ __launch_bounds__(NQ * 64) void block_attn_kernel(AttnArgs p) {
 // also drain every prefetch in flight).
 //
 // LDS slot: K [32 keys][D] with 16-byte chunk c of key k at c ^ kswz(k), and
-// V^T [D][32 keys] with chunk c of row d at c ^ ((d >> 2) & 3): the 16 lanes
-// of an MFMA fragment read (16 keys or 16 d-rows at one chunk) then hit
-// distinct banks.
+// V^T [D][32 keys] with chunk c of row d at c ^ ((d >> 1) & 3): each group of
+// 8 lanes of an MFMA fragment read (8 keys or 8 d-rows at one chunk; LDS
+// serves 16-byte reads 8 lanes at a time) then hits 8 distinct bank groups.
 template <int KCH>
 __device__ __forceinline__ int kswz(int k) {
   return ((((k >> 3) & 3) << 2) | (k & 3)) & (KCH - 1);
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(NQ * 64) void block_attn_lds_kernel(AttnArgs p) {
         off = k * D + ((ch ^ kswz<KCH>(k)) << 3);
       } else {
         const int jj = i - 32 * KCH, d = jj >> 2, ch = jj & 3;
-        off = SLOT_K + d * 32 + ((ch ^ ((d >> 2) & 3)) << 3);
+        off = SLOT_K + d * 32 + ((ch ^ ((d >> 1) & 3)) << 3);
       }
       *reinterpret_cast<u32x4*>(sl + off) = src.v[u];
     }
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(NQ * 64) void block_attn_lds_kernel(AttnArgs p) {
     for (int dt = 0; dt < DT; ++dt) {
       const int d = dt * 16 + r16;
       vf[dt].v = *reinterpret_cast<const uint4*>(sl + SLOT_K + d * 32 +
-                                                 ((kg ^ ((d >> 2) & 3)) << 3));
+                                                 ((kg ^ ((d >> 1) & 3)) << 3));
     }
     const bool tail = kb + 32 > kend;   // uniform: the chunk's last, partial step
     if (tail) {
