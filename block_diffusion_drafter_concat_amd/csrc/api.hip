@@ -436,7 +436,14 @@ dflash_status inject_impl(dflash_handle* h, const void* ctx, const SeqTable& seq
     te.freq = epi.freq;
     te.seq = seq;
     const AOperand<uint16_t> At = a_single<uint16_t>(ctx, D.H, D.H, total);
-    DF_HIP(launch_tiled(At, D.kvd, D.H, 2 * D.L, 1, te, st));
+    // 256 x 256 tiles, or 256 x 128 when the former would not cover the 256
+    // compute units twice (the last partial round then weighs less)
+    const int64_t big_tiles = static_cast<int64_t>((total + kPreBM - 1) / kPreBM) *
+                              ((D.kvd + kPreBN - 1) / kPreBN) * 2 * D.L;
+    if (big_tiles < 512)
+      DF_HIP((launch_tiled_cfg<kPreBM, 128, 2, 4>(At, D.kvd, D.H, 2 * D.L, 1, te, st)));
+    else
+      DF_HIP(launch_tiled(At, D.kvd, D.H, 2 * D.L, 1, te, st));
   } else {
     DF_HIP(run_rows<T>(a_single<T>(ctx, D.H, D.H, total), D.H, g.tiles_inj, 1, 1, epi, st,
                        NoPerLaunch{}));
