@@ -360,6 +360,47 @@ def workload_27b(torch, L, configs, reps: int) -> dict:
     return out
 
 
+def draft_latency(torch, L, configs, shape, w, reps: int = 20) -> dict:
+    """Latency of one block pass (5 layers, 16 slots: 15 drafts) against an
+    autoregressive stand-in of the same width: 1 layer, 8 sequential steps,
+    each a 2-slot pass (anchor + one draft) whose draft anchors the next
+    step, the anchor's K/V row kept by advancing the committed length (the
+    autoregressive cache append).  Same kernels, same LM head; ctx 2048."""
+    one = configs.scaled(shape, n_layers=1)
+    w1 = dict(w)
+    w1["layers"] = w["layers"][:1]
+    dr5, dr1 = L.Drafter(shape, w), L.Drafter(one, w1)
+    lens = [CTX]
+    c5 = L.KVCache(shape, [CTX + 64])
+    c1 = L.KVCache(one, [CTX + 64])
+    fill_cache(torch, c5, lens, 6001)
+    fill_cache(torch, c1, lens, 6002)
+    anchor = torch.zeros(1, dtype=torch.int32, device="cuda")
+    d15 = torch.empty((1, BLOCK - 1), dtype=torch.int32, device="cuda")
+    d1 = torch.empty((1, 1), dtype=torch.int32, device="cuda")
+    ws5, ws1 = dr5.workspace(1, BLOCK, 1), dr1.workspace(1, 2, 1)
+    block_ms = event_time_ms(torch, lambda: dr5.draft_block(c5, BLOCK, anchor, d15, ws5), reps)
+    ar_steps = 8
+
+    def ar_loop():
+        c1.seq_len[0] = CTX
+        a = anchor
+        for _ in range(ar_steps):
+            dr1.draft_block(c1, 2, a, d1, ws1)
+            a = d1.view(1)
+            c1.seq_len[0] += 1
+    ar_ms = event_time_ms(torch, ar_loop, reps)
+    dr5.close()
+    dr1.close()
+    return {"block_pass": {"layers": shape.n_layers, "slots": BLOCK, "drafts": BLOCK - 1,
+                           "ms": round(block_ms, 4)},
+            "autoregressive": {"layers": 1, "steps": ar_steps, "drafts": ar_steps,
+                               "ms": round(ar_ms, 4)},
+            "block_drafts_per_ms": round((BLOCK - 1) / block_ms, 2),
+            "ar_drafts_per_ms": round(ar_steps / ar_ms, 2),
+            "ctx": CTX}
+
+
 def step_bytes(shape, n_new: int) -> dict:
     """Algorithmic HBM bytes of one step (each tensor read or written once)."""
     H, V, L = shape.hidden, shape.vocab, shape.n_layers
@@ -533,6 +574,8 @@ def main():
     # ---- the per-block launch sequence as a HIP graph, then other workloads
     graph = graph_vs_eager(torch, dr, cache, anchor, draft, ws, K)
     log(f"graph: {graph}")
+    latency = draft_latency(torch, L, configs, shape, dr.w)   # device weights, no copy
+    log(f"draft latency: {latency}")
     workloads = None
     if not args.no_workloads:
         workloads = {}
@@ -573,6 +616,7 @@ def main():
         "kernels": kernels,
         "prefill_mfma": prefill,
         "graph": graph,
+        "draft_latency": latency,
         "workloads": workloads,
         "cpu_baseline": cpu,
     }

@@ -239,6 +239,43 @@ def test_small_bf16_batch_of_blocks(torch, nb, B):
     draft_compare(shape, res, ids, hid, z, f"small-bf16 batch {nb} x B{B}")
 
 
+def test_autoregressive_stand_in_steps(torch):
+    """The autoregressive stand-in used for the draft-latency comparison: a
+    1-layer drafter run as 2-slot passes, each pass's draft anchoring the
+    next, the anchor's K/V row (written by the pass at the first free row)
+    kept by advancing the committed length.  The oracle gets the same
+    anchors and a cache extended with the anchor's layer-0 K/V, formed from
+    its own pieces (bf16 RMSNorm of the embedding row, projection, RoPE at the
+    anchor's position)."""
+    shape = configs.scaled(small_bf16_shape(), n_layers=1)
+    w = configs.make_weights(shape, 61)
+    dr = L.Drafter(shape, w)
+    n0 = 40
+    caches = synthetic_cache(shape, 61, [n0])
+    cache = L.KVCache(shape, [n0 + 32])
+    upload_cache(cache, caches)
+    ws = dr.workspace(1, 2, 1)
+    kc, vc = caches[0][0]
+    kc, vc = np.asarray(kc, np.float64), np.asarray(vc, np.float64)
+    lw = w["layers"][0]
+    anchor = configs.make_anchors(shape, 61, 1)
+    for step in range(3):
+        ids, hid, z = _draft(torch, dr, shape, cache, 2, anchor, ws)
+        res = O.draft_block(w, shape, [[(kc, vc)]], anchor, 2)
+        draft_compare(shape, res, ids, hid, z, f"autoregressive step {step}")
+        # keep the anchor's K/V: the GPU by advancing the committed length,
+        # the oracle by appending the same row
+        pos = n0 + step
+        u = O.bf16_round(O.rmsnorm(np.asarray(w["embed"], np.float64)[int(anchor[0])][None],
+                                   lw["attn_norm"], shape.rms_eps))
+        k = (u @ np.asarray(lw["wk"], np.float64).T).reshape(1, shape.n_kv_heads, shape.head_dim)
+        v = (u @ np.asarray(lw["wv"], np.float64).T).reshape(1, shape.n_kv_heads, shape.head_dim)
+        kc = np.concatenate([kc, O.bf16_round(O.rope(k, [pos], shape.rope_theta))])
+        vc = np.concatenate([vc, O.bf16_round(v)])
+        cache.seq_len[0] += 1
+        anchor = ids[:, 0].astype(np.int32)
+
+
 def test_draft_is_deterministic(torch):
     shape = small_bf16_shape()
     w = configs.make_weights(shape, 32)
