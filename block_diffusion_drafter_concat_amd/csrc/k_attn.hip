@@ -320,7 +320,7 @@ __global__ __launch_bounds__(NQ * 64) void block_attn_lds_kernel(AttnArgs p) {
   // kg*8 .. +8 (the V^T fragment's keys).
   auto compute = [&](int slot, int kb) {
     const T* sl = lds + slot * SLOT;
-    Frag8<T> kf[2][DS], vf[DT];
+    Frag8<T> kf[2][DS];
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       const int k = (r16 >> 2) * 8 + t2 * 4 + (r16 & 3);
@@ -329,17 +329,7 @@ __global__ __launch_bounds__(NQ * 64) void block_attn_lds_kernel(AttnArgs p) {
         kf[t2][ds].v = *reinterpret_cast<const uint4*>(
             sl + k * D + (((ds * 4 + kg) ^ kswz<KCH>(k)) << 3));
     }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = dt * 16 + r16;
-      vf[dt].v = *reinterpret_cast<const uint4*>(sl + SLOT_K + d * 32 +
-                                                 ((kg ^ ((d >> 1) & 3)) << 3));
-    }
     const bool tail = kb + 32 > kend;   // uniform: the chunk's last, partial step
-    if (tail) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) mask_tail(vf[dt], kb + kg * 8, kend);
-    }
     f32x4 s0 = zero4(), s1 = zero4();
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
@@ -375,6 +365,19 @@ __global__ __launch_bounds__(NQ * 64) void block_attn_lds_kernel(AttnArgs p) {
     }
     m_run = mx;
     l_run += ls;
+    // V^T fragments, read once the K fragments are dead (fewer live registers:
+    // two waves per SIMD)
+    Frag8<T> vf[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = dt * 16 + r16;
+      vf[dt].v = *reinterpret_cast<const uint4*>(sl + SLOT_K + d * 32 +
+                                                 ((kg ^ ((d >> 1) & 3)) << 3));
+    }
+    if (tail) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) mask_tail(vf[dt], kb + kg * 8, kend);
+    }
     // P = hi + lo in bf16 (see pack8)
     Frag8<T> pf, pl;
     pack8(pf, x);
@@ -500,12 +503,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p) {
   store_out4<T>(p, b, g, r, dt * 16 + (lane >> 4) * 4, out);
 }
 
-// 32-key steps in flight per workgroup (bf16): at most 16 staged 16-byte
-// chunks per thread (64 VGPRs), so narrower workgroups prefetch fewer steps.
+// 32-key steps in flight per workgroup (bf16): at most 8 staged 16-byte
+// chunks per thread (32 VGPRs), so that two waves fit on a SIMD; narrower
+// workgroups prefetch fewer steps.
 template <int D, int NQ>
 constexpr int attn_prefetch() {
   constexpr int per = (2 * 32 * D / 8 + NQ * 64 - 1) / (NQ * 64);
-  return 16 / per < 1 ? 1 : (16 / per > 4 ? 4 : 16 / per);
+  return 8 / per < 1 ? 1 : (8 / per > 4 ? 4 : 8 / per);
 }
 
 template <typename T, int D, int NQ>
