@@ -41,15 +41,60 @@ inline dflash_status hip_status(hipError_t e) { return e == hipSuccess ? DFLASH_
 
 // Attention split: chunks per (sequence, kv head) at most kMaxAttnChunks, and
 // at most kAttnSlotBudget partial slots over the whole batch (or one chunk
-// per (sequence, kv head) if the batch is larger); chunk sizes aim at about
-// kAttnTargetWgs workgroups (two per compute unit).
-constexpr int kMaxAttnChunks = 64;
+// per (sequence, kv head) if the batch is larger).  The bf16 block-attention
+// kernel fits two workgroups on a compute unit, so kAttnConcurrent (2 x 256
+// CUs) of them run at once; attn_chunk() picks the chunk length.
+constexpr int kMaxAttnChunks = 128;
 constexpr int kAttnSlotBudget = 2048;
-constexpr int kAttnTargetWgs = 512;
+constexpr int kAttnConcurrent = 512;
+constexpr int kAttnWgOverhead = 64;   // fixed cost of a workgroup, in keys
 int64_t attn_slots(int batch, int n_kv) {
   const int64_t all = static_cast<int64_t>(batch) * n_kv;
   return std::min<int64_t>(all * kMaxAttnChunks, std::max<int64_t>(kAttnSlotBudget, all));
 }
+// Keys per attention workgroup: a multiple of 128, at most max_c chunks per
+// (sequence, kv head), chosen to minimise an estimated makespan in units of
+// keys.  A workgroup costs (its keys + kAttnWgOverhead); the dispatcher hands
+// workgroups, in grid order, to the first of kAttnConcurrent free places.
+//  - Near-uniform batch (longest <= 1.25 x shortest): every workgroup is a
+//    full chunk, so the work runs in whole rounds:
+//        ceil(workgroups / kAttnConcurrent) * (chunk + overhead).
+//  - Ragged batch: one round costs the longest job; over several rounds the
+//    late workgroups fill the gaps that short ones leave, and the remaining
+//    imbalance shrinks as the workgroups grow more numerous:
+//        total / kAttnConcurrent + 0.215 * (chunk + overhead) * kAttnConcurrent / workgroups
+//    (the 0.215 fitted to the ragged batch-16 workload, contexts 512..8192).
+// Ties go to the longer chunk (fewer partials to merge).
+int attn_chunk(const int32_t* keys, int nb, int n_kv, int max_keys, int max_c) {
+  int lo = 128, min_keys = max_keys;
+  while ((max_keys + lo - 1) / lo > max_c) lo += 128;
+  for (int b = 0; b < nb; ++b) min_keys = std::min(min_keys, static_cast<int>(keys[b]));
+  const bool uniform = 4 * static_cast<int64_t>(max_keys) <= 5 * static_cast<int64_t>(min_keys);
+  const int hi = std::max(lo, (max_keys + 127) / 128 * 128);
+  int best = hi;
+  double best_cost = -1.0;
+  for (int c = hi; c >= lo; c -= 128) {
+    int64_t wgs = 0, work = 0;
+    for (int b = 0; b < nb; ++b) {
+      const int64_t n = (keys[b] + c - 1) / c;
+      wgs += n;
+      work += keys[b] + n * kAttnWgOverhead;
+    }
+    wgs *= n_kv;
+    work *= n_kv;
+    const double job = c + kAttnWgOverhead;
+    double cost;
+    if (uniform) cost = static_cast<double>((wgs + kAttnConcurrent - 1) / kAttnConcurrent) * job;
+    else if (wgs <= kAttnConcurrent) cost = job;
+    else cost = static_cast<double>(work) / kAttnConcurrent + 0.215 * job * kAttnConcurrent / wgs;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = c;
+    }
+  }
+  return best;
+}
+
 // Rows per launch of the weight-streaming GEMM.
 constexpr int kMaxRowsPerLaunch = 128;
 // LM-head tiles (32 vocabulary rows each) walked by one workgroup.
@@ -406,7 +451,6 @@ template <typename T>
 dflash_status inject_impl(dflash_handle* h, const void* ctx, const SeqTable& seq, int total,
                           dflash_kv* kv, void* ws, hipStream_t st) {
   const Dims D = dims(h->cfg);
-  const Layout L = layout(h, 1, 1, total);
   const GemmPlan g = gemm_plan(D);
   DF_MARK(DFLASH_SEC_INJECT, -1, false);
   EpiInject<T> epi{};
@@ -493,14 +537,12 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
                       h->layers[0].attn_norm, u, eps, st));
   DF_MARK(DFLASH_SEC_EMBED, -1, true);
 
-  // attention split (see kAttnTargetWgs): multiples of 128 keys
-  int64_t total_keys = 0;
-  for (int b = 0; b < nb; ++b) total_keys += seq.len[b] + B;
+  // attention split (see attn_chunk)
+  int32_t keys[DFLASH_MAX_BATCH];
+  for (int b = 0; b < nb; ++b) keys[b] = seq.len[b] + B;
   const int max_c = static_cast<int>(
       std::max<int64_t>(1, std::min<int64_t>(kMaxAttnChunks, attn_slots(nb, D.Hkv) / (nb * D.Hkv))));
-  int chunk = static_cast<int>(
-      std::max<int64_t>(128, (total_keys * D.Hkv / kAttnTargetWgs + 127) / 128 * 128));
-  while ((max_keys + chunk - 1) / chunk > max_c) chunk += 128;
+  const int chunk = attn_chunk(keys, nb, D.Hkv, max_keys, max_c);
   AttnArgs aa{};
   aa.q = qb;
   aa.ldq = D.qd;
