@@ -9,6 +9,8 @@
 #include <atomic>
 #include <new>
 
+#include <hip/hip_ext.h>
+
 #include "../../include/dflash.h"
 #include "gemm_epilogues.h"
 #include "gemm_skinny.h"
@@ -114,6 +116,7 @@ Dims dims(const dflash_config& c) {
 struct GemmPlan {
   int tiles_qkv, tiles_o, tiles_gu, tiles_d, tiles_lm, tiles_fc, tiles_inj;
   int ks_o, ks_d;      // K-splits of the O and down projections (partials -> next norm)
+  int ks_qkv;          // K-split of the bf16 QKV projection (partials -> RoPE finish)
   int wg_lm;           // LM-head workgroups
 };
 
@@ -201,6 +204,7 @@ GemmPlan gemm_plan(const Dims& D) {
   g.tiles_inj = D.L * 2 * D.kvd / 32;
   g.ks_o = pick_ksplit(g.tiles_o, D.qd);
   g.ks_d = pick_ksplit(g.tiles_d, D.F);
+  g.ks_qkv = pick_ksplit(g.tiles_qkv, D.H);
   g.wg_lm = (g.tiles_lm + kLmTilesPerWg - 1) / kLmTilesPerWg;
   return g;
 }
@@ -239,6 +243,11 @@ Layout layout(const dflash_handle* h, int max_batch, int max_block, int64_t max_
       qkvp = std::max(qkvp, static_cast<size_t>(mp.ks_qkv) * m * (D.qd + 2 * D.kvd) * 4);
     }
   }
+  if (h->cfg.dtype == DFLASH_BF16) {
+    // bf16 QKV below the mid-M path: weight-streaming split partials
+    const size_t ms = std::min(M, static_cast<size_t>(kMidMinRows - 1));
+    qkvp = std::max(qkvp, static_cast<size_t>(g.ks_qkv) * ms * (D.qd + 2 * D.kvd) * 4);
+  }
   L.part_off = off; off += align_up(part);
   L.qkvp_off = off; off += align_up(qkvp);
   L.lm_off = off;   off += align_up(M * g.wg_lm * 8);
@@ -264,6 +273,19 @@ hipError_t mark(const dflash_handle* h, int section, int layer, bool stop, hipSt
 }
 #define DF_MARK(sec, layer, stop) DF_HIP(mark(h, sec, layer, stop, st))
 
+// The caller's events for (section, layer), if that point is set.
+bool timing_events(const dflash_handle* h, int section, int layer, hipEvent_t* a, hipEvent_t* b) {
+  for (int i = 0; i < h->n_timing; ++i) {
+    const dflash_timing_point& p = h->timing[i];
+    if (p.section == section && (p.layer == layer || layer < 0)) {
+      *a = static_cast<hipEvent_t>(p.ev_start);
+      *b = static_cast<hipEvent_t>(p.ev_stop);
+      return true;
+    }
+  }
+  return false;
+}
+
 // RoPE inverse frequencies theta^(-2i/d) in double.
 RopeFreq rope_freq(const dflash_config& c) {
   RopeFreq f{};
@@ -279,26 +301,61 @@ template <typename P> P* at(void* ws, size_t off) {
 
 // ------------------------------------------------------------- GEMM launcher
 // One launch over rows [A.m0, A.m0 + A.mc): ksplit workgroups per tile group
-// (grid.y), nw waves per workgroup, tiles_per_wg consecutive tiles each.
+// (grid.y), nw waves per workgroup, tiles_per_wg steps of pt pair tiles each.
+// pt = 2 is taken only for one 16-row group (mc <= 16); skinny_pt() says
+// which pt a launch runs with, for epilogues that count workgroups.
+inline int skinny_pt(int pt, int mc) { return pt == 2 && mc <= 16 ? 2 : 1; }
+inline int skinny_wgs(int n_tiles, int tiles_per_wg, int pt) {
+  return ((n_tiles + pt - 1) / pt + tiles_per_wg - 1) / tiles_per_wg;
+}
 template <typename T, int NW, class Epi>
 hipError_t launch_skinny_nw(const AOperand<T>& A, int K, int n_tiles, int tiles_per_wg,
-                            int ksplit, const Epi& epi, hipStream_t st) {
+                            int ksplit, const Epi& epi, hipStream_t st, int pt = 1,
+                            hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
   const int kper = K / (NW * ksplit);
-  dim3 grid((n_tiles + tiles_per_wg - 1) / tiles_per_wg, ksplit);
+  // the kernel's slab pick: 32-column steps never straddle slabs, and its
+  // 40-bit reciprocal of slab_k is exact for columns below K
+  if (A.slab_k % 32 != 0 || static_cast<int64_t>(K) * A.slab_k >= (int64_t{1} << 40))
+    return hipErrorInvalidValue;
   const int mc = A.mc;
+  pt = skinny_pt(pt, mc);
+  dim3 grid(skinny_wgs(n_tiles, tiles_per_wg, pt), ksplit);
+  // with timing events, the dispatch records them itself (the span is the
+  // kernel's execution, without the packets an event record adds)
+  AOperand<T> a_arg = A;
+  int k_arg = K, nt_arg = n_tiles, tpw_arg = tiles_per_wg;
+  Epi e_arg = epi;
+  void* argv[] = {&a_arg, &k_arg, &nt_arg, &tpw_arg, &e_arg};
+  hipError_t ext = hipSuccess;
+#define DF_SK(MT, U, PT)                                                                        \
+  do {                                                                                          \
+    if (ev0)                                                                                    \
+      ext = hipExtLaunchKernel(reinterpret_cast<const void*>(&skinny_gemm_kernel<T, MT, U, NW, PT, Epi>), \
+                               grid, dim3(NW * 64), argv, 0, st, ev0, ev1, 0);                  \
+    else                                                                                        \
+      skinny_gemm_kernel<T, MT, U, NW, PT, Epi><<<grid, NW * 64, 0, st>>>(A, K, n_tiles,         \
+                                                                          tiles_per_wg, epi);   \
+  } while (0)
   if (mc <= 16) {
-    if (kper % 64 == 0) skinny_gemm_kernel<T, 1, 2, NW, Epi><<<grid, NW * 64, 0, st>>>(A, K, n_tiles, tiles_per_wg, epi);
-    else skinny_gemm_kernel<T, 1, 1, NW, Epi><<<grid, NW * 64, 0, st>>>(A, K, n_tiles, tiles_per_wg, epi);
+    if (pt == 2) {
+      if (kper % 64 == 0) DF_SK(1, 2, 2);
+      else DF_SK(1, 1, 2);
+    } else {
+      if (kper % 64 == 0) DF_SK(1, 2, 1);
+      else DF_SK(1, 1, 1);
+    }
   } else if (mc <= 32) {
-    if (kper % 64 == 0) skinny_gemm_kernel<T, 2, 2, NW, Epi><<<grid, NW * 64, 0, st>>>(A, K, n_tiles, tiles_per_wg, epi);
-    else skinny_gemm_kernel<T, 2, 1, NW, Epi><<<grid, NW * 64, 0, st>>>(A, K, n_tiles, tiles_per_wg, epi);
+    if (kper % 64 == 0) DF_SK(2, 2, 1);
+    else DF_SK(2, 1, 1);
   } else if (mc <= 64) {
-    skinny_gemm_kernel<T, 4, 1, NW, Epi><<<grid, NW * 64, 0, st>>>(A, K, n_tiles, tiles_per_wg, epi);
+    DF_SK(4, 1, 1);
   } else if (mc <= 128) {
-    skinny_gemm_kernel<T, 8, 1, NW, Epi><<<grid, NW * 64, 0, st>>>(A, K, n_tiles, tiles_per_wg, epi);
+    DF_SK(8, 1, 1);
   } else {
     return hipErrorInvalidValue;
   }
+#undef DF_SK
+  if (ext != hipSuccess) return ext;
   return hipGetLastError();
 }
 
@@ -307,15 +364,15 @@ hipError_t launch_skinny_nw(const AOperand<T>& A, int K, int n_tiles, int tiles_
 // best streaming configuration measured on MI355X for these shapes.
 template <typename T, class Epi, class PerLaunch>
 hipError_t run_rows(AOperand<T> A, int K, int n_tiles, int tiles_per_wg, int ksplit, Epi epi,
-                    hipStream_t st, PerLaunch per_launch, int nw = 4) {
+                    hipStream_t st, PerLaunch per_launch, int nw = 4, int pt = 1) {
   if (nw == 8 && K % (8 * ksplit * 32) != 0) nw = 4;
   for (int m0 = 0, li = 0; m0 < A.M; m0 += kMaxRowsPerLaunch, ++li) {
     A.m0 = m0;
     A.mc = A.M - m0 < kMaxRowsPerLaunch ? A.M - m0 : kMaxRowsPerLaunch;
     per_launch(epi, li);
     hipError_t e = nw == 8
-                       ? launch_skinny_nw<T, 8, Epi>(A, K, n_tiles, tiles_per_wg, ksplit, epi, st)
-                       : launch_skinny_nw<T, 4, Epi>(A, K, n_tiles, tiles_per_wg, ksplit, epi, st);
+                       ? launch_skinny_nw<T, 8, Epi>(A, K, n_tiles, tiles_per_wg, ksplit, epi, st, pt)
+                       : launch_skinny_nw<T, 4, Epi>(A, K, n_tiles, tiles_per_wg, ksplit, epi, st, pt);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -577,6 +634,17 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
       DF_HIP(launch_qkv_finish(true, qkvp, mp.ks_qkv, static_cast<int64_t>(M) * nq, M, D.qd,
                                D.kvd, D.d, B, qb, D.qd, kv->k[l], kv->v[l], kv->cap_total, freq,
                                seq, st));
+    } else if (bf) {
+      // 192 tiles on the 8B shape fill 3/4 of the CUs: split K over workgroups,
+      // then sum the slabs and rotate in the finishing kernel
+      const int nq = D.qd + 2 * D.kvd;
+      EpiQKVPartF32<T> e{static_cast<const T*>(w.wq), static_cast<const T*>(w.wk),
+                         static_cast<const T*>(w.wv), D.H, D.qd, D.kvd, qkvp, nq, M};
+      DF_HIP(run_rows<T>(a_single<T>(u, D.H, D.H, M), D.H, g.tiles_qkv, 1, g.ks_qkv, e, st,
+                         NoPerLaunch{}));
+      DF_HIP(launch_qkv_finish(true, qkvp, g.ks_qkv, static_cast<int64_t>(M) * nq, M, D.qd,
+                               D.kvd, D.d, B, qb, D.qd, kv->k[l], kv->v[l], kv->cap_total, freq,
+                               seq, st));
     } else {
       EpiQKV<T> e{};
       e.wq = static_cast<const T*>(w.wq);
@@ -605,8 +673,10 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
       DF_HIP(launch_mid<128>(a16(ob, D.qd), D.H, D.qd, ks_o, e, st));
     } else {
       EpiPartialF32<T> e{static_cast<const T*>(w.wo), D.qd, part, D.H, M};
+      // two pair tiles per step share each A fragment (measured faster here,
+      // slower on the QKV, down and LM-head shapes)
       DF_HIP(run_rows<T>(a_single<T>(ob, D.qd, D.qd, M), D.qd, g.tiles_o, 1, g.ks_o, e, st,
-                         NoPerLaunch{}));
+                         NoPerLaunch{}, 4, 2));
     }
     DF_MARK(DFLASH_SEC_O_PROJ, l, true);
     // feed-forward half: x += O partials; u = RMSNorm(x)
@@ -645,7 +715,8 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
   DF_MARK(DFLASH_SEC_LM_HEAD, -1, false);
   {
     float2* lm_part = at<float2>(ws, L.lm_off);
-    EpiLMHead<T, 1> e1{static_cast<const T*>(h->w.lm_head), D.H, D.V, g.wg_lm, lm_part, dbg_z};
+    const int n_wg = g.wg_lm;
+    EpiLMHead<T, 1> e1{static_cast<const T*>(h->w.lm_head), D.H, D.V, n_wg, lm_part, dbg_z};
     EpiLMHead<T, 2> e2{static_cast<const T*>(h->w.lm_head), D.H, D.V, g.wg_lm, lm_part, dbg_z};
     EpiLMHead<T, 4> e4{static_cast<const T*>(h->w.lm_head), D.H, D.V, g.wg_lm, lm_part, dbg_z};
     EpiLMHead<T, 8> e8{static_cast<const T*>(h->w.lm_head), D.H, D.V, g.wg_lm, lm_part, dbg_z};
@@ -653,22 +724,33 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
     if (mid) {
       const int n_parts = (D.V + 255) / 256;
       TEpiArgmax e{static_cast<const uint16_t*>(h->w.lm_head), D.H, D.V, n_parts, lm_part, dbg_z};
+      DF_MARK(DFLASH_SEC_LM_GEMM, -1, false);
       DF_HIP(launch_mid<256>(a16(u, D.H), D.V, D.H, 1, e, st));
+      DF_MARK(DFLASH_SEC_LM_GEMM, -1, true);
       DF_HIP(launch_lm_argmax_finalize(lm_part, n_parts, M, B, draft, st));
     }
+    // one launch covers M: the LM-GEMM timing point (if set) is recorded by
+    // that dispatch; otherwise around the launches
+    hipEvent_t ev0 = nullptr, ev1 = nullptr;
+    const bool one = M <= kMaxRowsPerLaunch && timing_events(h, DFLASH_SEC_LM_GEMM, -1, &ev0, &ev1);
+    if (!mid && !one) DF_MARK(DFLASH_SEC_LM_GEMM, -1, false);
     for (int m0 = 0; !mid && m0 < M; m0 += kMaxRowsPerLaunch) {
       AOperand<T> Ai = A;
       Ai.m0 = m0;
       Ai.mc = M - m0 < kMaxRowsPerLaunch ? M - m0 : kMaxRowsPerLaunch;
       const int mt = (Ai.mc + 15) / 16;
       hipError_t e;
-      if (mt <= 1) e = launch_skinny_nw<T, 4>(Ai, D.H, g.tiles_lm, kLmTilesPerWg, 1, e1, st);
-      else if (mt <= 2) e = launch_skinny_nw<T, 4>(Ai, D.H, g.tiles_lm, kLmTilesPerWg, 1, e2, st);
-      else if (mt <= 4) e = launch_skinny_nw<T, 4>(Ai, D.H, g.tiles_lm, kLmTilesPerWg, 1, e4, st);
-      else e = launch_skinny_nw<T, 4>(Ai, D.H, g.tiles_lm, kLmTilesPerWg, 1, e8, st);
+      const hipEvent_t a = one ? ev0 : nullptr, b = one ? ev1 : nullptr;
+      if (mt <= 1) e = launch_skinny_nw<T, 4>(Ai, D.H, g.tiles_lm, kLmTilesPerWg, 1, e1, st, 1, a, b);
+      else if (mt <= 2) e = launch_skinny_nw<T, 4>(Ai, D.H, g.tiles_lm, kLmTilesPerWg, 1, e2, st, 1, a, b);
+      else if (mt <= 4) e = launch_skinny_nw<T, 4>(Ai, D.H, g.tiles_lm, kLmTilesPerWg, 1, e4, st, 1, a, b);
+      else e = launch_skinny_nw<T, 4>(Ai, D.H, g.tiles_lm, kLmTilesPerWg, 1, e8, st, 1, a, b);
       DF_HIP(e);
     }
-    if (!mid) DF_HIP(launch_lm_argmax_finalize(lm_part, g.wg_lm, M, B, draft, st));
+    if (!mid) {
+      if (!one) DF_MARK(DFLASH_SEC_LM_GEMM, -1, true);
+      DF_HIP(launch_lm_argmax_finalize(lm_part, n_wg, M, B, draft, st));
+    }
   }
   DF_MARK(DFLASH_SEC_LM_HEAD, -1, true);
   return DFLASH_OK;
@@ -820,7 +902,7 @@ dflash_status dflash_draft_block(dflash_handle* h, dflash_kv* kv, int32_t block_
 dflash_status dflash_set_timing(dflash_handle* h, const dflash_timing_point* points, int32_t n) {
   if (!h || n < 0 || n > 32 || (n > 0 && !points)) return DFLASH_ERR_INVALID_ARG;
   for (int i = 0; i < n; ++i)
-    if (points[i].section < DFLASH_SEC_FUSE_GEMM || points[i].section > DFLASH_SEC_LM_HEAD ||
+    if (points[i].section < DFLASH_SEC_FUSE_GEMM || points[i].section > DFLASH_SEC_LM_GEMM ||
         !points[i].ev_start || !points[i].ev_stop)
       return DFLASH_ERR_INVALID_ARG;
   for (int i = 0; i < n; ++i) h->timing[i] = points[i];

@@ -37,6 +37,39 @@ struct EpiPartialF32 {
   __device__ void finish(State&, int, int, int) const {}
 };
 
+// Fused Q/K/V projection as fp32 K-split partials: output column n of the
+// stacked [Wq; Wk; Wv] (qd + 2 kvd rows) goes to out[(split * slab_rows + m) *
+// ldo + n]; a finishing kernel sums the splits and applies RoPE.  qd and kvd
+// are multiples of 32, so a 32-row tile never straddles two matrices.
+template <typename T>
+struct EpiQKVPartF32 {
+  using State = NoState;
+  const T* wq;
+  const T* wk;
+  const T* wv;
+  int K, qd, kvd;
+  float* out;
+  int64_t ldo;
+  int64_t slab_rows;
+  __device__ void init(State&) const {}
+  __device__ void rows(int tile, int r16, const T*& w0, const T*& w1) const {
+    const int n = tile * 32;
+    const T* base = n < qd ? wq + static_cast<int64_t>(n) * K
+                  : n < qd + kvd ? wk + static_cast<int64_t>(n - qd) * K
+                                 : wv + static_cast<int64_t>(n - qd - kvd) * K;
+    w0 = base + static_cast<int64_t>(r16) * K;
+    w1 = w0 + static_cast<int64_t>(16) * K;
+  }
+  __device__ void apply(State&, int, int tile, int split, int m, int i, bool valid, float v0,
+                        float v1) const {
+    if (!valid) return;
+    float* o = out + (split * slab_rows + m) * ldo + tile * 32 + i;
+    o[0] = v0;
+    o[16] = v1;
+  }
+  __device__ void finish(State&, int, int, int) const {}
+};
+
 // SwiGLU: h[m, j] = silu(u . wg[j]) * (u . wu[j]), stored in the handle type.
 template <typename T>
 struct EpiSwiGLU {

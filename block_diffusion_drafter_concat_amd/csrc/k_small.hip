@@ -1,6 +1,7 @@
 // Small memory-bound kernels of the drafter pass: block embedding, residual
 // RMSNorm, the QKV finish of batched blocks, LM-head argmax finalize and
 // greedy verification.
+#include <algorithm>
 #include "kernels.h"
 
 namespace dflash {
@@ -222,7 +223,8 @@ __global__ __launch_bounds__(256) void lm_argmax_finalize_kernel(const float2* _
 // partial slabs [ks][M][qd + 2 kvd]: sum the slabs, rotate q and k at the
 // block position len[b] + j (pairs (c, c + d/2) of a head), store q to its
 // buffer and k, v to the layer's cache at row off[b] + len[b] + j (V
-// transposed).  One workgroup per row.
+// transposed).  grid.x runs over rows; the grid.y workgroups of a row split
+// its columns (few rows still spread over the GPU).
 template <typename T>
 __global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict__ part, int ks,
                                                          int64_t slab, int qd, int kvd, int d,
@@ -234,24 +236,29 @@ __global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict
   const int64_t row = seq.off[b] + pos;
   const int nq = qd + 2 * kvd, half = d / 2;
   const float* pr = part + static_cast<int64_t>(m) * nq;
-  for (int p = threadIdx.x; p < (qd + kvd) / 2; p += 256) {
-    const int c = p % half, col = (p / half) * d + c;   // [q heads | k heads] columns
-    float x0 = 0.f, x1 = 0.f;
-    for (int s = 0; s < ks; ++s) {
-      x0 += pr[s * slab + col];
-      x1 += pr[s * slab + col + half];
+  // flat work index: rotation pairs of the q and k columns, then v columns;
+  // grid.y workgroups share a row's work
+  const int n_pairs = (qd + kvd) / 2, total = n_pairs + kvd;
+  for (int p = blockIdx.y * 256 + threadIdx.x; p < total; p += gridDim.y * 256) {
+    if (p < n_pairs) {
+      const int c = p % half, col = (p / half) * d + c;   // [q heads | k heads] columns
+      float x0 = 0.f, x1 = 0.f;
+      for (int s = 0; s < ks; ++s) {
+        x0 += pr[s * slab + col];
+        x1 += pr[s * slab + col + half];
+      }
+      float cs, sn;
+      rope_cos_sin(pos, c, freq, cs, sn);
+      T* dst = col < qd ? q + static_cast<int64_t>(m) * ldq + col
+                        : kc + (static_cast<int64_t>((col - qd) / d) * cap + row) * d + c;
+      stf(dst, x0 * cs - x1 * sn);
+      stf(dst + half, x1 * cs + x0 * sn);
+    } else {
+      const int cv = p - n_pairs;
+      float x = 0.f;
+      for (int s = 0; s < ks; ++s) x += pr[s * slab + qd + kvd + cv];
+      stf(vc + static_cast<int64_t>(cv) * cap + row, x);
     }
-    float cs, sn;
-    rope_cos_sin(pos, c, freq, cs, sn);
-    T* dst = col < qd ? q + static_cast<int64_t>(m) * ldq + col
-                      : kc + (static_cast<int64_t>((col - qd) / d) * cap + row) * d + c;
-    stf(dst, x0 * cs - x1 * sn);
-    stf(dst + half, x1 * cs + x0 * sn);
-  }
-  for (int cv = threadIdx.x; cv < kvd; cv += 256) {
-    float x = 0.f;
-    for (int s = 0; s < ks; ++s) x += pr[s * slab + qd + kvd + cv];
-    stf(vc + static_cast<int64_t>(cv) * cap + row, x);
   }
 }
 
@@ -259,12 +266,16 @@ hipError_t launch_qkv_finish(bool bf16, const float* part, int ks, int64_t slab,
                              int kvd, int d, int B, void* q, int64_t ldq, void* kc, void* vc,
                              int64_t cap, const RopeFreq& freq, const SeqTable& seq,
                              hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  // enough workgroups to cover the GPU when rows are few
+  const int total = (qd + kvd) / 2 + kvd;
+  const dim3 grid(rows, std::max(1, std::min((total + 255) / 256, 1024 / rows)));
   if (bf16)
-    qkv_finish_kernel<uint16_t><<<rows, 256, 0, st>>>(
+    qkv_finish_kernel<uint16_t><<<grid, 256, 0, st>>>(
         part, ks, slab, qd, kvd, d, B, static_cast<uint16_t*>(q), ldq,
         static_cast<uint16_t*>(kc), static_cast<uint16_t*>(vc), cap, freq, seq);
   else
-    qkv_finish_kernel<float><<<rows, 256, 0, st>>>(part, ks, slab, qd, kvd, d, B,
+    qkv_finish_kernel<float><<<grid, 256, 0, st>>>(part, ks, slab, qd, kvd, d, B,
                                                    static_cast<float*>(q), ldq,
                                                    static_cast<float*>(kc),
                                                    static_cast<float*>(vc), cap, freq, seq);

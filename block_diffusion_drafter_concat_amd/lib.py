@@ -31,7 +31,7 @@ EXPORTS = ("dflash_target_layer_ids", "dflash_create", "dflash_destroy",
 # dflash_section
 SECTIONS = {"fuse_gemm": 1, "fuse_norm": 2, "inject": 3, "embed": 4, "attn_norm": 5, "qkv": 6,
             "attention": 7, "o_proj": 8, "ffn_norm": 9, "gate_up": 10, "down": 11,
-            "final_norm": 12, "lm_head": 13}
+            "final_norm": 12, "lm_head": 13, "lm_gemm": 14}
 
 
 class DflashError(RuntimeError):

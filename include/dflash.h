@@ -215,7 +215,10 @@ typedef enum {
   DFLASH_SEC_GATE_UP = 10,    /* per layer: gate/up projection + SwiGLU */
   DFLASH_SEC_DOWN = 11,       /* per layer: down projection + residual */
   DFLASH_SEC_FINAL_NORM = 12, /* final RMSNorm */
-  DFLASH_SEC_LM_HEAD = 13     /* LM head with fused argmax */
+  DFLASH_SEC_LM_HEAD = 13,    /* LM head with fused argmax (GEMM and the argmax fold) */
+  DFLASH_SEC_LM_GEMM = 14     /* the LM-head GEMM launch alone (argmax partials in its epilogue);
+                                 when one dispatch covers the rows, that dispatch records the
+                                 two events itself, so the span is its execution time */
 } dflash_section;
 
 typedef struct {

@@ -176,3 +176,21 @@ def test_fuse_and_verify_host_checks():
     assert lib.dflash_verify_workspace_size(16, 16, 151936) >= 16 * 16 * 8
     assert L.status_string(L.ERR_CAPACITY) == "cache capacity exceeded"
     lib.dflash_destroy(h)
+
+
+def test_set_timing_host_checks():
+    lib = L.load()
+    st, h, keep = _create(configs.TINY_F32)
+    assert st == L.OK
+    every = (L.TimingPoint * len(L.SECTIONS))(*[
+        L.TimingPoint(sec, -1, _FAKE, _FAKE + 8) for sec in L.SECTIONS.values()])
+    assert lib.dflash_set_timing(h, every, len(L.SECTIONS)) == L.OK
+    assert sorted(L.SECTIONS.values()) == list(range(1, len(L.SECTIONS) + 1))
+    for bad in (0, len(L.SECTIONS) + 1):
+        pt = (L.TimingPoint * 1)(L.TimingPoint(bad, -1, _FAKE, _FAKE + 8))
+        assert lib.dflash_set_timing(h, pt, 1) == L.ERR_INVALID_ARG
+    pt = (L.TimingPoint * 1)(L.TimingPoint(L.SECTIONS["lm_gemm"], -1, None, _FAKE))
+    assert lib.dflash_set_timing(h, pt, 1) == L.ERR_INVALID_ARG
+    assert lib.dflash_set_timing(h, None, 33) == L.ERR_INVALID_ARG
+    assert lib.dflash_set_timing(h, None, 0) == L.OK
+    assert lib.dflash_destroy(h) == L.OK
