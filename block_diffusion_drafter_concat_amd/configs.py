@@ -155,3 +155,23 @@ def make_features(shape: DrafterShape, wid: int, n_tokens: int, name: str = "fea
 def make_anchors(shape: DrafterShape, wid: int, batch: int, name: str = "anchor") -> np.ndarray:
     """Anchor token ids uniform on [0, V-2] (V-1 is the mask token)."""
     return synth.integers((batch,), 0, shape.vocab - 2, wid, synth.STREAM_INDICES, name)
+
+
+def make_training_layout(shape: DrafterShape, wid: int, lens, blocks_per_seq: int,
+                         block_size: int) -> tuple:
+    """Seeded training layout over sequences with context lengths ``lens``.
+
+    Returns (tokens, block_seq, anchor_pos): tokens[s] holds lens[s] + block_size
+    ids uniform on [0, V-2] (so every anchor in 0..lens[s] has its labels);
+    block i belongs to sequence block_seq[i] and starts at anchor_pos[i], drawn
+    uniformly from 0..lens[s] without repeats while there are enough positions.
+    """
+    tokens, block_seq, anchor_pos = [], [], []
+    for s, L in enumerate(lens):
+        tokens.append(synth.integers((int(L) + block_size,), 0, shape.vocab - 2, wid,
+                                     synth.STREAM_INDICES, f"train_tokens{s}"))
+        g = synth.rng(wid, synth.STREAM_INDICES, f"train_anchors{s}")
+        n = min(blocks_per_seq, int(L) + 1)
+        anchor_pos += [int(a) for a in np.sort(g.choice(int(L) + 1, size=n, replace=False))]
+        block_seq += [s] * n
+    return tokens, np.asarray(block_seq, dtype=np.int32), np.asarray(anchor_pos, dtype=np.int32)

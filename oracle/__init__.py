@@ -7,4 +7,5 @@ from .dflash_oracle import *  # noqa: F401,F403
 from .dflash_oracle import (bf16_round, rmsnorm, rope, silu, argmax_lowest,  # noqa: F401
                             target_layer_ids, fuse_context, inject_kv, block_attention,
                             decoder_layer, draft_block, verify_greedy, prefill,
-                            append_context, ROUNDING_POINTS)
+                            append_context, loss_weights, cross_entropy, train_forward,
+                            ROUNDING_POINTS)

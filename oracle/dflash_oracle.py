@@ -34,6 +34,14 @@ Readings of points the pages leave open (each repeated where it is used):
   R6 every argmax breaks ties by the lowest index.
   R7 verification: a = length of the longest prefix with target_argmax[j] ==
      draft[j+1]; bonus = target_argmax[a].
+  R8 training layout: block i of sequence s starts at anchor position a_i
+     (0 <= a_i <= L_s): slot 0 holds the token at a_i, slots 1..B-1 the mask
+     token, slot j sits at position a_i + j; the block sees context rows
+     [0, a_i) of s and its own block, nothing else; slot j >= 1 is scored
+     against the token at a_i + j.
+  R9 loss weights: the k-th predicted slot (k = j = 1..B-1) weighs
+     exp(-(k-1)/gamma); the loss is the weighted mean over every scored slot
+     of every block, sum(w * ce) / sum(w).
 """
 from __future__ import annotations
 
@@ -314,3 +322,55 @@ def append_context(cache, weights, shape, feats) -> list:
     new = inject_kv(c, L + np.arange(c.shape[0]), weights["layers"], shape, rb)
     return [(np.concatenate([k, nk]), np.concatenate([v, nv]))
             for (k, v), (nk, nv) in zip(cache, new)]
+
+
+# ------------------------------------------- (N2) training-layout forward
+
+def loss_weights(block_size: int, gamma: float) -> np.ndarray:
+    """Weight of draft slots 1..B-1: w_k = exp(-(k-1)/gamma) for the k-th
+    predicted token of a block ([Arch] 训练策略 2: earlier slots weigh more,
+    because an early miss cascades).  Reading R9: k = slot index j."""
+    k = np.arange(1, int(block_size), dtype=np.float64)
+    return np.exp(-(k - 1.0) / float(gamma))
+
+
+def cross_entropy(logits, label) -> np.ndarray:
+    """-log softmax(logits)[label] over the last axis, float64."""
+    z = _f64(logits)
+    m = z.max(axis=-1, keepdims=True)
+    lse = m[..., 0] + np.log(np.exp(z - m).sum(axis=-1))
+    return lse - np.take_along_axis(z, np.asarray(label)[..., None], axis=-1)[..., 0]
+
+
+def train_forward(weights, shape, caches, block_seq, anchor_pos, tokens, block_size: int,
+                  gamma: float) -> dict:
+    """Training-layout forward and its position-weighted loss (readings R8, R9).
+
+    [Arch] 训练策略 1: blocks start at randomly sampled anchor tokens, as each
+    draft block at inference starts at a verified token; 技术细节补充 /
+    稀疏注意力训练: bidirectional inside a block, no flow between blocks.
+    Block i is exactly an inference block whose context is the first a_i rows
+    of its sequence's cache, so it is computed as one: ``draft_block`` over
+    per-block views of the caches.
+
+    caches[s] = [(K [L_s, Hkv, d], V [L_s, Hkv, d]) per layer]; block_seq,
+    anchor_pos: [n]; tokens[s]: the token ids of sequence s (length >
+    a_i + B - 1 for its blocks).  Returns logits [n, B, V], slot_loss [n, B-1]
+    (cross-entropy of slot j against tokens[s][a_i + j]) and loss (weighted
+    mean).
+    """
+    B = int(block_size)
+    views, anchors, labels = [], [], []
+    for s_i, a in zip(block_seq, anchor_pos):
+        s_i, a = int(s_i), int(a)
+        views.append([(k[:a], v[:a]) for k, v in caches[s_i]])
+        tok = np.asarray(tokens[s_i])
+        anchors.append(int(tok[a]))
+        labels.append(tok[a + 1:a + B])
+    out = draft_block(weights, shape, views, anchors, B)
+    logits = out["logits"]
+    labels = np.stack(labels).astype(np.int64)
+    slot_loss = cross_entropy(logits[:, 1:, :], labels)
+    w = loss_weights(B, gamma)[None, :] * np.ones_like(slot_loss)
+    loss = float((w * slot_loss).sum() / w.sum())
+    return {"logits": logits, "slot_loss": slot_loss, "loss": loss, "labels": labels}

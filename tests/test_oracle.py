@@ -554,3 +554,137 @@ def test_param_count_matches_2b_claim():
     want = int(_golden_lines("param_scale.txt")[0].split(":")[1])
     p = configs.TARGET_27B_LIKE.drafter_params()
     assert round(p / 1e9) == want
+
+
+# ------------------------------------------------------------ training layout
+
+def test_loss_weights_properties():
+    """w_k = exp(-(k-1)/gamma): the first draft slot weighs 1, the weights fall
+    geometrically with ratio exp(-1/gamma), and a large gamma is uniform."""
+    for B, gamma in [(2, 1.0), (8, 3.0), (16, 7.0)]:
+        w = O.loss_weights(B, gamma)
+        assert w.shape == (B - 1,) and w[0] == 1.0
+        assert np.all(np.diff(w) < 0) or B == 2
+        np.testing.assert_allclose(w[1:] / w[:-1], np.full(B - 2, np.e ** (-1.0 / gamma)),
+                                   rtol=1e-14)
+    np.testing.assert_allclose(O.loss_weights(16, 1e12), np.ones(15), rtol=1e-10)
+
+
+def test_cross_entropy_matches_torch_and_limits():
+    g = np.random.default_rng(31)
+    z = g.standard_normal((3, 5, 17)) * 4
+    lab = g.integers(0, 17, size=(3, 5))
+    want = torch.nn.functional.cross_entropy(torch.from_numpy(z).reshape(-1, 17),
+                                             torch.from_numpy(lab).reshape(-1),
+                                             reduction="none").numpy().reshape(3, 5)
+    np.testing.assert_allclose(O.cross_entropy(z, lab), want, rtol=1e-12, atol=1e-12)
+    # equal logits: log V; one dominant logit at the label: ~0; far from it: the gap
+    np.testing.assert_allclose(O.cross_entropy(np.zeros((2, 9)), [0, 4]), np.log(9), rtol=1e-14)
+    big = np.zeros(6); big[2] = 800.0
+    assert O.cross_entropy(big, 2) < 1e-300 + 1e-12
+    np.testing.assert_allclose(O.cross_entropy(big, 0), 800.0, rtol=1e-14)
+
+
+def _train_case(dtype="f32"):
+    shape = _tiny_shape(dtype=dtype)
+    w = configs.make_weights(shape, 921)
+    lens = [13, 0, 29]
+    feats = [configs.make_features(shape, 921, L, name=f"s{s}_") if L else None
+             for s, L in enumerate(lens)]
+    caches = []
+    for f, L in zip(feats, lens):
+        if L:
+            caches += O.prefill(w, shape, [f])
+        else:
+            caches.append([(np.zeros((0, shape.n_kv_heads, shape.head_dim)),) * 2
+                           for _ in range(shape.n_layers)])
+    tokens, bseq, apos = configs.make_training_layout(shape, 921, lens, 4, 6)
+    return shape, w, feats, caches, tokens, bseq, apos
+
+
+def test_training_block_equals_inference_on_the_prefix():
+    """Block i of the training layout is the inference draft of the sequence
+    cut at its anchor: its context cache is the prefill of the first a_i
+    feature rows (injection is per row and position), its anchor the token at
+    a_i, its positions a_i .. a_i + B - 1."""
+    shape, w, feats, caches, tokens, bseq, apos = _train_case()
+    B = 6
+    out = O.train_forward(w, shape, caches, bseq, apos, tokens, B, gamma=4.0)
+    for i, (s, a) in enumerate(zip(bseq, apos)):
+        if a:
+            pre = O.prefill(w, shape, [[f[:a] for f in feats[s]]])
+        else:
+            pre = [[(np.zeros((0, shape.n_kv_heads, shape.head_dim)),) * 2
+                    for _ in range(shape.n_layers)]]
+        ref = O.draft_block(w, shape, pre, [tokens[s][a]], B)
+        np.testing.assert_allclose(out["logits"][i], ref["logits"][0], rtol=1e-12, atol=1e-12)
+        np.testing.assert_array_equal(out["labels"][i], tokens[s][a + 1:a + B])
+
+
+def test_training_blocks_see_nothing_past_their_anchor_or_each_other():
+    shape, w, feats, caches, tokens, bseq, apos = _train_case()
+    B = 6
+    out = O.train_forward(w, shape, caches, bseq, apos, tokens, B, gamma=4.0)
+    # rows at or after every anchor of sequence 2 replaced by noise: no block of
+    # sequence 2 may change; rows before the last anchor do matter
+    s2 = [i for i in range(len(bseq)) if bseq[i] == 2]
+    a_min = min(apos[i] for i in s2)
+    g = np.random.default_rng(5)
+    noisy = [list(c) for c in caches]
+    noisy[2] = [(np.concatenate([k[:a_min], g.standard_normal(k[a_min:].shape)]),
+                 np.concatenate([v[:a_min], g.standard_normal(v[a_min:].shape)]))
+                for k, v in caches[2]]
+    out2 = O.train_forward(w, shape, noisy, bseq, apos, tokens, B, gamma=4.0)
+    for i in range(len(bseq)):
+        if bseq[i] != 2 or apos[i] == a_min:
+            np.testing.assert_array_equal(out2["logits"][i], out["logits"][i])
+        else:
+            assert np.abs(out2["logits"][i] - out["logits"][i]).max() > 1e-6
+    # one block alone gives the same numbers as inside the whole layout (up to
+    # the summation order of the stacked row products)
+    for i in (0, len(bseq) - 1):
+        one = O.train_forward(w, shape, caches, bseq[i:i + 1], apos[i:i + 1], tokens, B, 4.0)
+        np.testing.assert_allclose(one["logits"][0], out["logits"][i], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(one["slot_loss"][0], out["slot_loss"][i], rtol=1e-12)
+
+
+def test_training_loss_is_the_weighted_mean_of_slot_losses():
+    shape, w, feats, caches, tokens, bseq, apos = _train_case()
+    B = 6
+    out = O.train_forward(w, shape, caches, bseq, apos, tokens, B, gamma=2.5)
+    z = torch.from_numpy(out["logits"][:, 1:, :]).reshape(-1, shape.vocab)
+    ce = torch.nn.functional.cross_entropy(z, torch.from_numpy(out["labels"]).reshape(-1),
+                                           reduction="none").numpy().reshape(-1, B - 1)
+    np.testing.assert_allclose(out["slot_loss"], ce, rtol=1e-12, atol=1e-12)
+    big = O.train_forward(w, shape, caches, bseq, apos, tokens, B, gamma=1e15)
+    np.testing.assert_allclose(big["loss"], ce.mean(), rtol=1e-12)
+    # gamma -> 0: only the first draft slot of each block counts
+    small = O.train_forward(w, shape, caches, bseq, apos, tokens, B, gamma=1e-3)
+    np.testing.assert_allclose(small["loss"], ce[:, 0].mean(), rtol=1e-9)
+
+
+def test_multi_block_attention_equals_dense_masked_reference():
+    """Several blocks of one sequence at different anchors, packed with the
+    sequence's whole context: block i may see context rows before a_i and its
+    own block (inter-block flow blocked), nothing else."""
+    g = np.random.default_rng(12)
+    Hq, Hkv, d, B, L = 4, 2, 8, 4, 23
+    anchors = [0, 5, 5, 23]
+    ck, cv = g.standard_normal((L, Hkv, d)), g.standard_normal((L, Hkv, d))
+    qs = [g.standard_normal((B, Hq, d)) for _ in anchors]
+    ks = [g.standard_normal((B, Hkv, d)) for _ in anchors]
+    vs = [g.standard_normal((B, Hkv, d)) for _ in anchors]
+    keys = np.concatenate([ck] + ks)
+    vals = np.concatenate([cv] + vs)
+    mask = np.zeros((len(anchors) * B, keys.shape[0]), dtype=bool)
+    for i, a in enumerate(anchors):
+        mask[i * B:(i + 1) * B, :a] = True
+        mask[i * B:(i + 1) * B, L + i * B:L + (i + 1) * B] = True
+    G = Hq // Hkv
+    kk = np.repeat(keys.transpose(1, 0, 2), G, axis=0)
+    vv = np.repeat(vals.transpose(1, 0, 2), G, axis=0)
+    ref = _sdpa(np.concatenate(qs).transpose(1, 0, 2), kk, vv, mask).transpose(1, 0, 2)
+    for i, a in enumerate(anchors):
+        got = O.block_attention(qs[i], np.concatenate([ck[:a], ks[i]]),
+                                np.concatenate([cv[:a], vs[i]]))
+        np.testing.assert_allclose(got, ref[i * B:(i + 1) * B], rtol=1e-10, atol=1e-12)
