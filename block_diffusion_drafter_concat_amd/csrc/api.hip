@@ -213,7 +213,8 @@ GemmPlan gemm_plan(const Dims& D) {
 // Every call lays out its own scratch from offset 0 with sizes that grow with
 // (batch, block, tokens); dflash_workspace_size takes the largest.
 struct Layout {
-  size_t x_off, u_off, q_off, o_off, h_off, part_off, qkvp_off, lm_off, ao_off, aml_off, ver_off;
+  size_t x_off, u_off, q_off, o_off, h_off, part_off, qkvp_off, lm_off, bkv_off, ao_off, aml_off,
+      ver_off;
   size_t total;
 };
 
@@ -243,14 +244,17 @@ Layout layout(const dflash_handle* h, int max_batch, int max_block, int64_t max_
       qkvp = std::max(qkvp, static_cast<size_t>(mp.ks_qkv) * m * (D.qd + 2 * D.kvd) * 4);
     }
   }
-  if (h->cfg.dtype == DFLASH_BF16) {
-    // bf16 QKV below the mid-M path: weight-streaming split partials
-    const size_t ms = std::min(M, static_cast<size_t>(kMidMinRows - 1));
+  {
+    // QKV on the weight-streaming split path: bf16 below the mid-M path, and
+    // every float32 training-layout call
+    const size_t ms = h->cfg.dtype == DFLASH_BF16 ? std::min(M, static_cast<size_t>(kMidMinRows - 1)) : M;
     qkvp = std::max(qkvp, static_cast<size_t>(g.ks_qkv) * ms * (D.qd + 2 * D.kvd) * 4);
   }
   L.part_off = off; off += align_up(part);
   L.qkvp_off = off; off += align_up(qkvp);
-  L.lm_off = off;   off += align_up(M * g.wg_lm * 8);
+  L.lm_off = off;   off += align_up(M * g.wg_lm * 16);   // argmax: 8 B, training loss: 16 B
+  // training layout: block K and V^T, kTrainSlab rows per block
+  L.bkv_off = off;  off += align_up(2 * static_cast<size_t>(D.Hkv) * max_batch * kTrainSlab * D.d * es);
   const size_t qr = static_cast<size_t>((D.G * max_block + 15) / 16 * 16);
   const size_t slots = static_cast<size_t>(attn_slots(max_batch, D.Hkv));
   L.ao_off = off;  off += align_up(slots * qr * D.d * 4);
@@ -553,11 +557,25 @@ dflash_status inject_impl(dflash_handle* h, const void* ctx, const SeqTable& seq
   return DFLASH_OK;
 }
 
+// A training-layout request: entry b of the batch is a block at anchor
+// position len[b] of the sequence whose cache slab starts at off[b]; the LM
+// head then scores slots 1..B-1 against labels (device [n][B-1]).
+struct TrainSpec {
+  int n;
+  const int32_t* len;      // host [n]
+  const int64_t* off;      // host [n]
+  const int32_t* labels;   // device [n][B-1]
+  float gamma;
+  float* slot_loss;        // device [n][B-1]
+  float* loss;             // device [1]
+};
+
 template <typename T>
 dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* anchors,
-                         int32_t* draft, float* dbg_h, float* dbg_z, void* ws, hipStream_t st) {
+                         int32_t* draft, float* dbg_h, float* dbg_z, void* ws, hipStream_t st,
+                         const TrainSpec* tr = nullptr) {
   const Dims D = dims(h->cfg);
-  const int nb = kv->batch, M = nb * B;
+  const int nb = tr ? tr->n : kv->batch, M = nb * B;
   const bool bf = h->cfg.dtype == DFLASH_BF16;
   const Layout L = layout(h, nb, B, 1);
   const GemmPlan g = gemm_plan(D);
@@ -565,12 +583,17 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
 
   SeqTable seq{};
   seq.n = nb;
-  int max_keys = 0;
+  int max_keys = 0;   // keys in the cache per entry (training: the context part only)
   for (int b = 0; b < nb; ++b) {
-    seq.len[b] = kv->seq_len[b];
-    seq.off[b] = kv->seq_off[b];
-    max_keys = (kv->seq_len[b] + B > max_keys) ? kv->seq_len[b] + B : max_keys;
+    seq.len[b] = tr ? tr->len[b] : kv->seq_len[b];
+    seq.off[b] = tr ? tr->off[b] : kv->seq_off[b];
+    const int nk = seq.len[b] + (tr ? 0 : B);
+    max_keys = nk > max_keys ? nk : max_keys;
   }
+  // training layout: the blocks' own K/V in the workspace, kTrainSlab rows each
+  const int64_t capb = static_cast<int64_t>(nb) * kTrainSlab;
+  T* bk = tr ? at<T>(ws, L.bkv_off) : nullptr;
+  T* bv = tr ? bk + static_cast<int64_t>(D.Hkv) * capb * D.d : nullptr;
   const RopeFreq freq = rope_freq(h->cfg);
   float* x = at<float>(ws, L.x_off);
   T* u = at<T>(ws, L.u_off);
@@ -599,7 +622,8 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
   for (int b = 0; b < nb; ++b) keys[b] = seq.len[b] + B;
   const int max_c = static_cast<int>(
       std::max<int64_t>(1, std::min<int64_t>(kMaxAttnChunks, attn_slots(nb, D.Hkv) / (nb * D.Hkv))));
-  const int chunk = attn_chunk(keys, nb, D.Hkv, max_keys, max_c);
+  // (training: one chunk of every entry holds its block's keys)
+  const int chunk = attn_chunk(keys, nb, D.Hkv, max_keys, tr ? max_c - 1 : max_c);
   AttnArgs aa{};
   aa.q = qb;
   aa.ldq = D.qd;
@@ -612,9 +636,16 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
   aa.n_kv = D.Hkv;
   aa.head_dim = D.d;
   aa.chunk = chunk;
-  aa.max_chunks = (max_keys + chunk - 1) / chunk;
+  aa.max_chunks = (max_keys + chunk - 1) / chunk + (tr ? 1 : 0);
   aa.scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(D.d)));
   aa.seq = seq;
+  aa.kb = bk;
+  aa.vb = bv;
+  aa.capb = capb;
+  // where the QKV finish puts the block's K/V: the cache, or the block buffer
+  auto kdst = [&](int l) -> void* { return tr ? static_cast<void*>(bk) : kv->k[l]; };
+  auto vdst = [&](int l) -> void* { return tr ? static_cast<void*>(bv) : kv->v[l]; };
+  const int64_t dcap = tr ? capb : kv->cap_total;
 
   int pending = 0;   // K-split slabs of the last projection, not yet added to x
   for (int l = 0; l < D.L; ++l) {
@@ -632,19 +663,20 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
                      static_cast<const uint16_t*>(w.wv), D.H, D.qd, D.kvd, qkvp, nq, M};
       DF_HIP(launch_mid<128>(a16(u, D.H), nq, D.H, mp.ks_qkv, e, st));
       DF_HIP(launch_qkv_finish(true, qkvp, mp.ks_qkv, static_cast<int64_t>(M) * nq, M, D.qd,
-                               D.kvd, D.d, B, qb, D.qd, kv->k[l], kv->v[l], kv->cap_total, freq,
-                               seq, st));
-    } else if (bf) {
+                               D.kvd, D.d, B, qb, D.qd, kdst(l), vdst(l), dcap, freq, seq, st,
+                               tr != nullptr));
+    } else if (bf || tr) {
       // 192 tiles on the 8B shape fill 3/4 of the CUs: split K over workgroups,
-      // then sum the slabs and rotate in the finishing kernel
+      // then sum the slabs and rotate in the finishing kernel (which also
+      // sends a training layout's block K/V to the block buffer)
       const int nq = D.qd + 2 * D.kvd;
       EpiQKVPartF32<T> e{static_cast<const T*>(w.wq), static_cast<const T*>(w.wk),
                          static_cast<const T*>(w.wv), D.H, D.qd, D.kvd, qkvp, nq, M};
       DF_HIP(run_rows<T>(a_single<T>(u, D.H, D.H, M), D.H, g.tiles_qkv, 1, g.ks_qkv, e, st,
                          NoPerLaunch{}));
-      DF_HIP(launch_qkv_finish(true, qkvp, g.ks_qkv, static_cast<int64_t>(M) * nq, M, D.qd,
-                               D.kvd, D.d, B, qb, D.qd, kv->k[l], kv->v[l], kv->cap_total, freq,
-                               seq, st));
+      DF_HIP(launch_qkv_finish(bf, qkvp, g.ks_qkv, static_cast<int64_t>(M) * nq, M, D.qd,
+                               D.kvd, D.d, B, qb, D.qd, kdst(l), vdst(l), dcap, freq, seq, st,
+                               tr != nullptr));
     } else {
       EpiQKV<T> e{};
       e.wq = static_cast<const T*>(w.wq);
@@ -713,6 +745,34 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
   if (dbg_h)
     DF_HIP(hipMemcpyAsync(dbg_h, x, static_cast<size_t>(M) * D.H * 4, hipMemcpyDeviceToDevice, st));
   DF_MARK(DFLASH_SEC_LM_HEAD, -1, false);
+  if (tr) {
+    // training layout: cross-entropy partials on the weight-streaming GEMM,
+    // then the per-slot losses and their weighted mean
+    float4* lpart = at<float4>(ws, L.lm_off);
+    const T* W = static_cast<const T*>(h->w.lm_head);
+    EpiLMLoss<T, 1> l1{W, D.H, D.V, g.wg_lm, lpart, tr->labels, B, dbg_z};
+    EpiLMLoss<T, 2> l2{W, D.H, D.V, g.wg_lm, lpart, tr->labels, B, dbg_z};
+    EpiLMLoss<T, 4> l4{W, D.H, D.V, g.wg_lm, lpart, tr->labels, B, dbg_z};
+    EpiLMLoss<T, 8> l8{W, D.H, D.V, g.wg_lm, lpart, tr->labels, B, dbg_z};
+    const AOperand<T> A = a_single<T>(u, D.H, D.H, M);
+    DF_MARK(DFLASH_SEC_LM_GEMM, -1, false);
+    for (int m0 = 0; m0 < M; m0 += kMaxRowsPerLaunch) {
+      AOperand<T> Ai = A;
+      Ai.m0 = m0;
+      Ai.mc = M - m0 < kMaxRowsPerLaunch ? M - m0 : kMaxRowsPerLaunch;
+      const int mt = (Ai.mc + 15) / 16;
+      hipError_t e;
+      if (mt <= 1) e = launch_skinny_nw<T, 4>(Ai, D.H, g.tiles_lm, kLmTilesPerWg, 1, l1, st);
+      else if (mt <= 2) e = launch_skinny_nw<T, 4>(Ai, D.H, g.tiles_lm, kLmTilesPerWg, 1, l2, st);
+      else if (mt <= 4) e = launch_skinny_nw<T, 4>(Ai, D.H, g.tiles_lm, kLmTilesPerWg, 1, l4, st);
+      else e = launch_skinny_nw<T, 4>(Ai, D.H, g.tiles_lm, kLmTilesPerWg, 1, l8, st);
+      DF_HIP(e);
+    }
+    DF_MARK(DFLASH_SEC_LM_GEMM, -1, true);
+    DF_HIP(launch_lm_loss(lpart, g.wg_lm, M, B, tr->gamma, tr->slot_loss, tr->loss, st));
+    DF_MARK(DFLASH_SEC_LM_HEAD, -1, true);
+    return DFLASH_OK;
+  }
   {
     float2* lm_part = at<float2>(ws, L.lm_off);
     const int n_wg = g.wg_lm;
@@ -897,6 +957,46 @@ dflash_status dflash_draft_block(dflash_handle* h, dflash_kv* kv, int32_t block_
                                     dbg_logits, ws, st)
              : draft_impl<float>(h, kv, block_size, anchor_ids, draft_ids, dbg_final_hidden,
                                  dbg_logits, ws, st);
+}
+
+dflash_status dflash_train_forward(dflash_handle* h, const dflash_kv* kv, int32_t n_blocks,
+                                   int32_t block_size, const int32_t* block_seq,
+                                   const int32_t* anchor_pos, const int32_t* anchor_ids,
+                                   const int32_t* labels, float gamma, float* slot_loss,
+                                   float* loss, float* dbg_logits, void* ws, void* stream) {
+  if (!h || !block_seq || !anchor_pos || !anchor_ids || !labels || !slot_loss || !loss || !ws)
+    return DFLASH_ERR_INVALID_ARG;
+  if (block_size < 2 || block_size > DFLASH_MAX_BLOCK) return DFLASH_ERR_INVALID_ARG;
+  if (n_blocks < 1 || n_blocks > DFLASH_MAX_BATCH) return DFLASH_ERR_INVALID_ARG;
+  if (!(gamma > 0.f) || !(gamma < INFINITY)) return DFLASH_ERR_INVALID_ARG;
+  dflash_status s = check_kv(h, kv);
+  if (s != DFLASH_OK) return s;
+  const Dims D = dims(h->cfg);
+  if (D.G * block_size > 80) return DFLASH_ERR_UNSUPPORTED;
+  if (!aligned16(ws)) return DFLASH_ERR_INVALID_ARG;
+  // one chunk per (block, kv head) must stay free for the block's own keys
+  if (std::min<int64_t>(kMaxAttnChunks, attn_slots(n_blocks, D.Hkv) / (n_blocks * D.Hkv)) < 2)
+    return DFLASH_ERR_UNSUPPORTED;
+  int32_t len[DFLASH_MAX_BATCH];
+  int64_t off[DFLASH_MAX_BATCH];
+  int max_len = 0;
+  for (int i = 0; i < n_blocks; ++i) {
+    const int sq = block_seq[i];
+    if (sq < 0 || sq >= kv->batch) return DFLASH_ERR_INVALID_ARG;
+    if (anchor_pos[i] < 0 || anchor_pos[i] > kv->seq_len[sq]) return DFLASH_ERR_INVALID_ARG;
+    len[i] = anchor_pos[i];
+    off[i] = kv->seq_off[sq];
+    max_len = len[i] > max_len ? len[i] : max_len;
+  }
+  if ((max_len + 255) / 256 > kMaxAttnChunks * 64) return DFLASH_ERR_UNSUPPORTED;
+  const TrainSpec tr{n_blocks, len, off, labels, gamma, slot_loss, loss};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  dflash_kv* kvm = const_cast<dflash_kv*>(kv);   // read only: the caches and the slab table
+  return h->cfg.dtype == DFLASH_BF16
+             ? draft_impl<uint16_t>(h, kvm, block_size, anchor_ids, nullptr, nullptr, dbg_logits,
+                                    ws, st, &tr)
+             : draft_impl<float>(h, kvm, block_size, anchor_ids, nullptr, nullptr, dbg_logits, ws,
+                                 st, &tr);
 }
 
 dflash_status dflash_set_timing(dflash_handle* h, const dflash_timing_point* points, int32_t n) {

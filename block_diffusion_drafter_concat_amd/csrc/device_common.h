@@ -150,6 +150,24 @@ struct SeqTable {
   int32_t n;                  // sequences
 };
 
+// (max, sum of exp(x - max)) of a union of two value sets; an empty set has
+// max -inf.  The log-sum-exp is max + log(sum).
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  if (m2 == -INFINITY) return;
+  if (m == -INFINITY) {
+    m = m2;
+    s = s2;
+    return;
+  }
+  const float mx = fmaxf(m, m2);
+  s = s * expf(m - mx) + s2 * expf(m2 - mx);
+  m = mx;
+}
+
+// Rows of the block K/V buffer per training-layout block (a multiple of 32,
+// so the V^T reads of a 32-key step stay inside the block's rows).
+constexpr int kTrainSlab = 32;
+
 // Which sequence an input row belongs to (rows grouped by sequence).
 __device__ __forceinline__ int seq_of_row(const SeqTable& t, int row) {
   int b = 0;

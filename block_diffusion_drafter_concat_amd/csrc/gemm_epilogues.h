@@ -272,4 +272,66 @@ struct EpiLMHead {
   }
 };
 
+// Cross-entropy partials of the LM head for the training layout.  Row m is
+// slot j = m % B of block m / B; slots j >= 1 are scored against
+// labels[(m / B) * (B - 1) + j - 1] (slot 0, the anchor, is not scored).  Per
+// row, a workgroup leaves part[m][n_wg] = (max, sum of exp(z - max) over its
+// columns, the label's logit if it is one of them else -inf, 0).
+template <typename T, int MT>
+struct EpiLMLoss {
+  struct State {
+    float mx[MT], sm[MT], zl[MT];
+  };
+  const T* W;
+  int K, V;
+  int n_wg;
+  float4* part;
+  const int32_t* labels;
+  int B;
+  float* dbg;          // [rows][V] or null
+  __device__ void init(State& s) const {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) { s.mx[mt] = -INFINITY; s.sm[mt] = 0.f; s.zl[mt] = -INFINITY; }
+  }
+  __device__ void rows(int tile, int r16, const T*& w0, const T*& w1) const {
+    const int c0 = min(tile * 32 + r16, V - 1), c1 = min(tile * 32 + 16 + r16, V - 1);
+    w0 = W + static_cast<int64_t>(c0) * K;
+    w1 = W + static_cast<int64_t>(c1) * K;
+  }
+  __device__ void apply(State& s, int mt, int tile, int, int m, int i, bool valid, float v0,
+                        float v1) const {
+    const int c0 = tile * 32 + i, c1 = c0 + 16;
+    if (valid && dbg) {
+      if (c0 < V) dbg[static_cast<int64_t>(m) * V + c0] = v0;
+      if (c1 < V) dbg[static_cast<int64_t>(m) * V + c1] = v1;
+    }
+    const int j = m % B;
+    const int lab = valid && j > 0 ? labels[(m / B) * (B - 1) + j - 1] : -1;
+#pragma unroll
+    for (int q = 0; q < MT; ++q) {
+      if (q != mt) continue;
+      if (c0 < V) lse_merge(s.mx[q], s.sm[q], v0, 1.f);
+      if (c1 < V) lse_merge(s.mx[q], s.sm[q], v1, 1.f);
+      if (lab == c0) s.zl[q] = v0;
+      if (lab == c1) s.zl[q] = v1;
+    }
+  }
+  __device__ void finish(State& s, int wg, int m0, int mc) const {
+    const int t = threadIdx.x, i = t & 15, rr = t >> 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      float mx = s.mx[mt], sm = s.sm[mt], zl = s.zl[mt];
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) {
+        const float om = __shfl_xor(mx, o, 16), os = __shfl_xor(sm, o, 16);
+        zl = fmaxf(zl, __shfl_xor(zl, o, 16));
+        lse_merge(mx, sm, om, os);
+      }
+      const int m = mt * 16 + rr;
+      if (i == 0 && m < mc)
+        part[static_cast<int64_t>(m0 + m) * n_wg + wg] = make_float4(mx, sm, zl, 0.f);
+    }
+  }
+};
+
 }  // namespace dflash

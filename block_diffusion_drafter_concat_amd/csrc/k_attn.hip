@@ -84,14 +84,13 @@ __global__ __launch_bounds__(NQ * 64) void block_attn_kernel(AttnArgs p) {
   const int qt = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r16 = lane & 15, kg = lane >> 4;
   const int B = p.B, G = p.G, GB = G * B;
-  const int n_keys = p.seq.len[b] + B;
-  const int kbeg = c * p.chunk;
-  if (kbeg >= n_keys) return;
-  const int kend = min(kbeg + p.chunk, n_keys);
-  const int n_chunks_b = (n_keys + p.chunk - 1) / p.chunk;
-  const int64_t base = p.seq.off[b];
-  const T* Kg = static_cast<const T*>(p.kc) + static_cast<int64_t>(g) * p.cap * D;
-  const T* Vg = static_cast<const T*>(p.vc) + static_cast<int64_t>(g) * D * p.cap;
+  KeySpan span;
+  if (!attn_key_span(p, b, c, span)) return;
+  const int kbeg = span.kbeg, kend = span.kend, n_keys = span.n_src;
+  const int n_chunks_b = span.n_chunks;
+  const int64_t base = span.base, cap = span.cap;
+  const T* Kg = static_cast<const T*>(span.k) + static_cast<int64_t>(g) * cap * D;
+  const T* Vg = static_cast<const T*>(span.v) + static_cast<int64_t>(g) * D * cap;
   const int r = qt * 16 + r16;   // this lane's query row (MFMA column)
 
   Frag8<T> qf[DS];
@@ -124,7 +123,7 @@ __global__ __launch_bounds__(NQ * 64) void block_attn_kernel(AttnArgs p) {
     }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
-      ld_frag(vf[buf][dt], Vg + static_cast<int64_t>(dt * 16 + r16) * p.cap + base + kb + kg * 8);
+      ld_frag(vf[buf][dt], Vg + static_cast<int64_t>(dt * 16 + r16) * cap + base + kb + kg * 8);
   };
   auto step = [&](int buf, int kb) {
     if (kb + 32 > kend) {
@@ -241,15 +240,14 @@ __global__ __launch_bounds__(NQ * 64) void block_attn_lds_kernel(AttnArgs p) {
   const int t = threadIdx.x, qt = t >> 6, lane = t & 63;
   const int r16 = lane & 15, kg = lane >> 4;
   const int B = p.B, G = p.G, GB = G * B;
-  const int n_keys = p.seq.len[b] + B;
-  const int kbeg = c * p.chunk;
-  if (kbeg >= n_keys) return;
-  const int kend = min(kbeg + p.chunk, n_keys);
+  KeySpan span;
+  if (!attn_key_span(p, b, c, span)) return;
+  const int kbeg = span.kbeg, kend = span.kend, n_keys = span.n_src;
   const int n_steps = (kend - kbeg + 31) / 32;
-  const int n_chunks_b = (n_keys + p.chunk - 1) / p.chunk;
-  const int64_t base = p.seq.off[b];
-  const T* Kg = static_cast<const T*>(p.kc) + static_cast<int64_t>(g) * p.cap * D;
-  const T* Vg = static_cast<const T*>(p.vc) + static_cast<int64_t>(g) * D * p.cap;
+  const int n_chunks_b = span.n_chunks;
+  const int64_t base = span.base, cap = span.cap;
+  const T* Kg = static_cast<const T*>(span.k) + static_cast<int64_t>(g) * cap * D;
+  const T* Vg = static_cast<const T*>(span.v) + static_cast<int64_t>(g) * D * cap;
   const int r = qt * 16 + r16;   // this lane's query row (MFMA column)
 
   Frag8<T> qf[DS];
@@ -287,7 +285,7 @@ __global__ __launch_bounds__(NQ * 64) void block_attn_lds_kernel(AttnArgs p) {
         src = Kg + (base + key) * D + (i % KCH) * 8;
       } else {
         const int jj = i - 32 * KCH;
-        src = Vg + static_cast<int64_t>(jj >> 2) * p.cap + base + kb + (jj & 3) * 8;
+        src = Vg + static_cast<int64_t>(jj >> 2) * cap + base + kb + (jj & 3) * 8;
       }
       dst.v[u] = *reinterpret_cast<const u32x4*>(src);
     }
@@ -456,8 +454,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p) {
   constexpr int DT = D / 16, QR = NQ * 16;
   const int g = blockIdx.y, b = blockIdx.z;
   const int B = p.B, G = p.G, GB = G * B;
-  const int n_keys = p.seq.len[b] + B;
-  const int n_chunks_b = (n_keys + p.chunk - 1) / p.chunk;
+  const int n_chunks_b = attn_n_chunks(p, b);
   if (n_chunks_b <= 1) return;   // written directly by the attention kernel
   const int e = blockIdx.x * 256 + threadIdx.x;   // (qt, dt, lane)
   if (e >= NQ * DT * 64) return;

@@ -218,22 +218,108 @@ __global__ __launch_bounds__(256) void lm_argmax_finalize_kernel(const float2* _
   }
 }
 
+// ------------------------------------------------------------ training loss
+// Row m (slot j = m % B >= 1 of block m / B): fold the per-workgroup
+// (max, sum, label logit) partials of the LM head into the slot's
+// cross-entropy  log(sum_v exp(z_v)) - z_label  (zhichai.net, "DFlash 的架构
+// 密码", 训练策略 2: the loss of the draft slots).  Fixed fold order.
+__global__ __launch_bounds__(256) void lm_loss_finalize_kernel(const float4* __restrict__ part,
+                                                               int n_wg, int B,
+                                                               float* __restrict__ slot_loss) {
+  __shared__ float sm_m[4], sm_s[4], sm_z[4];
+  const int m = blockIdx.x, j = m % B;
+  if (j == 0) return;
+  float mx = -INFINITY, sm = 0.f, zl = -INFINITY;
+  const float4* pr = part + static_cast<int64_t>(m) * n_wg;
+  constexpr int kU = 8;
+  for (int w0 = threadIdx.x; w0 < n_wg; w0 += 256 * kU) {
+    float4 q[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int w = w0 + u * 256;
+      q[u] = w < n_wg ? pr[w] : make_float4(-INFINITY, 0.f, -INFINITY, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      lse_merge(mx, sm, q[u].x, q[u].y);
+      zl = fmaxf(zl, q[u].z);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float om = __shfl_xor(mx, o, 64), os = __shfl_xor(sm, o, 64);
+    zl = fmaxf(zl, __shfl_xor(zl, o, 64));
+    lse_merge(mx, sm, om, os);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    sm_m[threadIdx.x >> 6] = mx;
+    sm_s[threadIdx.x >> 6] = sm;
+    sm_z[threadIdx.x >> 6] = zl;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w) {
+      lse_merge(mx, sm, sm_m[w], sm_s[w]);
+      zl = fmaxf(zl, sm_z[w]);
+    }
+    slot_loss[(m / B) * (B - 1) + (j - 1)] = mx + logf(sm) - zl;
+  }
+}
+
+// loss = sum w_j * slot_loss / sum w_j over every scored slot of n_blocks
+// blocks, w_j = exp(-(j-1)/gamma) for slot j = 1..B-1 (zhichai.net, "DFlash
+// 的架构密码", 训练策略 2: earlier slots weigh more).  One workgroup, fixed
+// order.
+__global__ __launch_bounds__(256) void loss_reduce_kernel(const float* __restrict__ slot_loss,
+                                                          int n, int B, float inv_gamma,
+                                                          float* __restrict__ loss) {
+  __shared__ float sa[4], sb[4];
+  float a = 0.f, wsum = 0.f;
+  for (int e = threadIdx.x; e < n * (B - 1); e += 256) {
+    const int k = e % (B - 1);   // slot j = k + 1
+    const float w = expf(-static_cast<float>(k) * inv_gamma);
+    a += w * slot_loss[e];
+    wsum += w;
+  }
+  a = wave_sum(a);
+  wsum = wave_sum(wsum);
+  if ((threadIdx.x & 63) == 0) {
+    sa[threadIdx.x >> 6] = a;
+    sb[threadIdx.x >> 6] = wsum;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) loss[0] = ((sa[0] + sa[1]) + (sa[2] + sa[3])) / ((sb[0] + sb[1]) + (sb[2] + sb[3]));
+}
+
+hipError_t launch_lm_loss(const float4* part, int n_wg, int rows, int B, float gamma,
+                          float* slot_loss, float* loss, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  lm_loss_finalize_kernel<<<rows, 256, 0, st>>>(part, n_wg, B, slot_loss);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  loss_reduce_kernel<<<1, 256, 0, st>>>(slot_loss, rows / B, B, 1.0f / gamma, loss);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------ QKV finish
 // Block row m = b * B + j of a batch whose QKV projection left ks fp32
 // partial slabs [ks][M][qd + 2 kvd]: sum the slabs, rotate q and k at the
 // block position len[b] + j (pairs (c, c + d/2) of a head), store q to its
 // buffer and k, v to the layer's cache at row off[b] + len[b] + j (V
-// transposed).  grid.x runs over rows; the grid.y workgroups of a row split
-// its columns (few rows still spread over the GPU).
+// transposed; with block_rows, to rows b * kTrainSlab + j of a training
+// layout's block buffer instead).  grid.x runs over rows; the grid.y
+// workgroups of a row split its columns (few rows still spread over the GPU).
 template <typename T>
 __global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict__ part, int ks,
                                                          int64_t slab, int qd, int kvd, int d,
                                                          int B, T* __restrict__ q, int64_t ldq,
                                                          T* __restrict__ kc, T* __restrict__ vc,
-                                                         int64_t cap, RopeFreq freq, SeqTable seq) {
+                                                         int64_t cap, RopeFreq freq, SeqTable seq,
+                                                         bool block_rows) {
   const int m = blockIdx.x, b = m / B, j = m % B;
   const int pos = seq.len[b] + j;
-  const int64_t row = seq.off[b] + pos;
+  // training layout: the block's K/V go to its own rows of the block buffer
+  const int64_t row = block_rows ? static_cast<int64_t>(b) * kTrainSlab + j : seq.off[b] + pos;
   const int nq = qd + 2 * kvd, half = d / 2;
   const float* pr = part + static_cast<int64_t>(m) * nq;
   // flat work index: rotation pairs of the q and k columns, then v columns;
@@ -265,7 +351,7 @@ __global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict
 hipError_t launch_qkv_finish(bool bf16, const float* part, int ks, int64_t slab, int rows, int qd,
                              int kvd, int d, int B, void* q, int64_t ldq, void* kc, void* vc,
                              int64_t cap, const RopeFreq& freq, const SeqTable& seq,
-                             hipStream_t st) {
+                             hipStream_t st, bool block_rows) {
   if (rows <= 0) return hipSuccess;
   // enough workgroups to cover the GPU when rows are few
   const int total = (qd + kvd) / 2 + kvd;
@@ -273,12 +359,13 @@ hipError_t launch_qkv_finish(bool bf16, const float* part, int ks, int64_t slab,
   if (bf16)
     qkv_finish_kernel<uint16_t><<<grid, 256, 0, st>>>(
         part, ks, slab, qd, kvd, d, B, static_cast<uint16_t*>(q), ldq,
-        static_cast<uint16_t*>(kc), static_cast<uint16_t*>(vc), cap, freq, seq);
+        static_cast<uint16_t*>(kc), static_cast<uint16_t*>(vc), cap, freq, seq, block_rows);
   else
     qkv_finish_kernel<float><<<grid, 256, 0, st>>>(part, ks, slab, qd, kvd, d, B,
                                                    static_cast<float*>(q), ldq,
                                                    static_cast<float*>(kc),
-                                                   static_cast<float*>(vc), cap, freq, seq);
+                                                   static_cast<float*>(vc), cap, freq, seq,
+                                                   block_rows);
   return hipGetLastError();
 }
 

@@ -24,11 +24,19 @@ hipError_t launch_resid_rmsnorm(bool bf16, float* x, const float* part, int n_sp
 
 // QKV of a batch of blocks from ks fp32 partial slabs [ks][rows][qd + 2 kvd]
 // (slab = rows * (qd + 2 kvd)): sum, RoPE on q and k at the block positions,
-// q -> q[rows][ldq], k -> K cache rows, v -> transposed V cache.
+// q -> q[rows][ldq], k -> K cache rows, v -> transposed V cache (block_rows:
+// rows b * kTrainSlab + j of a training layout's block K/V buffer instead,
+// kc / vc / cap then naming that buffer).
 hipError_t launch_qkv_finish(bool bf16, const float* part, int ks, int64_t slab, int rows, int qd,
                              int kvd, int d, int B, void* q, int64_t ldq, void* kc, void* vc,
                              int64_t cap, const RopeFreq& freq, const SeqTable& seq,
-                             hipStream_t st);
+                             hipStream_t st, bool block_rows = false);
+
+// Training layout: per-slot cross-entropy from the LM head's (max, sum,
+// label logit) partials [rows][n_wg], then the weighted mean over all slots
+// (rows = n_blocks * B; slot 0 of a block is not scored).
+hipError_t launch_lm_loss(const float4* part, int n_wg, int rows, int B, float gamma,
+                          float* slot_loss, float* loss, hipStream_t st);
 
 // Draft ids from the LM head's per-workgroup (value, index) partials [rows][n_wg].
 hipError_t launch_lm_argmax_finalize(const float2* part, int n_wg, int rows, int B, int32_t* draft,

@@ -26,7 +26,7 @@ F32, BF16 = 0, 1
 EXPORTS = ("dflash_target_layer_ids", "dflash_create", "dflash_destroy",
            "dflash_workspace_size", "dflash_fuse_context", "dflash_inject_kv",
            "dflash_draft_block", "dflash_verify_greedy", "dflash_verify_workspace_size",
-           "dflash_set_timing", "dflash_status_string")
+           "dflash_train_forward", "dflash_set_timing", "dflash_status_string")
 
 # dflash_section
 SECTIONS = {"fuse_gemm": 1, "fuse_norm": 2, "inject": 3, "embed": 4, "attn_norm": 5, "qkv": 6,
@@ -102,6 +102,9 @@ def load() -> C.CDLL:
     lib.dflash_verify_greedy.restype = C.c_int
     lib.dflash_verify_workspace_size.argtypes = [i32, i32, i32]
     lib.dflash_verify_workspace_size.restype = C.c_size_t
+    lib.dflash_train_forward.argtypes = [vp, C.POINTER(KV), i32, i32, pi32, pi32, vp, vp,
+                                         C.c_float, vp, vp, vp, vp, vp]
+    lib.dflash_train_forward.restype = C.c_int
     lib.dflash_set_timing.argtypes = [vp, C.POINTER(TimingPoint), i32]
     lib.dflash_set_timing.restype = C.c_int
     lib.dflash_status_string.argtypes = [C.c_int]
@@ -238,6 +241,21 @@ class Drafter:
                                            _ptr(anchors), _ptr(draft_ids), _ptr(dbg_hidden),
                                            _ptr(dbg_logits), _ptr(ws), _stream(stream)),
                "dflash_draft_block")
+
+
+    def train_forward(self, cache: "KVCache", block_size: int, block_seq, anchor_pos, anchor_ids,
+                      labels, gamma: float, slot_loss, loss, ws, dbg_logits=None,
+                      stream=None) -> None:
+        """Training-layout forward: block i of sequence block_seq[i] at anchor
+        anchor_pos[i] (host int sequences); anchor_ids int32 [n], labels int32
+        [n, B-1], slot_loss float32 [n, B-1], loss float32 [1] (device)."""
+        bs = np.ascontiguousarray(block_seq, dtype=np.int32)
+        ap = np.ascontiguousarray(anchor_pos, dtype=np.int32)
+        _check(self.lib.dflash_train_forward(
+            self.handle, C.byref(cache.c), len(bs), block_size,
+            bs.ctypes.data_as(C.POINTER(C.c_int32)), ap.ctypes.data_as(C.POINTER(C.c_int32)),
+            _ptr(anchor_ids), _ptr(labels), float(gamma), _ptr(slot_loss), _ptr(loss),
+            _ptr(dbg_logits), _ptr(ws), _stream(stream)), "dflash_train_forward")
 
 
 def verify_greedy(target_logits, draft_ids, accept, bonus, ws, stream=None) -> None:

@@ -19,6 +19,11 @@
  *                         and bonus token (same page, 训练策略 1; ai-stack.site,
  *                         "DFlash：基于块扩散的闪存推测解码方法", 实践 2).
  *
+ * and, for the training layout, dflash_train_forward: several blocks per
+ * sequence at sampled anchors, each seeing only the context before its
+ * anchor, scored with the position-decayed cross-entropy (same page, 训练策略
+ * 1 and 2).
+ *
  * Conventions shared by every call
  *   - Pointers marked (device) are HIP device memory; (host) is host memory.
  *     All buffers belong to the caller.  The library never allocates device
@@ -200,6 +205,35 @@ dflash_status dflash_verify_greedy(const void *target_logits, dflash_dtype dtype
                                    int32_t vocab, int32_t *accept, int32_t *bonus, void *ws,
                                    void *stream);
 size_t dflash_verify_workspace_size(int32_t batch, int32_t block_size, int32_t vocab);
+
+/* Training-layout forward and its position-weighted loss.  Block i belongs to
+ * sequence block_seq[i] of kv and starts at anchor position a = anchor_pos[i]
+ * (0 <= a <= seq_len): slot 0 holds anchor_ids[i] (the token at a), slots
+ * 1..B-1 the mask token, slot j sits at position a + j.  The block sees the
+ * first a context rows of its sequence's cache and its own B slots, nothing
+ * else -- several blocks share one sequence's cache, and the cache is only
+ * read (the blocks' own K/V live in the workspace).  Slot j >= 1 is scored
+ * by cross-entropy against labels[i][j-1] (the token at a + j):
+ * slot_loss[i][j-1] = log(sum_v exp(z_v)) - z_label, and
+ * loss[0] = sum w_j slot_loss / sum w_j with w_j = exp(-(j-1)/gamma).
+ * zhichai.net, "DFlash 的架构密码", 训练策略 1 (blocks start at randomly
+ * sampled anchor tokens), 训练策略 2 (exponentially decaying weights over the
+ * block), 技术细节补充 / 稀疏注意力训练 (bidirectional inside a block, no flow
+ * between blocks).
+ *   block_seq, anchor_pos: host int32 [n_blocks]; anchor_ids: device int32
+ *   [n_blocks]; labels: device int32 [n_blocks][B-1], each in [0, vocab);
+ *   slot_loss: device float32 [n_blocks][B-1]; loss: device float32 [1];
+ *   dbg_logits: optional device float32 [n_blocks * B][vocab].
+ * n_blocks 1..DFLASH_MAX_BATCH, B 2..DFLASH_MAX_BLOCK, gamma > 0 and finite;
+ * ws from dflash_workspace_size(h, >= n_blocks, >= B, ...).  The caller owns
+ * every buffer; nothing is allocated.  Argument errors return before anything
+ * is enqueued; labels out of range give an undefined loss (not checked on the
+ * device). */
+dflash_status dflash_train_forward(dflash_handle *h, const dflash_kv *kv, int32_t n_blocks,
+                                   int32_t block_size, const int32_t *block_seq,
+                                   const int32_t *anchor_pos, const int32_t *anchor_ids,
+                                   const int32_t *labels, float gamma, float *slot_loss,
+                                   float *loss, float *dbg_logits, void *ws, void *stream);
 
 /* Timing hook for profiling.  Sections of the launch sequence: */
 typedef enum {

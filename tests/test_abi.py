@@ -194,3 +194,32 @@ def test_set_timing_host_checks():
     assert lib.dflash_set_timing(h, None, 33) == L.ERR_INVALID_ARG
     assert lib.dflash_set_timing(h, None, 0) == L.OK
     assert lib.dflash_destroy(h) == L.OK
+
+
+def test_train_forward_host_checks():
+    """Every rejected training-layout call returns before anything is enqueued
+    (the device pointers here are fake)."""
+    lib = L.load()
+    shape = configs.TINY_F32
+    st, h, keep = _create(shape)
+    assert st == L.OK
+    p = C.c_void_p(_FAKE)
+    kv, k1 = _kv(shape, [40, 7], [64, 32])
+
+    def call(n=2, B=8, seq=(0, 1), anc=(40, 0), gamma=4.0, ids=p, labels=p, sl=p, loss=p,
+             ws=p, kvp=None):
+        bs = (C.c_int32 * max(1, len(seq)))(*seq)
+        ap = (C.c_int32 * max(1, len(anc)))(*anc)
+        return lib.dflash_train_forward(h, C.byref(kv) if kvp is None else kvp, n, B, bs, ap,
+                                        ids, labels, gamma, sl, loss, None, ws, None)
+
+    for kw in (dict(n=0), dict(n=65), dict(B=1), dict(B=17), dict(seq=(0, 2)), dict(seq=(-1, 0)),
+               dict(anc=(41, 0)), dict(anc=(0, 8)), dict(anc=(-1, 0)), dict(gamma=0.0),
+               dict(gamma=-1.0), dict(gamma=float("inf")), dict(gamma=float("nan")),
+               dict(ids=None), dict(labels=None), dict(sl=None), dict(loss=None), dict(ws=None),
+               dict(ws=C.c_void_p(_FAKE + 8))):
+        assert call(**kw) == L.ERR_INVALID_ARG, kw
+    assert lib.dflash_train_forward(h, None, 2, 8, (C.c_int32 * 2)(0, 1), (C.c_int32 * 2)(0, 0),
+                                    p, p, 4.0, p, p, None, p, None) == L.ERR_INVALID_ARG
+    assert k1[4][0] == 40 and k1[4][1] == 7   # the caches' lengths are only read
+    assert lib.dflash_destroy(h) == L.OK
