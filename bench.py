@@ -315,6 +315,46 @@ def workload_batch16(torch, L, configs, synth, dr, shape, reps: int) -> dict:
     return out
 
 
+def workload_training(torch, L, configs, dr, shape, reps: int) -> dict:
+    """Training layout: 4 sequences of context 2048 sharing nothing, 16 blocks
+    of 16 slots each at sampled anchors (64 blocks, 1024 block rows); one
+    dflash_train_forward call = the forward of every block and the weighted
+    cross-entropy of its 15 draft slots (gamma = 4)."""
+    lens, per_seq, B, gamma = [CTX] * 4, 16, BLOCK, 4.0
+    cache = L.KVCache(shape, [n + 64 for n in lens])
+    fill_cache(torch, cache, lens, 5001)
+    tokens, bseq, apos = configs.make_training_layout(shape, 5001, lens, per_seq, B)
+    n = len(bseq)
+    anchor_ids = torch.tensor([int(tokens[s][a]) for s, a in zip(bseq, apos)], dtype=torch.int32,
+                              device="cuda")
+    labels = torch.from_numpy(np.stack([tokens[s][a + 1:a + B] for s, a in zip(bseq, apos)])
+                              .astype(np.int32)).cuda()
+    ws = dr.workspace(n, B, 1)
+    slot = torch.empty((n, B - 1), dtype=torch.float32, device="cuda")
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    fn = lambda: dr.train_forward(cache, B, bseq, apos, anchor_ids, labels, gamma, slot, loss, ws)
+    ms = event_time_ms(torch, fn, reps)
+    kern = section_times(torch, dr, fn, layer_sections(shape.n_layers), max(3, reps // 4))
+    M, H, F, V = n * B, shape.hidden, shape.ffn, shape.vocab
+    qd, kvd = shape.q_dim, shape.kv_dim
+    flops = {"qkv": 2.0 * M * (qd + 2 * kvd) * H, "o_proj": 2.0 * M * H * qd,
+             "gate_up": 2.0 * M * 2 * F * H, "down": 2.0 * M * H * F, "lm_gemm": 2.0 * M * V * H}
+    kernels = {}
+    for k, v in kern.items():
+        e = {"avg_us": round(v * 1e3, 2)}
+        if k in flops:
+            tf = flops[k] / (v * 1e-3) / 1e12
+            e.update({"TFLOP/s": round(tf, 1), "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)})
+        kernels[k] = e
+    out = {"workload": "qwen3-8b-shaped training layout: 4 x ctx 2048, 16 blocks/seq of 16 slots",
+           "blocks": n, "block_rows": M, "train_forward_ms": round(ms, 4),
+           "blocks_per_s": round(n / (ms * 1e-3), 1),
+           "scored_tokens_per_s": round(n * (B - 1) / (ms * 1e-3), 1),
+           "loss": round(float(loss.item()), 5), "kernels": kernels}
+    del cache
+    return out
+
+
 def workload_long(torch, L, configs, dr, shape, repeats: int = 3) -> dict:
     """Batch 1: one 32768-token prefill (fuse + inject), then 256 steps that
     each append n ~ U{1..16} fresh feature rows and draft a 16-slot block."""
@@ -631,6 +671,9 @@ def main():
         t1 = time.time()
         workloads["long_ctx_incremental"] = workload_long(torch, L, configs, dr, shape)
         log(f"long-context loop done ({time.time() - t1:.1f}s)")
+        t1 = time.time()
+        workloads["training_layout"] = workload_training(torch, L, configs, dr, shape, 10)
+        log(f"training layout done ({time.time() - t1:.1f}s)")
         dr.close()
         del dr
         torch.cuda.empty_cache()

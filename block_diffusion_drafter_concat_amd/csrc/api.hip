@@ -746,8 +746,9 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
     DF_HIP(hipMemcpyAsync(dbg_h, x, static_cast<size_t>(M) * D.H * 4, hipMemcpyDeviceToDevice, st));
   DF_MARK(DFLASH_SEC_LM_HEAD, -1, false);
   if (tr) {
-    // training layout: cross-entropy partials on the weight-streaming GEMM,
-    // then the per-slot losses and their weighted mean
+    // training layout: cross-entropy partials (tiled GEMM for many block
+    // rows, else the weight-streaming one), then the per-slot losses and
+    // their weighted mean
     float4* lpart = at<float4>(ws, L.lm_off);
     const T* W = static_cast<const T*>(h->w.lm_head);
     EpiLMLoss<T, 1> l1{W, D.H, D.V, g.wg_lm, lpart, tr->labels, B, dbg_z};
@@ -755,8 +756,16 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
     EpiLMLoss<T, 4> l4{W, D.H, D.V, g.wg_lm, lpart, tr->labels, B, dbg_z};
     EpiLMLoss<T, 8> l8{W, D.H, D.V, g.wg_lm, lpart, tr->labels, B, dbg_z};
     const AOperand<T> A = a_single<T>(u, D.H, D.H, M);
+    int n_parts = g.wg_lm;
     DF_MARK(DFLASH_SEC_LM_GEMM, -1, false);
-    for (int m0 = 0; m0 < M; m0 += kMaxRowsPerLaunch) {
+    if (mid) {
+      // many block rows: the LDS-tiled GEMM, 256 vocabulary rows per tile
+      n_parts = (D.V + 255) / 256;
+      TEpiLoss e{static_cast<const uint16_t*>(h->w.lm_head), D.H, D.V, n_parts, B, lpart,
+                 tr->labels, dbg_z};
+      DF_HIP(launch_mid<256>(a16(u, D.H), D.V, D.H, 1, e, st));
+    }
+    for (int m0 = 0; !mid && m0 < M; m0 += kMaxRowsPerLaunch) {
       AOperand<T> Ai = A;
       Ai.m0 = m0;
       Ai.mc = M - m0 < kMaxRowsPerLaunch ? M - m0 : kMaxRowsPerLaunch;
@@ -769,7 +778,7 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
       DF_HIP(e);
     }
     DF_MARK(DFLASH_SEC_LM_GEMM, -1, true);
-    DF_HIP(launch_lm_loss(lpart, g.wg_lm, M, B, tr->gamma, tr->slot_loss, tr->loss, st));
+    DF_HIP(launch_lm_loss(lpart, n_parts, M, B, tr->gamma, tr->slot_loss, tr->loss, st));
     DF_MARK(DFLASH_SEC_LM_HEAD, -1, true);
     return DFLASH_OK;
   }

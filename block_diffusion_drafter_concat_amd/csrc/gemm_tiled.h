@@ -447,6 +447,50 @@ struct TEpiArgmax {
   }
 };
 
+// Training-layout LM head: per row, over this tile's columns, the max logit,
+// the sum of exp(z - max) and the label's logit (or -inf) ->
+// part[m][n_parts] as float4 (max, sum, label logit, 0).  Row m is slot
+// j = m % B of block m / B; slot 0 (the anchor) has no label.
+struct TEpiLoss {
+  const uint16_t* W;
+  int K, V, n_parts, B;
+  float4* part;
+  const int32_t* labels;
+  float* dbg;   // [M][V] or null
+  __device__ WRows wrows(int, int n, int) const { return wrows_single(W, K, n, V); }
+  __device__ void store(const TiledSlice& s, void*, int t, int nt) const {
+    const int lane = t & 63, wave = t >> 6, nw = nt >> 6;
+    for (int lr = wave; lr < 64; lr += nw) {   // one wave per row
+      const int m = s.row(lr);
+      if (m >= s.M) continue;
+      const int j = m % B;
+      const int lab = j > 0 ? labels[(m / B) * (B - 1) + j - 1] : -1;
+      float mx = -INFINITY, zl = -INFINITY;
+      for (int c = lane; c < s.bn; c += 64) {
+        const int n = s.n0 + c;
+        if (n >= V) break;
+        const float v = s.at(lr, c);
+        if (dbg) dbg[static_cast<int64_t>(m) * V + n] = v;
+        mx = fmaxf(mx, v);
+        if (n == lab) zl = v;
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        zl = fmaxf(zl, __shfl_xor(zl, o, 64));
+      }
+      float sm = 0.f;
+      for (int c = lane; c < s.bn; c += 64) {
+        if (s.n0 + c >= V) break;
+        sm += expf(s.at(lr, c) - mx);
+      }
+      sm = wave_sum(sm);
+      if (lane == 0)
+        part[static_cast<int64_t>(m) * n_parts + s.tile_n] = make_float4(mx, sm, zl, 0.f);
+    }
+  }
+};
+
 // KV injection over rows of context features.  Part p = 2 * layer + (0: K,
 // 1: V); its N = Hkv * d columns are that layer's k (or v) projection.  K
 // gets RoPE at the row's position (the pair partner of column c is c + d/2);
