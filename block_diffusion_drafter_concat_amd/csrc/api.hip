@@ -44,11 +44,11 @@ inline dflash_status hip_status(hipError_t e) { return e == hipSuccess ? DFLASH_
 // Attention split: chunks per (sequence, kv head) at most kMaxAttnChunks, and
 // at most kAttnSlotBudget partial slots over the whole batch (or one chunk
 // per (sequence, kv head) if the batch is larger).  The bf16 block-attention
-// kernel fits two workgroups on a compute unit, so kAttnConcurrent (2 x 256
+// kernel fits three workgroups on a compute unit, so kAttnConcurrent (3 x 256
 // CUs) of them run at once; attn_chunk() picks the chunk length.
 constexpr int kMaxAttnChunks = 128;
 constexpr int kAttnSlotBudget = 2048;
-constexpr int kAttnConcurrent = 512;
+constexpr int kAttnConcurrent = 768;
 constexpr int kAttnWgOverhead = 64;   // fixed cost of a workgroup, in keys
 int64_t attn_slots(int batch, int n_kv) {
   const int64_t all = static_cast<int64_t>(batch) * n_kv;

@@ -4,23 +4,29 @@
 // 技术细节补充 / 稀疏注意力训练; zaocj.com news article on DFlash: bidirectional
 // attention in a single forward pass).
 //
-// The block's own K/V were written by the QKV epilogue into the cache rows
-// just past the committed context, so a sequence's visible keys are the
-// contiguous rows [0, len + B) of its slab.
+// At inference the block's own K/V were written by the QKV epilogue into the
+// cache rows just past the committed context, so a sequence's visible keys are
+// the contiguous rows [0, len + B) of its slab.  In the training layout
+// (AttnArgs::kb set) an entry's visible keys are the first len rows of its
+// sequence's slab plus its block's own rows in a separate buffer, read as one
+// extra chunk (KeySpan).
 //
-// Work split (HBM-bound over the K/V stream): workgroup = (context chunk,
-// kv-head g, sequence b) with one wave per 16-query tile; the G*B queries of
-// the kv head (G = q heads per kv head) are MFMA columns.  Every wave walks
-// the whole chunk in 32-key steps with the next step's K/V fragments in
-// flight; the waves of a workgroup read the same keys, so the repeats hit
-// L1/L2 and HBM sees each K/V byte once.  No cross-wave merge is needed.
+// Work split (HBM-bound over the K/V stream): workgroup = (key chunk, kv-head
+// g, sequence b) with one wave per 16-query tile; the G*B queries of the kv
+// head (G = q heads per kv head) are MFMA columns.
 //   S^T[keys x queries] = K[keys x d] . Q^T   (K rows permuted so that the
 //                                             C layout equals the next B layout)
-//   O^T[d x queries]   += V^T[d x keys] . P^T (V^T straight from the transposed
-//                                             V cache, 16 contiguous bytes/lane)
-// Softmax is online in fp32 (base-2 with the scale folded in).  Chunks meet in
-// the workspace in MFMA C-layout order; a merge kernel combines them in chunk
-// order.
+//   O^T[d x queries]   += V^T[d x keys] . P^T (V^T rows of the transposed V
+//                                             cache, 16 contiguous bytes/lane)
+// Softmax is online in fp32 (base-2 with the scale folded in).  float32:
+// every wave streams its fragments from global memory (repeats across waves
+// hit L1/L2).  bf16: the workgroup loads each 32-key step once into an LDS
+// ring with LDS-destination loads (block_attn_dma_kernel).  Chunks meet in
+// the workspace in MFMA C-layout order; a merge kernel combines them.
+#include <atomic>
+#include <type_traits>
+
+#include "gemm_tiled.h"   // LDS-destination load and LDS-read helpers
 #include "kernels_attn.h"
 
 namespace dflash {
@@ -204,45 +210,65 @@ __global__ __launch_bounds__(NQ * 64) void block_attn_kernel(AttnArgs p) {
   if (kg == 0) p.part_ml[slot * QR + r] = make_float2(m_run, l);
 }
 
-// bf16 variant with the K/V stream staged through LDS.  The workgroup's
-// threads load each 32-key step once (K rows and V^T rows, 16-byte chunks)
-// P steps ahead into registers, write it into one of two LDS slots, and the
-// waves read their MFMA fragments from there.  P steps of 16 KB (head dim
-// 128) per workgroup are in flight at once.  The loads go to registers and
-// the slot is published with an explicit LDS wait and a plain s_barrier: the
-// compiler's waits on the loads stay exact (a workgroup fence here would
-// also drain every prefetch in flight).
-//
-// LDS slot: K [32 keys][D] with 16-byte chunk c of key k at c ^ kswz(k), and
-// V^T [D][32 keys] with chunk c of row d at c ^ ((d >> 1) & 3): each group of
-// 8 lanes of an MFMA fragment read (8 keys or 8 d-rows at one chunk; LDS
-// serves 16-byte reads 8 lanes at a time) then hits 8 distinct bank groups.
+// LDS slot of one 32-key step: K [32 keys][D] with 16-byte chunk c of key k
+// at c ^ kswz(k), and V^T [D][32 keys] with chunk c of row d at
+// c ^ ((d >> 1) & 3): each group of 8 lanes of an MFMA fragment read (8 keys
+// or 8 d-rows at one chunk; LDS serves 16-byte reads 8 lanes at a time) then
+// hits 8 distinct bank groups.
 template <int KCH>
 __device__ __forceinline__ int kswz(int k) {
   return ((((k >> 3) & 3) << 2) | (k & 3)) & (KCH - 1);
 }
 
-template <int D, int NQ, int P>
-__global__ __launch_bounds__(NQ * 64) void block_attn_lds_kernel(AttnArgs p) {
+// bf16 variant whose K/V stream goes global -> LDS with LDS-destination buffer
+// loads (no staging registers, no LDS stores): a ring of NSLOT step slots per
+// workgroup with NSLOT - 1 steps in flight.  48 KB of ring per workgroup
+// (head dim 128: 3 slots) lets three workgroups share a CU, whose waves then
+// overlap one another's softmax and MFMA latency with the loads; measured at
+// 35K keys: 3 slots 27.8 us, 4 slots 29.1, 5 slots 30.4 (loads alone 23-24,
+// math alone 21-22).  Slot layout
+// and swizzles as above: a lane of a 1 KB load instruction
+// writes LDS chunk q = 64 i + lane of the slot, so it fetches the global chunk
+// that belongs there.  Fragment reads are instructions the compiler does not
+// track (tile_ds_read) with explicit waits, so the loads in flight are never
+// drained before an LDS read; each step: wait for this wave's loads of the
+// step, barrier (every wave's loads landed; the slot of the previous step is
+// free), refill that slot NSLOT - 1 steps ahead, compute.
+template <int D>
+constexpr int attn_dma_slots() {
+  return 49152 / (2 * 32 * D * 2) > 8 ? 8 : 49152 / (2 * 32 * D * 2);
+}
+
+__device__ __forceinline__ Frag8<uint16_t> as_frag(const u32x4_t& x) {
+  Frag8<uint16_t> f;
+  f.v = make_uint4(x.x, x.y, x.z, x.w);
+  return f;
+}
+
+template <int D, int NQ, int NSLOT>
+__global__ __launch_bounds__(NQ * 64) void block_attn_dma_kernel(AttnArgs p) {
   using T = uint16_t;
   constexpr int DS = D / 32;   // 32-wide k steps over the head dimension
   constexpr int DT = D / 16;   // 16-row tiles of O^T
   constexpr int QR = NQ * 16;  // query rows (padded)
-  constexpr int NT = NQ * 64;
-  constexpr int KCH = D / 8;                   // 16-byte chunks per K row
-  constexpr int SLOT_K = 32 * D;               // elements of the K part of a slot
-  constexpr int SLOT = 2 * 32 * D;             // K + V^T elements per slot
-  constexpr int CH = SLOT / 8;                 // 16-byte chunks per step
-  constexpr int PER = (CH + NT - 1) / NT;      // chunks per thread per step
-  __shared__ __align__(16) T lds[2 * SLOT];
+  constexpr int KCH = D / 8;                    // 16-byte chunks per K row
+  constexpr int SLOT_K = 32 * D;                // elements of the K part of a slot
+  constexpr int SLOT = 2 * 32 * D;              // K + V^T elements per slot
+  constexpr int NIK = SLOT_K * 2 / 1024;        // 1 KB load instructions: K part
+  constexpr int PERK = (NIK + NQ - 1) / NQ;     // K (and V^T) instructions per wave
+  constexpr int PERW = 2 * PERK;                // per wave (extra ones repeat the last)
+  constexpr int T2OFF = 4 * D * 2;              // bytes between the two K fragment tiles
+  static_assert(PERW * (NSLOT - 2) < 64, "vmcnt range");
+  extern __shared__ __align__(16) uint16_t lds_ring[];
 
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int t = threadIdx.x, qt = t >> 6, lane = t & 63;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), qt = wave;
   const int r16 = lane & 15, kg = lane >> 4;
   const int B = p.B, G = p.G, GB = G * B;
   KeySpan span;
   if (!attn_key_span(p, b, c, span)) return;
-  const int kbeg = span.kbeg, kend = span.kend, n_keys = span.n_src;
+  const int kbeg = span.kbeg, kend = span.kend;
   const int n_steps = (kend - kbeg + 31) / 32;
   const int n_chunks_b = span.n_chunks;
   const int64_t base = span.base, cap = span.cap;
@@ -262,49 +288,41 @@ __global__ __launch_bounds__(NQ * 64) void block_attn_lds_kernel(AttnArgs p) {
     for (int ds = 0; ds < DS; ++ds) zero_frag(qf[ds]);
   }
 
-  // chunk i of a step: K (key i / KCH, chunk i % KCH) for i < 32 KCH, else
-  // V^T (row d = j / 4, keys (j % 4) * 8 .. +8) with j = i - 32 KCH.  K rows
-  // past the sequence's keys are clamped (their scores are masked); V^T reads
-  // stay inside the sequence's slab (capacities are multiples of 32).
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  struct StepRegs {
-    u32x4 v[PER];
-  };
-  static_assert(P == 1 || P == 2 || P == 4, "prefetch depth");
-  StepRegs R0, R1, R2, R3;   // step s lives in R(s % P) (named: no stack array)
-  // Every thread issues the same PER loads at every refill (chunk indices past
-  // the step are clamped, and so is the step), so the compiler's count of
-  // loads in flight is the same on every path and its waits stay exact.
-  auto gload = [&](StepRegs& dst, int kb) {
+  // per-lane byte offsets of this wave's load instructions (step-invariant):
+  // K chunk (key k, chunk ch) sits at LDS chunk k*KCH + (ch ^ kswz(k)); V^T
+  // chunk (row d, chunk ch) at SLOT_K/8 + d*4 + (ch ^ ((d >> 1) & 3))
+  // Wave w issues K instructions w*PERK .. +PERK and the same V^T ones, so
+  // which part an instruction loads is known at compile time.
+  uint32_t voff[PERW];
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int i = min(t + u * NT, CH - 1);
-      const T* src;
-      if (i < 32 * KCH) {
-        const int key = min(kb + i / KCH, n_keys - 1);
-        src = Kg + (base + key) * D + (i % KCH) * 8;
-      } else {
-        const int jj = i - 32 * KCH;
-        src = Vg + static_cast<int64_t>(jj >> 2) * cap + base + kb + (jj & 3) * 8;
-      }
-      dst.v[u] = *reinterpret_cast<const u32x4*>(src);
-    }
-  };
-  // (a clamped chunk index rewrites the last chunk with the same data)
-  auto lstore = [&](const StepRegs& src, int slot) {
-    T* sl = lds + slot * SLOT;
+  for (int u = 0; u < PERK; ++u) {
+    const int ii = min(wave * PERK + u, NIK - 1);
+    const int q = ii * 64 + lane;
+    const int k = q / KCH, ch = (q % KCH) ^ kswz<KCH>(q / KCH);
+    voff[u] = static_cast<uint32_t>((k * D + ch * 8) * 2);
+    const int d = q >> 2, cv = (q & 3) ^ ((d >> 1) & 3);
+    voff[PERK + u] = static_cast<uint32_t>((static_cast<int64_t>(d) * cap + cv * 8) * 2);
+  }
+  const uint64_t head_bytes = static_cast<uint64_t>(cap) * D * 2;
+  // Rows past the chunk's keys (up to the step's 32) are read too: they lie
+  // inside the entry's slab (capacities are multiples of 32), their scores
+  // are masked and their V entries zeroed.
+  auto issue = [&](int st) {
+    const int kb = kbeg + 32 * min(st, n_steps - 1);   // steps past the end repeat the last
+    lds_u16* sl = (lds_u16*)(lds_ring) + (st % NSLOT) * SLOT;
+    const int soff_k = static_cast<int>((base + kb) * D * 2);
+    const int soff_v = static_cast<int>((base + kb) * 2);
+    // (the resources are locals and the offset an int: a resource temporary
+    // passed to the builtin, or an unsigned array element as its offset, makes
+    // the host pass drop the kernel's launch stub without a diagnostic)
+    const __amdgpu_buffer_rsrc_t krs = tile_rsrc(Kg, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = tile_rsrc(Vg, head_bytes);
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int i = min(t + u * NT, CH - 1);
-      int off;
-      if (i < 32 * KCH) {
-        const int k = i / KCH, ch = i % KCH;
-        off = k * D + ((ch ^ kswz<KCH>(k)) << 3);
-      } else {
-        const int jj = i - 32 * KCH, d = jj >> 2, ch = jj & 3;
-        off = SLOT_K + d * 32 + ((ch ^ ((d >> 1) & 3)) << 3);
-      }
-      *reinterpret_cast<u32x4*>(sl + off) = src.v[u];
+    for (int u = 0; u < PERK; ++u) {
+      const int ii = min(wave * PERK + u, NIK - 1);
+      const int vk = static_cast<int>(voff[u]), vv = static_cast<int>(voff[PERK + u]);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, sl + ii * 512, 16, vk, soff_k, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, sl + SLOT_K + ii * 512, 16, vv, soff_v, 0, 0);
     }
   };
 
@@ -313,31 +331,44 @@ __global__ __launch_bounds__(NQ * 64) void block_attn_lds_kernel(AttnArgs p) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = zero4();
 
-  // K fragment rows: tile t2 row rr <-> key (rr/4)*8 + t2*4 + rr%4 of the
-  // step, so the S^T C layout gives lane group kg the 8 consecutive keys
-  // kg*8 .. +8 (the V^T fragment's keys).
-  auto compute = [&](int slot, int kb) {
-    const T* sl = lds + slot * SLOT;
-    Frag8<T> kf[2][DS];
+  // Fragment addresses.  K tile t2 row rr <-> key (rr/4)*8 + t2*4 + rr%4, so
+  // the S^T C layout gives lane group kg keys kg*8 .. +8; that key's swizzle
+  // is r16 & (KCH - 1) for both tiles (tile 1 sits T2OFF bytes later).  V^T
+  // row d = dt*16 + r16 has swizzle (r16 >> 1) & 3 (tile dt 1 KB later).
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u16*)(lds_ring)));
+  const int k0 = (r16 >> 2) * 8 + (r16 & 3);
+  uint32_t koff[DS];
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      const int k = (r16 >> 2) * 8 + t2 * 4 + (r16 & 3);
+  for (int ds = 0; ds < DS; ++ds)
+    koff[ds] = lds0 + 2 * (k0 * D + (((ds * 4 + kg) ^ (r16 & (KCH - 1))) << 3));
+  const uint32_t vofs = lds0 + 2 * (SLOT_K + r16 * 32 + ((kg ^ ((r16 >> 1) & 3)) << 3));
+
+  // tail_c: std::true_type for the chunk's last step (the only one that can
+  // hold keys past kend), so full steps carry no masking code at all
+  auto compute = [&](auto tail_c, int slot, int kb) {
+    constexpr bool tail = decltype(tail_c)::value;
+    const uint32_t sb = static_cast<uint32_t>(slot * SLOT * 2);
+    u32x4_t kf0[DS], kf1[DS], vf[DT];
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds)
-        kf[t2][ds].v = *reinterpret_cast<const uint4*>(
-            sl + k * D + (((ds * 4 + kg) ^ kswz<KCH>(k)) << 3));
+    for (int ds = 0; ds < DS; ++ds) {
+      kf0[ds] = tile_ds_read<0>(koff[ds] + sb);
+      kf1[ds] = tile_ds_read<T2OFF>(koff[ds] + sb);
     }
-    const bool tail = kb + 32 > kend;   // uniform: the chunk's last, partial step
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    tile_tie_all(kf0, std::make_integer_sequence<int, DS>{});
+    tile_tie_all(kf1, std::make_integer_sequence<int, DS>{});
     f32x4 s0 = zero4(), s1 = zero4();
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
-      s0 = mfma16(s0, kf[0][ds], qf[ds]);
-      s1 = mfma16(s1, kf[1][ds], qf[ds]);
+      s0 = mfma16(s0, as_frag(kf0[ds]), qf[ds]);
+      s1 = mfma16(s1, as_frag(kf1[ds]), qf[ds]);
     }
+    // V^T fragments now: their reads overlap the softmax
+    tile_read_frags(vf, vofs + sb, std::make_integer_sequence<int, DT>{});
     float x[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = (e < 4 ? s0[e] : s1[e - 4]) * p.scale_log2;
-    if (tail) {
+    if constexpr (tail) {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (kb + kg * 8 + e >= kend) x[e] = -INFINITY;
@@ -347,36 +378,24 @@ __global__ __launch_bounds__(NQ * 64) void block_attn_lds_kernel(AttnArgs p) {
     for (int e = 0; e < 8; ++e) mx = fmaxf(mx, x[e]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // exponents are <= 0 (2^x of -inf is 0); the hardware 2^x is used as is
-    float ls = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      x[e] = __builtin_amdgcn_exp2f(x[e] - mx);
-      ls += x[e];
-    }
-    // rescale only when some query's running max moved (else alpha == 1)
-    if (__any(mx != m_run)) {
+    // Lazy rescale: the reference max m_run moves only when a row's max
+    // passes it by more than 8 (base 2), so the exponents stay <= 8 and the
+    // accumulators (in AGPRs: a rescale moves each one out and back) are
+    // touched rarely.  o and l share the reference, so o / l is unchanged.
+    if (__any(mx > m_run + 8.0f)) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - mx);
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt] = o[dt] * alpha;
+      m_run = mx;
     }
-    m_run = mx;
+    float ls = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[e] = __builtin_amdgcn_exp2f(x[e] - m_run);
+      ls += x[e];
+    }
     l_run += ls;
-    // V^T fragments, read once the K fragments are dead (fewer live registers:
-    // two waves per SIMD)
-    Frag8<T> vf[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = dt * 16 + r16;
-      vf[dt].v = *reinterpret_cast<const uint4*>(sl + SLOT_K + d * 32 +
-                                                 ((kg ^ ((d >> 1) & 3)) << 3));
-    }
-    if (tail) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) mask_tail(vf[dt], kb + kg * 8, kend);
-    }
-    // P = hi + lo in bf16 (see pack8)
     Frag8<T> pf, pl;
     pack8(pf, x);
     const uint32_t hw[4] = {pf.v.x, pf.v.y, pf.v.z, pf.v.w};
@@ -385,45 +404,37 @@ __global__ __launch_bounds__(NQ * 64) void block_attn_lds_kernel(AttnArgs p) {
     for (int e = 0; e < 8; ++e)
       lo[e] = x[e] - __uint_as_float((e & 1) ? (hw[e >> 1] & 0xffff0000u) : (hw[e >> 1] << 16));
     pack8(pl, lo);
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the V^T fragments
+    tile_tie_all(vf, std::make_integer_sequence<int, DT>{});
+    Frag8<T> v[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) v[dt] = as_frag(vf[dt]);
+    if constexpr (tail) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) mask_tail(v[dt], kb + kg * 8, kend);
+    }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      o[dt] = mfma16(o[dt], vf[dt], pf);
-      o[dt] = mfma16(o[dt], vf[dt], pl);
+      o[dt] = mfma16(o[dt], v[dt], pf);
+      o[dt] = mfma16(o[dt], v[dt], pl);
     }
   };
 
-  auto step_kb = [&](int s) { return kbeg + 32 * min(s, n_steps - 1); };
-  gload(R0, step_kb(0));
-  if constexpr (P > 1) gload(R1, step_kb(1));
-  if constexpr (P > 2) {
-    gload(R2, step_kb(2));
-    gload(R3, step_kb(3));
-  }
-  // one step: publish its slot, refill its registers P steps ahead, compute
-  auto one = [&](StepRegs& rq, int s) {
-    const int kb = kbeg + 32 * s;
-    lstore(rq, s & 1);
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this thread's slot writes
-    __builtin_amdgcn_s_barrier();          // slot s & 1 complete; slot (s+1) & 1 free
-    gload(rq, step_kb(s + P));
-    compute(s & 1, kb);
+#pragma unroll
+  for (int j = 0; j < NSLOT - 1; ++j) issue(j);
+  // the query fragments (loaded before the ring) are in: only ring loads may
+  // stay in flight (else the compiler drains the whole ring before the loop)
+  // (at most 63 in the field; the query loads are older than every ring load)
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(PERW * (NSLOT - 1) > 63 ? 63 : PERW * (NSLOT - 1)));
+  auto step = [&](auto tail_c, int s) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(PERW * (NSLOT - 2)));   // this wave's loads of step s
+    __builtin_amdgcn_s_barrier();                                 // everyone's; slot of s-1 free
+    issue(s + NSLOT - 1);
+    compute(tail_c, s % NSLOT, kbeg + 32 * s);
   };
-
-  // whole groups of P steps (no branch between the refills, so the waits on
-  // each step's registers leave the later steps' loads in flight), then the
-  // last n_steps % P steps
-  int s0 = 0;
-  for (; s0 + P <= n_steps; s0 += P) {
-    one(R0, s0);
-    if constexpr (P > 1) one(R1, s0 + 1);
-    if constexpr (P > 2) {
-      one(R2, s0 + 2);
-      one(R3, s0 + 3);
-    }
-  }
-  if (s0 < n_steps) one(R0, s0);
-  if constexpr (P > 1) if (s0 + 1 < n_steps) one(R1, s0 + 1);
-  if constexpr (P > 2) if (s0 + 2 < n_steps) one(R2, s0 + 2);
+  for (int s = 0; s < n_steps - 1; ++s) step(std::false_type{}, s);
+  step(std::true_type{}, n_steps - 1);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // no load may land after the workgroup ends
 
   float l = l_run;
   l += __shfl_xor(l, 16, 64);
@@ -446,21 +457,20 @@ __global__ __launch_bounds__(NQ * 64) void block_attn_lds_kernel(AttnArgs p) {
   if (kg == 0) p.part_ml[slot * QR + r] = make_float2(m_run, l);
 }
 
-// One thread per (query tile, 16-row d tile, lane) of a (kv head, sequence):
-// o = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c over the sequence's chunks,
-// in chunk order, all loads of 8 chunks issued before they are combined.
+// Chunk merge.  Workgroup (query tile qt, 16-row d tile dt) of a (kv head,
+// sequence): lane l owns output element (query row qt*16 + l%16, d rows
+// dt*16 + (l/16)*4 .. +4); wave w folds chunks w, w + 4, w + 8, ... (8 loads
+// in flight per thread) into o = sum_c 2^(m_c - M) O_c, l = sum_c 2^(m_c - M)
+// l_c, and the four waves' folds meet in LDS in wave order (deterministic).
 template <typename T, int D, int NQ>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p) {
   constexpr int DT = D / 16, QR = NQ * 16;
-  const int g = blockIdx.y, b = blockIdx.z;
+  const int qt = blockIdx.x / DT, dt = blockIdx.x % DT, g = blockIdx.y, b = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int B = p.B, G = p.G, GB = G * B;
   const int n_chunks_b = attn_n_chunks(p, b);
   if (n_chunks_b <= 1) return;   // written directly by the attention kernel
-  const int e = blockIdx.x * 256 + threadIdx.x;   // (qt, dt, lane)
-  if (e >= NQ * DT * 64) return;
-  const int lane = e & 63, dt = (e >> 6) % DT, qt = (e >> 6) / DT;
   const int r = qt * 16 + (lane & 15);
-  if (r >= GB) return;
   const int64_t slot0 = (static_cast<int64_t>(b) * p.n_kv + g) * p.max_chunks;
   const float2* ml = p.part_ml + slot0 * QR + r;
   const float4* po = reinterpret_cast<const float4*>(p.part_o) + (slot0 * NQ + qt) * DT * 64 +
@@ -468,14 +478,15 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p) {
   constexpr int kU = 8;
   float M = -1e30f, den = 0.f;
   float num[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < n_chunks_b; c0 += kU) {
+  for (int c0 = wave; c0 < n_chunks_b; c0 += 4 * kU) {
     float2 v[kU];
     float4 w4[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const bool ok = c0 + u < n_chunks_b;
-      v[u] = ok ? ml[static_cast<int64_t>(c0 + u) * QR] : make_float2(-1e30f, 0.f);
-      w4[u] = ok ? po[static_cast<int64_t>(c0 + u) * NQ * DT * 64] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int c = c0 + 4 * u;
+      const bool ok = c < n_chunks_b;
+      v[u] = ok ? ml[static_cast<int64_t>(c) * QR] : make_float2(-1e30f, 0.f);
+      w4[u] = ok ? po[static_cast<int64_t>(c) * NQ * DT * 64] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     float Mn = M;
 #pragma unroll
@@ -495,29 +506,50 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs p) {
     }
     M = Mn;
   }
-  const float inv = 1.0f / den;
-  const float out[4] = {num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv};
+  __shared__ float sm[4][64][6];
+  float* mine = sm[wave][lane];
+  mine[0] = M;
+  mine[1] = den;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) mine[2 + jj] = num[jj];
+  __syncthreads();
+  if (wave != 0 || r >= GB) return;
+  float Mt = sm[0][lane][0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) Mt = fmaxf(Mt, sm[w][lane][0]);
+  float dn = 0.f, nm[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float a = exp2f(sm[w][lane][0] - Mt);
+    dn += a * sm[w][lane][1];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) nm[jj] += a * sm[w][lane][2 + jj];
+  }
+  const float inv = 1.0f / dn;
+  const float out[4] = {nm[0] * inv, nm[1] * inv, nm[2] * inv, nm[3] * inv};
   store_out4<T>(p, b, g, r, dt * 16 + (lane >> 4) * 4, out);
-}
-
-// 32-key steps in flight per workgroup (bf16): at most 8 staged 16-byte
-// chunks per thread (32 VGPRs), so that two waves fit on a SIMD; narrower
-// workgroups prefetch fewer steps.
-template <int D, int NQ>
-constexpr int attn_prefetch() {
-  constexpr int per = (2 * 32 * D / 8 + NQ * 64 - 1) / (NQ * 64);
-  return 8 / per < 1 ? 1 : (8 / per > 4 ? 4 : 8 / per);
 }
 
 template <typename T, int D, int NQ>
 static hipError_t launch_attn_nq(const AttnArgs& a, dim3 grid, int batch, hipStream_t st) {
-  if constexpr (sizeof(T) == 2)
-    block_attn_lds_kernel<D, NQ, attn_prefetch<D, NQ>()><<<grid, NQ * 64, 0, st>>>(a);
-  else
+  if constexpr (sizeof(T) == 2) {
+    constexpr int NS = attn_dma_slots<D>();
+    constexpr int lds = NS * 2 * 32 * D * 2;
+    auto kern = &block_attn_dma_kernel<D, NQ, NS>;
+    static std::atomic<bool> attr_set{false};
+    if (!attr_set.load()) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      if (e != hipSuccess) return e;
+      attr_set.store(true);
+    }
+    kern<<<grid, NQ * 64, lds, st>>>(a);
+  } else {
     block_attn_kernel<T, D, NQ><<<grid, NQ * 64, 0, st>>>(a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_chunks <= 1) return e;
-  dim3 mgrid((NQ * (D / 16) * 64 + 255) / 256, a.n_kv, batch);
+  dim3 mgrid(NQ * (D / 16), a.n_kv, batch);
   attn_merge_kernel<T, D, NQ><<<mgrid, 256, 0, st>>>(a);
   return hipGetLastError();
 }
