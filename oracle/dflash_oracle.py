@@ -42,6 +42,16 @@ Readings of points the pages leave open (each repeated where it is used):
   R9 loss weights: the k-th predicted slot (k = j = 1..B-1) weighs
      exp(-(k-1)/gamma); the loss is the weighted mean over every scored slot
      of every block, sum(w * ce) / sum(w).
+  R10 stochastic drafting and verification (the pages: candidates are
+     accepted or rejected by the target's distribution and a rejection is
+     resampled, so the output distribution is the target's; the rule itself is
+     the textbook one the pages point to): drafter and target distributions
+     are softmax(logits / T) at one temperature T > 0; draft j (slot j >= 1)
+     is drawn by the Gumbel-max rule from caller uniforms; draft k (slot k+1)
+     is accepted while r_k * p_{k+1}(x) < q_k(x); at the first rejection a the
+     next token is drawn from (q_a - p_{a+1})_+ by inverse CDF with a caller
+     uniform u (smallest index whose cumulative weight exceeds u * total);
+     after B-1 acceptances it is drawn from q_{B-1} the same way.
 """
 from __future__ import annotations
 
@@ -374,3 +384,57 @@ def train_forward(weights, shape, caches, block_seq, anchor_pos, tokens, block_s
     w = loss_weights(B, gamma)[None, :] * np.ones_like(slot_loss)
     loss = float((w * slot_loss).sum() / w.sum())
     return {"logits": logits, "slot_loss": slot_loss, "loss": loss, "labels": labels}
+
+
+# ------------------------------------------- (N3) stochastic draft and verify
+
+def softmax_t(z, temperature: float) -> np.ndarray:
+    """softmax(z / T) over the last axis, float64."""
+    x = _f64(z) / float(temperature)
+    x = x - x.max(axis=-1, keepdims=True)
+    e = np.exp(x)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def gumbel_sample(logits, temperature: float, uniforms) -> np.ndarray:
+    """A draw from softmax(logits / T) per row by the Gumbel-max rule:
+    argmax_v (z_v / T - log(-log u_v)) with u_v uniform on (0, 1); ties to the
+    lowest index (reading R10)."""
+    g = -np.log(-np.log(_f64(uniforms)))
+    return argmax_lowest(_f64(logits) / float(temperature) + g, axis=-1).astype(np.int32)
+
+
+def sample_inverse_cdf(w, u: float) -> int:
+    """Smallest index whose cumulative weight exceeds u * sum(w) (u in [0, 1))."""
+    c = np.cumsum(_f64(w))
+    return int(np.searchsorted(c, float(u) * c[-1], side="right"))
+
+
+def verify_stochastic(target_logits, draft_logits, drafts, temperature: float, r, u) -> tuple:
+    """Speculative sampling over one block per sequence (reading R10).
+
+    target_logits [N, B, V]: row j is the target's distribution q_j of the
+    token after slot j; draft_logits [N, B, V]: slot j >= 1 proposed drafts[j-1]
+    from p_j; r [N, B-1], u [N]: caller uniforms.  Draft k is kept while
+    r_k * p_{k+1}(x_k) < q_k(x_k); the first rejected position a gets a fresh
+    token from (q_a - p_{a+1})_+, and a fully accepted block a bonus from
+    q_{B-1}.  Returns (accept [N], next_token [N]).
+    """
+    drafts = np.asarray(drafts)
+    N, Bm1 = drafts.shape
+    q = softmax_t(target_logits, temperature)
+    p = softmax_t(draft_logits, temperature)
+    accept = np.zeros(N, dtype=np.int32)
+    nxt = np.zeros(N, dtype=np.int32)
+    for n in range(N):
+        a = 0
+        while a < Bm1:
+            x = int(drafts[n, a])
+            if float(r[n, a]) * p[n, a + 1, x] < q[n, a, x]:
+                a += 1
+            else:
+                break
+        accept[n] = a
+        w = np.maximum(q[n, a] - p[n, a + 1], 0.0) if a < Bm1 else q[n, a]
+        nxt[n] = sample_inverse_cdf(w, u[n])
+    return accept, nxt

@@ -688,3 +688,90 @@ def test_multi_block_attention_equals_dense_masked_reference():
         got = O.block_attention(qs[i], np.concatenate([ck[:a], ks[i]]),
                                 np.concatenate([cv[:a], vs[i]]))
         np.testing.assert_allclose(got, ref[i * B:(i + 1) * B], rtol=1e-10, atol=1e-12)
+
+
+# ------------------------------------------------- stochastic draft and verify
+
+def test_inverse_cdf_closed_forms():
+    assert O.sample_inverse_cdf([0, 0, 5, 0], 0.0) == 2
+    assert O.sample_inverse_cdf([0, 0, 5, 0], 0.999) == 2
+    assert O.sample_inverse_cdf([1, 0, 3], 0.0) == 0
+    assert O.sample_inverse_cdf([1, 0, 3], 0.2499) == 0
+    assert O.sample_inverse_cdf([1, 0, 3], 0.25) == 2      # boundary goes right
+    g = np.random.default_rng(41)
+    w = g.random(17)
+    us = np.sort(g.random(50))
+    idx = [O.sample_inverse_cdf(w, u) for u in us]
+    assert all(a <= b for a, b in zip(idx, idx[1:])) and 0 <= idx[0] and idx[-1] < 17
+
+
+def test_gumbel_sample_limits_and_frequencies():
+    g = np.random.default_rng(42)
+    z = g.standard_normal((3, 9)) * 3
+    u = g.random((3, 9))
+    # a vanishing temperature is the greedy argmax; equal logits pick the largest u
+    np.testing.assert_array_equal(O.gumbel_sample(z, 1e-9, u), O.argmax_lowest(z, axis=1))
+    np.testing.assert_array_equal(O.gumbel_sample(np.zeros((3, 9)), 1.0, u), np.argmax(u, axis=1))
+    # frequencies of 40000 seeded draws against softmax(z / T)
+    zz = np.array([0.3, -1.0, 1.2, 0.0, 0.7])
+    T = 0.8
+    uu = g.random((40000, 5))
+    ids = O.gumbel_sample(np.broadcast_to(zz, (40000, 5)), T, uu)
+    freq = np.bincount(ids, minlength=5) / 40000
+    assert np.abs(freq - O.softmax_t(zz, T)).max() < 0.01
+
+
+def _verify_first_token_law(q_logits, p_logits, T, K):
+    """Law of the first emitted token of a 2-slot block (one draft): the draft x
+    weighted by p(x), r and u on K-point midpoint grids."""
+    V = q_logits.shape[-1]
+    p = O.softmax_t(p_logits, T)
+    xs, rs, us = np.meshgrid(np.arange(V), (np.arange(K) + 0.5) / K, (np.arange(K) + 0.5) / K,
+                             indexing="ij")
+    n = xs.size
+    tl = np.broadcast_to(q_logits, (n, 2, V))
+    dl = np.broadcast_to(p_logits, (n, 2, V))
+    acc, nxt = O.verify_stochastic(tl, dl, xs.reshape(n, 1), T, rs.reshape(n, 1), us.reshape(n))
+    first = np.where(acc > 0, xs.reshape(n), nxt)
+    law = np.zeros(V)
+    np.add.at(law, first, p[1][xs.reshape(n)] / (K * K))
+    return law
+
+
+def test_stochastic_verify_is_lossless():
+    """The first emitted token follows the target's distribution q_0 whatever
+    the drafter's p is (grid integration over the draft, r and u)."""
+    g = np.random.default_rng(43)
+    V, T = 4, 0.9
+    for _ in range(3):
+        ql = np.stack([g.standard_normal(V) * 1.5, g.standard_normal(V)])
+        pl = np.stack([np.zeros(V), g.standard_normal(V) * 1.5])
+        law = _verify_first_token_law(ql, pl, T, 120)
+        np.testing.assert_allclose(law, O.softmax_t(ql[0], T), atol=2.5 / 120)
+
+
+def test_stochastic_verify_special_cases():
+    g = np.random.default_rng(44)
+    N, B, V = 6, 5, 11
+    tl = g.standard_normal((N, B, V)) * 2
+    # drafter equal to the target (slot j proposes what row j-1 predicts): all accepted,
+    # the next token comes from the last row
+    dl = np.concatenate([np.zeros((N, 1, V)), tl[:, :-1, :]], axis=1)
+    drafts = g.integers(0, V, size=(N, B - 1))
+    r = g.random((N, B - 1)) * 0.999
+    u = g.random(N)
+    acc, nxt = O.verify_stochastic(tl, dl, drafts, 1.3, r, u)
+    assert (acc == B - 1).all()
+    for n in range(N):
+        assert nxt[n] == O.sample_inverse_cdf(O.softmax_t(tl[n, -1], 1.3), u[n])
+    # vanishing temperature with greedy drafts: the greedy rule (accept length and bonus)
+    dl = g.standard_normal((N, B, V)) * 2
+    gdr = O.argmax_lowest(dl[:, 1:, :], axis=2)
+    planted = tl.copy()
+    for n in range(N):          # plant agreement for the first n % B drafts
+        for j in range(min(n % B, B - 1)):
+            planted[n, j, gdr[n, j]] = planted[n, j].max() + 1.0
+    acc, nxt = O.verify_stochastic(planted, dl, gdr, 1e-9, r, u)
+    ga, gb = O.verify_greedy(planted, gdr)
+    np.testing.assert_array_equal(acc, ga)
+    np.testing.assert_array_equal(nxt, gb)
