@@ -306,11 +306,34 @@ def workload_batch16(torch, L, configs, synth, dr, shape, reps: int) -> dict:
                       device="cuda")
     v_ms = event_time_ms(torch, lambda: L.verify_greedy(logits, draft, acc, bon, vws), reps)
     v_bytes = wl.batch * BLOCK * shape.vocab * 2
+    # sampling at a temperature: Gumbel-max drafts from the drafter's fp32
+    # logits, then speculative-sampling verification against the target's
+    z = torch.empty((M, shape.vocab), dtype=torch.float32, device="cuda")
+    dr.draft_block(cache, BLOCK, anchors, draft, ws, dbg_logits=z)
+    z3 = z.reshape(wl.batch, BLOCK, shape.vocab)
+    uni = torch.rand((wl.batch, BLOCK - 1, shape.vocab), generator=g, device="cuda").clamp_(1e-12, 1 - 1e-7)
+    r = torch.rand((wl.batch, BLOCK - 1), generator=g, device="cuda")
+    u = torch.rand((wl.batch,), generator=g, device="cuda")
+    sws = torch.empty(L.stochastic_workspace_size(wl.batch, BLOCK, shape.vocab), dtype=torch.uint8,
+                      device="cuda")
+    nxt = torch.empty(wl.batch, dtype=torch.int32, device="cuda")
+    s_ms = event_time_ms(torch, lambda: L.sample_drafts(z3, 0.8, uni, draft, sws), reps)
+    vs_ms = event_time_ms(torch, lambda: L.verify_stochastic(logits, z3, draft, 0.8, r, u, acc, nxt,
+                                                             sws), reps)
+    s_bytes = 2 * wl.batch * (BLOCK - 1) * shape.vocab * 4                    # logits + uniforms
+    vs_bytes = wl.batch * BLOCK * shape.vocab * (2 + 4)                       # target bf16 + drafter fp32
+    stochastic = {"temperature": 0.8,
+                  "sample_drafts": {"avg_us": round(s_ms * 1e3, 2), "bytes": s_bytes,
+                                    "hbm_frac": round(s_bytes / (s_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                  "verify_stochastic": {"avg_us": round(vs_ms * 1e3, 2), "bytes": vs_bytes,
+                                        "hbm_frac": round(vs_bytes / (vs_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                        "mean_accept": round(float(acc.float().mean().item()), 3)}}
     out = {"workload": wl.name, "ctx_sum": int(sum(lens)), "draft_block_ms": round(ms, 4),
            "blocks_per_s": round(wl.batch / (ms * 1e-3), 1),
            "kernels": kernel_report(shape, kern, M, sum(lens) + wl.batch * BLOCK),
            "verify": {"avg_us": round(v_ms * 1e3, 2), "bytes": v_bytes,
-                      "hbm_frac": round(v_bytes / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+                      "hbm_frac": round(v_bytes / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+           "stochastic": stochastic}
     del cache
     return out
 

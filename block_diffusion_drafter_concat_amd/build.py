@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libdflash.so")
 OBJDIR = os.path.join(HERE, "_build")
 
-SOURCES = ["api.hip", "k_small.hip", "k_attn.hip"]
+SOURCES = ["api.hip", "k_small.hip", "k_attn.hip", "k_sample.hip"]
 ARCH = os.environ.get("DFLASH_ARCH", "gfx950")
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",

@@ -1008,6 +1008,44 @@ dflash_status dflash_train_forward(dflash_handle* h, const dflash_kv* kv, int32_
                                  st, &tr);
 }
 
+size_t dflash_stochastic_workspace_size(int32_t batch, int32_t block_size, int32_t vocab) {
+  if (batch < 1 || block_size < 2 || vocab < 1) return 0;
+  return stochastic_ws_bytes(batch, block_size, vocab);
+}
+
+dflash_status dflash_sample_drafts(const float* draft_logits, int32_t batch, int32_t block_size,
+                                   int32_t vocab, float temperature, const float* uniforms,
+                                   int32_t* draft_ids, void* ws, void* stream) {
+  if (!draft_logits || !uniforms || !draft_ids || !ws) return DFLASH_ERR_INVALID_ARG;
+  if (batch < 1 || batch > 65535 || block_size < 2 || block_size > DFLASH_MAX_BLOCK || vocab < 1)
+    return DFLASH_ERR_INVALID_ARG;
+  if (!(temperature > 0.f) || !(temperature < INFINITY)) return DFLASH_ERR_INVALID_ARG;
+  if (!aligned16(draft_logits) || !aligned16(uniforms)) return DFLASH_ERR_INVALID_ARG;
+  return hip_status(launch_sample_drafts(draft_logits, batch, block_size, vocab, temperature,
+                                         uniforms, draft_ids, ws, static_cast<hipStream_t>(stream)));
+}
+
+dflash_status dflash_verify_stochastic(const void* target_logits, dflash_dtype dtype,
+                                       const float* draft_logits, const int32_t* draft_ids,
+                                       int32_t batch, int32_t block_size, int32_t vocab,
+                                       float temperature, const float* r_accept,
+                                       const float* u_sample, int32_t* accept,
+                                       int32_t* next_token, void* ws, void* stream) {
+  if (!target_logits || !draft_logits || !draft_ids || !r_accept || !u_sample || !accept ||
+      !next_token || !ws)
+    return DFLASH_ERR_INVALID_ARG;
+  if (dtype != DFLASH_F32 && dtype != DFLASH_BF16) return DFLASH_ERR_INVALID_ARG;
+  if (batch < 1 || batch > 65535 || block_size < 2 || block_size > DFLASH_MAX_BLOCK || vocab < 1)
+    return DFLASH_ERR_INVALID_ARG;
+  if (!(temperature > 0.f) || !(temperature < INFINITY)) return DFLASH_ERR_INVALID_ARG;
+  if (!aligned16(ws) || !aligned16(target_logits) || !aligned16(draft_logits))
+    return DFLASH_ERR_INVALID_ARG;
+  return hip_status(launch_verify_stochastic(target_logits, dtype == DFLASH_BF16, draft_logits,
+                                             draft_ids, batch, block_size, vocab, temperature,
+                                             r_accept, u_sample, accept, next_token, ws,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 dflash_status dflash_set_timing(dflash_handle* h, const dflash_timing_point* points, int32_t n) {
   if (!h || n < 0 || n > 32 || (n > 0 && !points)) return DFLASH_ERR_INVALID_ARG;
   for (int i = 0; i < n; ++i)

@@ -38,6 +38,19 @@ hipError_t launch_qkv_finish(bool bf16, const float* part, int ks, int64_t slab,
 hipError_t launch_lm_loss(const float4* part, int n_wg, int rows, int B, float gamma,
                           float* slot_loss, float* loss, hipStream_t st);
 
+// Stochastic drafting and verification (k_sample.hip): Gumbel-max draws of
+// slots 1..B-1 from fp32 drafter logits [N][B][V] with uniforms [N][B-1][V];
+// speculative-sampling verification of drafts [N][B-1] against target logits
+// [N][B][V] (bf16 or fp32) with accept uniforms r [N][B-1] and sampling
+// uniforms u [N].  Workspace: stochastic_ws_bytes(N, B, V).
+size_t stochastic_ws_bytes(int batch, int B, int V);
+hipError_t launch_sample_drafts(const float* logits, int batch, int B, int V, float temperature,
+                                const float* uniforms, int32_t* ids, void* ws, hipStream_t st);
+hipError_t launch_verify_stochastic(const void* target_logits, bool bf16, const float* draft_logits,
+                                    const int32_t* drafts, int batch, int B, int V,
+                                    float temperature, const float* r, const float* u,
+                                    int32_t* accept, int32_t* next_tok, void* ws, hipStream_t st);
+
 // Draft ids from the LM head's per-workgroup (value, index) partials [rows][n_wg].
 hipError_t launch_lm_argmax_finalize(const float2* part, int n_wg, int rows, int B, int32_t* draft,
                                      hipStream_t st);

@@ -26,7 +26,9 @@ F32, BF16 = 0, 1
 EXPORTS = ("dflash_target_layer_ids", "dflash_create", "dflash_destroy",
            "dflash_workspace_size", "dflash_fuse_context", "dflash_inject_kv",
            "dflash_draft_block", "dflash_verify_greedy", "dflash_verify_workspace_size",
-           "dflash_train_forward", "dflash_set_timing", "dflash_status_string")
+           "dflash_train_forward", "dflash_set_timing", "dflash_status_string",
+           "dflash_stochastic_workspace_size", "dflash_sample_drafts",
+           "dflash_verify_stochastic")
 
 # dflash_section
 SECTIONS = {"fuse_gemm": 1, "fuse_norm": 2, "inject": 3, "embed": 4, "attn_norm": 5, "qkv": 6,
@@ -105,6 +107,13 @@ def load() -> C.CDLL:
     lib.dflash_train_forward.argtypes = [vp, C.POINTER(KV), i32, i32, pi32, pi32, vp, vp,
                                          C.c_float, vp, vp, vp, vp, vp]
     lib.dflash_train_forward.restype = C.c_int
+    lib.dflash_stochastic_workspace_size.argtypes = [i32, i32, i32]
+    lib.dflash_stochastic_workspace_size.restype = C.c_size_t
+    lib.dflash_sample_drafts.argtypes = [vp, i32, i32, i32, C.c_float, vp, vp, vp, vp]
+    lib.dflash_sample_drafts.restype = C.c_int
+    lib.dflash_verify_stochastic.argtypes = [vp, C.c_int, vp, vp, i32, i32, i32, C.c_float, vp,
+                                             vp, vp, vp, vp, vp]
+    lib.dflash_verify_stochastic.restype = C.c_int
     lib.dflash_set_timing.argtypes = [vp, C.POINTER(TimingPoint), i32]
     lib.dflash_set_timing.restype = C.c_int
     lib.dflash_status_string.argtypes = [C.c_int]
@@ -270,6 +279,32 @@ def verify_greedy(target_logits, draft_ids, accept, bonus, ws, stream=None) -> N
 
 def verify_workspace_size(batch: int, block: int, vocab: int) -> int:
     return int(load().dflash_verify_workspace_size(batch, block, vocab))
+
+
+def stochastic_workspace_size(batch: int, block: int, vocab: int) -> int:
+    return int(load().dflash_stochastic_workspace_size(batch, block, vocab))
+
+
+def sample_drafts(draft_logits, temperature: float, uniforms, draft_ids, ws, stream=None) -> None:
+    """draft_logits float32 [N, B, V], uniforms float32 [N, B-1, V], draft_ids int32 [N, B-1]."""
+    N, B, V = (int(s) for s in draft_logits.shape)
+    _check(load().dflash_sample_drafts(_ptr(draft_logits), N, B, V, float(temperature),
+                                       _ptr(uniforms), _ptr(draft_ids), _ptr(ws),
+                                       _stream(stream)), "dflash_sample_drafts")
+
+
+def verify_stochastic(target_logits, draft_logits, draft_ids, temperature: float, r_accept,
+                      u_sample, accept, next_token, ws, stream=None) -> None:
+    """target_logits [N, B, V] (float32 or bfloat16), draft_logits float32 [N, B, V],
+    draft_ids int32 [N, B-1], r_accept float32 [N, B-1], u_sample float32 [N]."""
+    torch = _torch()
+    N, B, V = (int(s) for s in target_logits.shape)
+    dt = BF16 if target_logits.dtype == torch.bfloat16 else F32
+    _check(load().dflash_verify_stochastic(_ptr(target_logits), dt, _ptr(draft_logits),
+                                           _ptr(draft_ids), N, B, V, float(temperature),
+                                           _ptr(r_accept), _ptr(u_sample), _ptr(accept),
+                                           _ptr(next_token), _ptr(ws), _stream(stream)),
+           "dflash_verify_stochastic")
 
 
 class KVCache:

@@ -19,7 +19,10 @@
  *                         and bonus token (same page, 训练策略 1; ai-stack.site,
  *                         "DFlash：基于块扩散的闪存推测解码方法", 实践 2).
  *
- * and, for the training layout, dflash_train_forward: several blocks per
+ * For sampling at a temperature, dflash_sample_drafts and
+ * dflash_verify_stochastic replace the argmax and the greedy verify (same
+ * page, FAQ 4: the output keeps the target's distribution).
+ * And, for the training layout, dflash_train_forward: several blocks per
  * sequence at sampled anchors, each seeing only the context before its
  * anchor, scored with the position-decayed cross-entropy (same page, 训练策略
  * 1 and 2).
@@ -205,6 +208,45 @@ dflash_status dflash_verify_greedy(const void *target_logits, dflash_dtype dtype
                                    int32_t vocab, int32_t *accept, int32_t *bonus, void *ws,
                                    void *stream);
 size_t dflash_verify_workspace_size(int32_t batch, int32_t block_size, int32_t vocab);
+
+/* Stochastic drafting and lossless verification (speculative sampling).
+ * Both distributions are softmax(logits / T) at one temperature T > 0 (finite);
+ * every random number is a caller input, so a call is deterministic.
+ * ai-stack.site, "DFlash：基于块扩散的闪存推测解码方法", FAQ 4 and the
+ * workflow answer (candidates are accepted or rejected by the target's
+ * distribution and a rejection is resampled, so the output keeps the target's
+ * distribution); the rule is the textbook speculative-sampling one that page
+ * points to.
+ *
+ * dflash_sample_drafts: draft_ids[n][j-1] = argmax_v (z[n][j][v] / T -
+ *   log(-log u[n][j-1][v])) for slots j = 1..B-1 (a draw from softmax(z / T);
+ *   ties to the lowest index).  draft_logits: device fp32 [batch][B][vocab]
+ *   (e.g. dflash_draft_block's dbg_logits); uniforms: device fp32
+ *   [batch][B-1][vocab] in (0, 1); draft_ids: device int32 [batch][B-1].
+ * dflash_verify_stochastic: draft k (slot k+1, token x = draft_ids[n][k]) is
+ *   kept while r[n][k] * p_{k+1}(x) < q_k(x), with q_j = softmax of target row j
+ *   (the target's distribution of the token after slot j) and p_j = softmax of
+ *   drafter row j; accept[n] = drafts kept (a); next_token[n] = the smallest
+ *   column whose cumulative weight exceeds u[n] * total, the weights being
+ *   (q_a - p_{a+1})_+ after a rejection and q_{B-1} after B-1 acceptances.
+ *   target_logits: device [batch][B][vocab] in `dtype`, 16-byte aligned;
+ *   draft_logits: device fp32 [batch][B][vocab]; r_accept: device fp32
+ *   [batch][B-1] in [0, 1); u_sample: device fp32 [batch] in [0, 1);
+ *   accept, next_token: device int32 [batch].
+ * Both take ws of dflash_stochastic_workspace_size(batch, B, vocab) bytes
+ * (device, 16-byte aligned) and enqueue on `stream`; every logits and uniform
+ * buffer must be 16-byte aligned.  Argument errors return before anything is
+ * enqueued. */
+size_t dflash_stochastic_workspace_size(int32_t batch, int32_t block_size, int32_t vocab);
+dflash_status dflash_sample_drafts(const float *draft_logits, int32_t batch, int32_t block_size,
+                                   int32_t vocab, float temperature, const float *uniforms,
+                                   int32_t *draft_ids, void *ws, void *stream);
+dflash_status dflash_verify_stochastic(const void *target_logits, dflash_dtype dtype,
+                                       const float *draft_logits, const int32_t *draft_ids,
+                                       int32_t batch, int32_t block_size, int32_t vocab,
+                                       float temperature, const float *r_accept,
+                                       const float *u_sample, int32_t *accept,
+                                       int32_t *next_token, void *ws, void *stream);
 
 /* Training-layout forward and its position-weighted loss.  Block i belongs to
  * sequence block_seq[i] of kv and starts at anchor position a = anchor_pos[i]

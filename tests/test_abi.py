@@ -223,3 +223,31 @@ def test_train_forward_host_checks():
                                     p, p, 4.0, p, p, None, p, None) == L.ERR_INVALID_ARG
     assert k1[4][0] == 40 and k1[4][1] == 7   # the caches' lengths are only read
     assert lib.dflash_destroy(h) == L.OK
+
+
+def test_stochastic_host_checks():
+    lib = L.load()
+    p = C.c_void_p(_FAKE)
+    assert lib.dflash_stochastic_workspace_size(4, 8, 1000) > 0
+    assert lib.dflash_stochastic_workspace_size(0, 8, 1000) == 0
+    ok = dict(logits=p, n=2, B=8, V=100, T=0.7, u=p, ids=p, ws=p)
+
+    def sample(**kw):
+        a = dict(ok, **kw)
+        return lib.dflash_sample_drafts(a["logits"], a["n"], a["B"], a["V"], a["T"], a["u"],
+                                        a["ids"], a["ws"], None)
+    for kw in (dict(logits=None), dict(u=None), dict(ids=None), dict(ws=None), dict(n=0),
+               dict(B=1), dict(B=17), dict(V=0), dict(T=0.0), dict(T=-1.0),
+               dict(T=float("inf")), dict(T=float("nan"))):
+        assert sample(**kw) == L.ERR_INVALID_ARG, kw
+
+    def verify(dtype=0, ws=p, T=0.7, B=8, **kw):
+        ptrs = dict(t=p, d=p, ids=p, r=p, u=p, acc=p, nxt=p)
+        ptrs.update(kw)
+        return lib.dflash_verify_stochastic(ptrs["t"], dtype, ptrs["d"], ptrs["ids"], 2, B, 100, T,
+                                            ptrs["r"], ptrs["u"], ptrs["acc"], ptrs["nxt"], ws,
+                                            None)
+    for kw in (dict(t=None), dict(d=None), dict(ids=None), dict(r=None), dict(u=None),
+               dict(acc=None), dict(nxt=None), dict(ws=None), dict(dtype=5), dict(T=0.0),
+               dict(B=1), dict(ws=C.c_void_p(_FAKE + 4))):
+        assert verify(**kw) == L.ERR_INVALID_ARG, kw

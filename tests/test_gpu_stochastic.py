@@ -1,0 +1,139 @@
+"""Stochastic drafting and speculative-sampling verification on the GPU.
+
+Against the oracle on the same seeded logits and uniforms: Gumbel-max draft
+ids bit-exact wherever the oracle's top-2 noisy score gap is not within fp32
+noise (1e-4); accept lengths bit-exact wherever every accept decision has a
+margin |r p - q| above 1e-5 max(p, q); next tokens bit-exact wherever the
+sampling target u * total is farther than 1e-4 * total from a cumulative
+boundary, and otherwise a column of positive weight whose cumulative interval
+lies within that tolerance of the target.  Then the losslessness of the whole
+device path: 20000 one-draft blocks with fresh uniforms emit first tokens
+distributed as the target's softmax.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from block_diffusion_drafter_concat_amd import lib as L
+from block_diffusion_drafter_concat_amd import synth
+
+from conftest import gpu_available
+from gpu_util import dev, to_np
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch
+    L.load()
+    return torch
+
+
+def _t(torch, a, dtype=np.float32):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=dtype)).cuda()
+
+
+@pytest.mark.parametrize("N,B,V,T", [(5, 6, 3001, 0.7), (3, 16, 20011, 1.3), (7, 2, 37, 0.4)])
+def test_sample_drafts_matches_oracle(torch, N, B, V, T):
+    z = synth.values((N, B, V), "f32", 71, synth.STREAM_LOGITS, f"drf{V}", std=3.0)
+    u = synth.rng(71, synth.STREAM_LOGITS, f"gu{V}").random((N, B - 1, V))
+    u = np.clip(u, 1e-12, 1 - 1e-7).astype(np.float32)
+    ws = torch.empty(L.stochastic_workspace_size(N, B, V), dtype=torch.uint8, device="cuda")
+    ids = torch.full((N, B - 1), -1, dtype=torch.int32, device="cuda")
+    L.sample_drafts(_t(torch, z), T, _t(torch, u), ids, ws)
+    torch.cuda.synchronize()
+    got = ids.cpu().numpy()
+    want = O.gumbel_sample(z[:, 1:, :], T, u)
+    s = z[:, 1:, :].astype(np.float64) / T - np.log(-np.log(u.astype(np.float64)))
+    srt = np.sort(s, axis=2)
+    ok = (srt[:, :, -1] - srt[:, :, -2]) >= 1e-4
+    print(f"sample N={N} B={B} V={V}: exempt {int((~ok).sum())}/{ok.size}", flush=True)
+    assert ((got == want) | ~ok).all()
+    picked = np.take_along_axis(s, got[..., None].astype(np.int64), axis=2)[..., 0]
+    assert (picked >= srt[:, :, -1] - 1e-4).all()
+
+
+def _verify_case(torch, N, B, V, T, dtype, wid):
+    tl = synth.values((N, B, V), dtype, wid, synth.STREAM_LOGITS, f"vt{V}", std=2.5)
+    # drafters near the target for half the sequences (long accepted prefixes)
+    noise = synth.values((N, B, V), "f32", wid, synth.STREAM_LOGITS, f"vn{V}", std=2.5)
+    dl = noise.copy()
+    for n in range(0, N, 2):
+        dl[n, 1:] = tl[n, :-1] + 0.05 * noise[n, 1:]
+    g = synth.rng(wid, synth.STREAM_LOGITS, f"vu{V}")
+    drafts = np.stack([O.gumbel_sample(dl[n, 1:], T, np.clip(g.random((B - 1, V)), 1e-12, 1 - 1e-7))
+                       for n in range(N)]).astype(np.int32)
+    r = g.random((N, B - 1)).astype(np.float32)
+    u = g.random(N).astype(np.float32)
+    ws = torch.empty(L.stochastic_workspace_size(N, B, V), dtype=torch.uint8, device="cuda")
+    acc = torch.full((N,), -1, dtype=torch.int32, device="cuda")
+    nxt = torch.full((N,), -1, dtype=torch.int32, device="cuda")
+    print(f"verify_stochastic {dtype} N={N} B={B} V={V} T={T}", flush=True)
+    L.verify_stochastic(dev(tl, dtype), _t(torch, dl), _t(torch, drafts, np.int32), T,
+                        _t(torch, r), _t(torch, u), acc, nxt, ws)
+    torch.cuda.synchronize()
+    return tl, dl, drafts, r, u, acc.cpu().numpy(), nxt.cpu().numpy()
+
+
+@pytest.mark.parametrize("N,B,V,T,dtype", [(8, 16, 5003, 0.8, "bf16"), (8, 16, 5003, 1.1, "f32"),
+                                           (4, 8, 20011, 1.0, "bf16"), (6, 2, 37, 0.5, "f32")])
+def test_verify_stochastic_matches_oracle(torch, N, B, V, T, dtype):
+    tl, dl, drafts, r, u, acc, nxt = _verify_case(torch, N, B, V, T, dtype, 72)
+    want_a, want_n = O.verify_stochastic(tl, dl, drafts, T, r, u)
+    q = O.softmax_t(tl, T)
+    p = O.softmax_t(dl, T)
+    exempt = 0
+    for n in range(N):
+        # accept decisions up to the oracle's stopping point, with margins
+        close = False
+        for k in range(min(int(want_a[n]) + 1, B - 1)):
+            x = drafts[n, k]
+            qq, pp = q[n, k, x], p[n, k + 1, x]
+            close |= abs(r[n, k] * pp - qq) < 1e-5 * max(pp, qq)
+        if close:
+            exempt += 1
+            continue
+        assert acc[n] == want_a[n], (n, acc[n], want_a[n])
+        a = int(want_a[n])
+        w = np.maximum(q[n, a] - p[n, a + 1], 0) if a < B - 1 else q[n, a]
+        c = np.cumsum(w)
+        target = float(u[n]) * c[-1]
+        v = int(want_n[n])
+        margin = min(abs(target - (c[v - 1] if v > 0 else 0.0)), abs(c[v] - target))
+        if margin >= 1e-4 * c[-1]:
+            assert nxt[n] == v, (n, nxt[n], v)
+        else:
+            g_ = int(nxt[n])
+            lo = c[g_ - 1] if g_ > 0 else 0.0
+            assert w[g_] > 0 and lo - 1e-4 * c[-1] <= target <= c[g_] + 1e-4 * c[-1]
+    print(f"accept {acc.tolist()} exempt {exempt}/{N}", flush=True)
+
+
+def test_stochastic_path_is_lossless_on_device(torch):
+    """20000 one-draft blocks: drafts sampled on the device from p, verified on
+    the device against q; the first emitted token follows q."""
+    N, B, V, T = 20000, 2, 5, 0.9
+    g = np.random.default_rng(73)
+    ql = np.array([0.4, -1.0, 1.1, 0.0, 0.6])
+    pl = np.array([-0.5, 0.9, 0.2, 0.3, -0.8])
+    tl = np.broadcast_to(np.stack([ql, ql]), (N, B, V)).astype(np.float32)
+    dl = np.broadcast_to(np.stack([pl, pl]), (N, B, V)).astype(np.float32)
+    ws = torch.empty(L.stochastic_workspace_size(N, B, V), dtype=torch.uint8, device="cuda")
+    ids = torch.empty((N, 1), dtype=torch.int32, device="cuda")
+    uni = np.clip(g.random((N, 1, V)), 1e-12, 1 - 1e-7).astype(np.float32)
+    L.sample_drafts(_t(torch, dl), T, _t(torch, uni), ids, ws)
+    acc = torch.empty(N, dtype=torch.int32, device="cuda")
+    nxt = torch.empty(N, dtype=torch.int32, device="cuda")
+    L.verify_stochastic(_t(torch, tl), _t(torch, dl), ids, T,
+                        _t(torch, g.random((N, 1))), _t(torch, g.random(N)), acc, nxt, ws)
+    torch.cuda.synchronize()
+    a, x, t = acc.cpu().numpy(), ids.cpu().numpy()[:, 0], nxt.cpu().numpy()
+    first = np.where(a > 0, x, t)
+    freq = np.bincount(first, minlength=V) / N
+    want = O.softmax_t(ql, T)
+    print(f"first-token frequencies {np.round(freq, 4)} vs q {np.round(want, 4)}", flush=True)
+    assert np.abs(freq - want).max() < 0.015
+    # the drafter alone would have drawn from p, which differs from q
+    assert np.abs(np.bincount(x, minlength=V) / N - want).max() > 0.05
