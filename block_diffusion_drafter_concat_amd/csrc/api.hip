@@ -227,10 +227,12 @@ Layout layout(const dflash_handle* h, int max_batch, int max_block, int64_t max_
   Layout L{};
   size_t off = 0;
   L.x_off = off;    off += align_up(M * D.H * 4);
-  L.u_off = off;    off += align_up(M * D.H * es);
+  // u and h may be stored fragment-major: whole 16-row groups
+  const size_t M16 = (M + 15) / 16 * 16;
+  L.u_off = off;    off += align_up(M16 * D.H * es);
   L.q_off = off;    off += align_up(M * D.qd * es);
   L.o_off = off;    off += align_up(M * D.qd * es);
-  L.h_off = off;    off += align_up(M * D.F * es);
+  L.h_off = off;    off += align_up(M16 * D.F * es);
   // K-split partial slabs: O / down projections [ks][M][H], fusion [ks][T][H]
   size_t part = static_cast<size_t>(g.ks_o > g.ks_d ? g.ks_o : g.ks_d) * M * D.H * 4;
   const size_t pf = static_cast<size_t>(fuse_part_rows(h, static_cast<int64_t>(T))) * D.H * 4;
@@ -384,6 +386,7 @@ hipError_t run_rows(AOperand<T> A, int K, int n_tiles, int tiles_per_wg, int ksp
 template <int BM, int BN, int WM, int WN, class Epi>
 hipError_t launch_tiled_cfg(const AOperand<uint16_t>& A, int N, int K, int parts, int ksplit,
                             const Epi& epi, hipStream_t st) {
+  if (A.frag) return hipErrorInvalidValue;   // reads row-major slabs only
   auto kern = &tiled_gemm_kernel<BM, BN, WM, WN, Epi>;
   constexpr size_t lds = tiled_lds_bytes(BM, BN);
   static std::atomic<bool> attr_set{false};
@@ -426,6 +429,13 @@ AOperand<T> a_single(const void* p, int64_t lda, int K, int M) {
   A.lda = lda;
   A.slab_k = K;
   A.M = M;
+  return A;
+}
+// u / h as the drafter's own kernels store them for a weight-streaming GEMM
+template <typename T>
+AOperand<T> a_frag(const void* p, int K, int M) {
+  AOperand<T> A = a_single<T>(p, K, K, M);
+  A.frag = 1;
   return A;
 }
 
@@ -604,6 +614,9 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
   const int64_t pstride = static_cast<int64_t>(M) * D.H;   // one K-split slab
   // batches of blocks: the layer GEMMs and the LM head on the LDS-tiled GEMM
   const bool mid = bf && M >= kMidMinRows;
+  // u and h feed the weight-streaming GEMM (fragment-major) unless the
+  // LDS-tiled one takes this many rows
+  const bool frag = !mid;
   const MidPlan mp = mid_plan(D, M);
   const int ks_o = mid ? mp.ks_o : g.ks_o, ks_d = mid ? mp.ks_d : g.ks_d;
   float* qkvp = at<float>(ws, L.qkvp_off);
@@ -614,7 +627,7 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
   // block embedding fused with layer 0's attention RMSNorm
   DF_MARK(DFLASH_SEC_EMBED, -1, false);
   DF_HIP(launch_embed(bf, h->w.embed, D.H, D.V, anchors, h->cfg.mask_token_id, nb, B, x,
-                      h->layers[0].attn_norm, u, eps, st));
+                      h->layers[0].attn_norm, u, eps, st, frag));
   DF_MARK(DFLASH_SEC_EMBED, -1, true);
 
   // attention split (see attn_chunk)
@@ -653,7 +666,8 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
     // attention half: x += (down partials of the previous layer); u = RMSNorm(x)
     if (l > 0) {
       DF_MARK(DFLASH_SEC_ATTN_NORM, l, false);
-      DF_HIP(launch_resid_rmsnorm(bf, x, part, pending, pstride, w.attn_norm, u, M, D.H, eps, st));
+      DF_HIP(launch_resid_rmsnorm(bf, x, part, pending, pstride, w.attn_norm, u, M, D.H, eps, st,
+                                  frag));
       DF_MARK(DFLASH_SEC_ATTN_NORM, l, true);
     }
     DF_MARK(DFLASH_SEC_QKV, l, false);
@@ -672,7 +686,7 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
       const int nq = D.qd + 2 * D.kvd;
       EpiQKVPartF32<T> e{static_cast<const T*>(w.wq), static_cast<const T*>(w.wk),
                          static_cast<const T*>(w.wv), D.H, D.qd, D.kvd, qkvp, nq, M};
-      DF_HIP(run_rows<T>(a_single<T>(u, D.H, D.H, M), D.H, g.tiles_qkv, 1, g.ks_qkv, e, st,
+      DF_HIP(run_rows<T>(a_frag<T>(u, D.H, M), D.H, g.tiles_qkv, 1, g.ks_qkv, e, st,
                          NoPerLaunch{}));
       DF_HIP(launch_qkv_finish(bf, qkvp, g.ks_qkv, static_cast<int64_t>(M) * nq, M, D.qd,
                                D.kvd, D.d, B, qb, D.qd, kdst(l), vdst(l), dcap, freq, seq, st,
@@ -690,7 +704,7 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
       e.freq = freq;
       e.seq = seq;
       // few tiles and no K-split (the epilogue needs whole sums): 8 waves each
-      DF_HIP(run_rows<T>(a_single<T>(u, D.H, D.H, M), D.H, g.tiles_qkv, 1, 1, e, st,
+      DF_HIP(run_rows<T>(a_frag<T>(u, D.H, M), D.H, g.tiles_qkv, 1, 1, e, st,
                          NoPerLaunch{}, 8));
     }
     DF_MARK(DFLASH_SEC_QKV, l, true);
@@ -713,7 +727,7 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
     DF_MARK(DFLASH_SEC_O_PROJ, l, true);
     // feed-forward half: x += O partials; u = RMSNorm(x)
     DF_MARK(DFLASH_SEC_FFN_NORM, l, false);
-    DF_HIP(launch_resid_rmsnorm(bf, x, part, ks_o, pstride, w.ffn_norm, u, M, D.H, eps, st));
+    DF_HIP(launch_resid_rmsnorm(bf, x, part, ks_o, pstride, w.ffn_norm, u, M, D.H, eps, st, frag));
     DF_MARK(DFLASH_SEC_FFN_NORM, l, true);
     DF_MARK(DFLASH_SEC_GATE_UP, l, false);
     if (mid) {
@@ -721,9 +735,8 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
                        D.H, D.F, 128, reinterpret_cast<uint16_t*>(hb), D.F};
       DF_HIP(launch_mid<128>(a16(u, D.H), 2 * D.F, D.H, 1, e, st));
     } else {
-      EpiSwiGLU<T> e{static_cast<const T*>(w.wg), static_cast<const T*>(w.wu), D.H, hb, D.F};
-      DF_HIP(run_rows<T>(a_single<T>(u, D.H, D.H, M), D.H, g.tiles_gu, 1, 1, e, st,
-                         NoPerLaunch{}));
+      EpiSwiGLU<T> e{static_cast<const T*>(w.wg), static_cast<const T*>(w.wu), D.H, hb, D.F, 1};
+      DF_HIP(run_rows<T>(a_frag<T>(u, D.H, M), D.H, g.tiles_gu, 1, 1, e, st, NoPerLaunch{}));
     }
     DF_MARK(DFLASH_SEC_GATE_UP, l, true);
     DF_MARK(DFLASH_SEC_DOWN, l, false);
@@ -732,7 +745,7 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
       DF_HIP(launch_mid<128>(a16(hb, D.F), D.H, D.F, ks_d, e, st));
     } else {
       EpiPartialF32<T> e{static_cast<const T*>(w.wd), D.F, part, D.H, M};
-      DF_HIP(run_rows<T>(a_single<T>(hb, D.F, D.F, M), D.F, g.tiles_d, 1, g.ks_d, e, st,
+      DF_HIP(run_rows<T>(a_frag<T>(hb, D.F, M), D.F, g.tiles_d, 1, g.ks_d, e, st,
                          NoPerLaunch{}));
     }
     DF_MARK(DFLASH_SEC_DOWN, l, true);
@@ -740,7 +753,8 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
   }
   // x += down partials of the last layer; u = RMSNorm(x)
   DF_MARK(DFLASH_SEC_FINAL_NORM, -1, false);
-  DF_HIP(launch_resid_rmsnorm(bf, x, part, pending, pstride, h->w.final_norm, u, M, D.H, eps, st));
+  DF_HIP(launch_resid_rmsnorm(bf, x, part, pending, pstride, h->w.final_norm, u, M, D.H, eps, st,
+                              frag));
   DF_MARK(DFLASH_SEC_FINAL_NORM, -1, true);
   if (dbg_h)
     DF_HIP(hipMemcpyAsync(dbg_h, x, static_cast<size_t>(M) * D.H * 4, hipMemcpyDeviceToDevice, st));
@@ -755,7 +769,7 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
     EpiLMLoss<T, 2> l2{W, D.H, D.V, g.wg_lm, lpart, tr->labels, B, dbg_z};
     EpiLMLoss<T, 4> l4{W, D.H, D.V, g.wg_lm, lpart, tr->labels, B, dbg_z};
     EpiLMLoss<T, 8> l8{W, D.H, D.V, g.wg_lm, lpart, tr->labels, B, dbg_z};
-    const AOperand<T> A = a_single<T>(u, D.H, D.H, M);
+    const AOperand<T> A = a_frag<T>(u, D.H, M);
     int n_parts = g.wg_lm;
     DF_MARK(DFLASH_SEC_LM_GEMM, -1, false);
     if (mid) {
@@ -789,7 +803,7 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
     EpiLMHead<T, 2> e2{static_cast<const T*>(h->w.lm_head), D.H, D.V, g.wg_lm, lm_part, dbg_z};
     EpiLMHead<T, 4> e4{static_cast<const T*>(h->w.lm_head), D.H, D.V, g.wg_lm, lm_part, dbg_z};
     EpiLMHead<T, 8> e8{static_cast<const T*>(h->w.lm_head), D.H, D.V, g.wg_lm, lm_part, dbg_z};
-    const AOperand<T> A = a_single<T>(u, D.H, D.H, M);
+    const AOperand<T> A = a_frag<T>(u, D.H, M);
     if (mid) {
       const int n_parts = (D.V + 255) / 256;
       TEpiArgmax e{static_cast<const uint16_t*>(h->w.lm_head), D.H, D.V, n_parts, lm_part, dbg_z};

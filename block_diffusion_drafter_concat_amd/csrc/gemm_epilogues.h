@@ -70,7 +70,9 @@ struct EpiQKVPartF32 {
   __device__ void finish(State&, int, int, int) const {}
 };
 
-// SwiGLU: h[m, j] = silu(u . wg[j]) * (u . wu[j]), stored in the handle type.
+// SwiGLU: h[m, j] = silu(u . wg[j]) * (u . wu[j]), stored in the handle type,
+// row-major (row stride ldh) or fragment-major (row length ldh) for the down
+// projection's A operand.
 template <typename T>
 struct EpiSwiGLU {
   using State = NoState;
@@ -79,6 +81,7 @@ struct EpiSwiGLU {
   int K;
   T* h;
   int64_t ldh;
+  int frag;
   __device__ void init(State&) const {}
   __device__ void rows(int tile, int r16, const T*& w0, const T*& w1) const {
     w0 = wg + static_cast<int64_t>(tile * 16 + r16) * K;
@@ -88,7 +91,9 @@ struct EpiSwiGLU {
                         float u) const {
     if (!valid) return;
     const float s = g / (1.0f + expf(-g));
-    stf(h + static_cast<int64_t>(m) * ldh + tile * 16 + i, s * u);
+    const int j = tile * 16 + i;
+    stf(h + (frag ? frag_major(m, j, static_cast<int>(ldh)) : static_cast<int64_t>(m) * ldh + j),
+        s * u);
   }
   __device__ void finish(State&, int, int, int) const {}
 };

@@ -16,7 +16,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ embed,
                                                     const int32_t* __restrict__ anchors,
                                                     int mask_id, int B, float* __restrict__ x,
                                                     const T* __restrict__ gain,
-                                                    T* __restrict__ u, float eps) {
+                                                    T* __restrict__ u, float eps, int frag) {
   __shared__ float red[4];
   const int m = blockIdx.x;
   const int b = m / B, j = m % B;
@@ -42,28 +42,29 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ embed,
   __syncthreads();
   const float tot = (red[0] + red[1]) + (red[2] + red[3]);
   const float r = 1.0f / sqrtf(tot / static_cast<float>(H) + eps);
-  T* o = u + static_cast<size_t>(m) * H;
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
     const int c = (q * 256 + threadIdx.x) * 4;
     if (c < H) {
+      // four columns of one aligned run of 32: contiguous in either layout
+      T* o = u + (frag ? frag_major(m, c, H) : static_cast<int64_t>(m) * H + c);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) stf(o + c + e, v[q][e] * r * ldf(gain + c + e));
+      for (int e = 0; e < 4; ++e) stf(o + e, v[q][e] * r * ldf(gain + c + e));
     }
   }
 }
 
 hipError_t launch_embed(bool bf16, const void* embed, int H, int V, const int32_t* anchors,
                         int mask_id, int batch, int B, float* x, const void* gain, void* u,
-                        float eps, hipStream_t st) {
-  if (H > 8192 || H % 4) return hipErrorInvalidValue;
+                        float eps, hipStream_t st, bool frag) {
+  if (H > 8192 || H % 4 || (frag && H % 32)) return hipErrorInvalidValue;
   dim3 grid(batch * B), block(256);
   const int per = (H + 1023) / 1024;
 #define DF_EMB(TT, P)                                                                          \
   embed_kernel<TT, P><<<grid, block, 0, st>>>(static_cast<const TT*>(embed), H, V, anchors,    \
                                               mask_id, B, x,                                   \
                                               static_cast<const TT*>(gain), static_cast<TT*>(u), \
-                                              eps)
+                                              eps, frag ? 1 : 0)
   if (bf16) {
     if (per <= 1) DF_EMB(uint16_t, 1); else if (per <= 2) DF_EMB(uint16_t, 2);
     else if (per <= 4) DF_EMB(uint16_t, 4); else DF_EMB(uint16_t, 8);
@@ -77,7 +78,8 @@ hipError_t launch_embed(bool bf16, const void* embed, int H, int V, const int32_
 
 // ------------------------------------------------------------------ RMSNorm
 // Row m: v = x[m] (if x) + sum over splits s of part[s][m] (in split order);
-// x[m] = v (if x); out[m] = v / sqrt(mean(v^2) + eps) * g (if out).
+// x[m] = v (if x); out[m] = v / sqrt(mean(v^2) + eps) * g (if out; row-major,
+// or fragment-major for a weight-streaming GEMM that reads it next).
 // The split-K partials of the producing GEMM meet here, together with the
 // residual add, so no GEMM has to wait on another workgroup.  RMSNorm:
 // zhichai.net, "DFlash 的架构密码", 技术细节补充 / 投影层 for the fusion norm;
@@ -88,7 +90,8 @@ __global__ __launch_bounds__(256) void resid_rmsnorm_kernel(float* __restrict__ 
                                                             const float* __restrict__ part,
                                                             int n_split, int64_t split_stride,
                                                             const T* __restrict__ gain,
-                                                            T* __restrict__ out, int H, float eps) {
+                                                            T* __restrict__ out, int H, float eps,
+                                                            int frag) {
   __shared__ float red[4];
   const int m = blockIdx.x;
   constexpr int kMaxSplit = NS;
@@ -131,15 +134,15 @@ __global__ __launch_bounds__(256) void resid_rmsnorm_kernel(float* __restrict__ 
   __syncthreads();
   const float tot = (red[0] + red[1]) + (red[2] + red[3]);
   const float r = 1.0f / sqrtf(tot / static_cast<float>(H) + eps);
-  T* o = out + static_cast<int64_t>(m) * H;
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
     const int c = (q * 256 + threadIdx.x) * 4;
     if (c < H) {
-      stf(o + c + 0, v[q].x * r * ldf(gain + c + 0));
-      stf(o + c + 1, v[q].y * r * ldf(gain + c + 1));
-      stf(o + c + 2, v[q].z * r * ldf(gain + c + 2));
-      stf(o + c + 3, v[q].w * r * ldf(gain + c + 3));
+      T* o = out + (frag ? frag_major(m, c, H) : static_cast<int64_t>(m) * H + c);
+      stf(o + 0, v[q].x * r * ldf(gain + c + 0));
+      stf(o + 1, v[q].y * r * ldf(gain + c + 1));
+      stf(o + 2, v[q].z * r * ldf(gain + c + 2));
+      stf(o + 3, v[q].w * r * ldf(gain + c + 3));
     }
   }
 }
@@ -147,11 +150,11 @@ __global__ __launch_bounds__(256) void resid_rmsnorm_kernel(float* __restrict__ 
 template <typename T>
 static hipError_t launch_rn(float* x, const float* part, int n_split, int64_t split_stride,
                             const void* gain, void* out, int rows, int H, float eps,
-                            hipStream_t st) {
+                            hipStream_t st, int frag) {
   const T* g = static_cast<const T*>(gain);
   T* o = static_cast<T*>(out);
   const int per = (H + 1023) / 1024;
-#define DF_RN(P, S) resid_rmsnorm_kernel<T, P, S><<<rows, 256, 0, st>>>(x, part, n_split, split_stride, g, o, H, eps)
+#define DF_RN(P, S) resid_rmsnorm_kernel<T, P, S><<<rows, 256, 0, st>>>(x, part, n_split, split_stride, g, o, H, eps, frag)
   if (n_split <= 4) {
     if (per <= 1) DF_RN(1, 4);
     else if (per <= 2) DF_RN(2, 4);
@@ -169,11 +172,12 @@ static hipError_t launch_rn(float* x, const float* part, int n_split, int64_t sp
 
 hipError_t launch_resid_rmsnorm(bool bf16, float* x, const float* part, int n_split,
                                 int64_t split_stride, const void* gain, void* out, int rows,
-                                int H, float eps, hipStream_t st) {
+                                int H, float eps, hipStream_t st, bool frag) {
   if (rows <= 0) return hipSuccess;
-  if (H > 8192 || H % 4 || n_split > 8) return hipErrorInvalidValue;
-  return bf16 ? launch_rn<uint16_t>(x, part, n_split, split_stride, gain, out, rows, H, eps, st)
-              : launch_rn<float>(x, part, n_split, split_stride, gain, out, rows, H, eps, st);
+  if (H > 8192 || H % 4 || n_split > 8 || (frag && H % 32)) return hipErrorInvalidValue;
+  const int f = frag ? 1 : 0;
+  return bf16 ? launch_rn<uint16_t>(x, part, n_split, split_stride, gain, out, rows, H, eps, st, f)
+              : launch_rn<float>(x, part, n_split, split_stride, gain, out, rows, H, eps, st, f);
 }
 
 // ------------------------------------------------------------------ LM-head argmax

@@ -14,13 +14,13 @@ namespace dflash {
 // (layer 0's attention norm), one workgroup per block slot.
 hipError_t launch_embed(bool bf16, const void* embed, int H, int V, const int32_t* anchors,
                         int mask_id, int batch, int B, float* x, const void* gain, void* u,
-                        float eps, hipStream_t st);
+                        float eps, hipStream_t st, bool frag = false);
 
 // Row m: v = x[m] + sum_s part[s * split_stride + m*H ...] (x and part may be
 // null); x[m] = v when x; out[m] = RMSNorm(v) * gain when out (handle type).
 hipError_t launch_resid_rmsnorm(bool bf16, float* x, const float* part, int n_split,
                                 int64_t split_stride, const void* gain, void* out, int rows,
-                                int H, float eps, hipStream_t st);
+                                int H, float eps, hipStream_t st, bool frag = false);
 
 // QKV of a batch of blocks from ks fp32 partial slabs [ks][rows][qd + 2 kvd]
 // (slab = rows * (qd + 2 kvd)): sum, RoPE on q and k at the block positions,
