@@ -52,6 +52,12 @@ Readings of points the pages leave open (each repeated where it is used):
      next token is drawn from (q_a - p_{a+1})_+ by inverse CDF with a caller
      uniform u (smallest index whose cumulative weight exceeds u * total);
      after B-1 acceptances it is drawn from q_{B-1} the same way.
+  R11 one loop cycle after the target scored a block (the pages: the block
+     starts at the verified bonus token; the committed tokens' target
+     features become context): the target's hidden states at the block's B
+     positions are given; slots 0..a (the anchor and the a accepted drafts)
+     are appended at positions L..L+a, L becomes L+a+1, and the next block is
+     drafted from the bonus token at position L+a+1.
 """
 from __future__ import annotations
 
@@ -332,6 +338,32 @@ def append_context(cache, weights, shape, feats) -> list:
     new = inject_kv(c, L + np.arange(c.shape[0]), weights["layers"], shape, rb)
     return [(np.concatenate([k, nk]), np.concatenate([v, nv]))
             for (k, v), (nk, nv) in zip(cache, new)]
+
+
+def verify_append_draft(weights, shape, caches, target_logits, drafts, block_feats,
+                        block_size: int) -> dict:
+    """One cycle of the speculative loop once the target has scored a block.
+
+    Verify the drafts ([Summary] 实践 2), append the anchor and the accepted
+    drafts -- whose target features the target produced while scoring the
+    block -- to each sequence's context, and draft the next block from the
+    bonus token ([Arch] 训练策略 1: every block starts at the verified token).
+    Reading R11.
+
+    caches[b]: as in draft_block; target_logits [N, B, V]; drafts [N, B-1];
+    block_feats: per fused target layer, [N*B, H] with row b*B + j = slot j
+    of sequence b.  Returns accept [N], bonus [N], the new caches, the next
+    draft_ids [N, B-1] and their top-2 gaps.
+    """
+    B = int(block_size)
+    accept, bonus = verify_greedy(target_logits, drafts)
+    new = []
+    for b, cache in enumerate(caches):
+        rows = slice(b * B, b * B + int(accept[b]) + 1)
+        new.append(append_context(cache, weights, shape, [np.asarray(f)[rows] for f in block_feats]))
+    d = draft_block(weights, shape, new, bonus, B)
+    return {"accept": accept, "bonus": bonus, "caches": new, "draft_ids": d["draft_ids"],
+            "gap": d["gap"]}
 
 
 # ------------------------------------------- (N2) training-layout forward

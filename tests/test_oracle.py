@@ -548,6 +548,85 @@ def test_speculative_loop_is_lossless(hf_llama):
             assert all(a == B - 1 for a in accepted[:-1])
 
 
+def test_verify_append_draft_matches_one_shot_context(hf_llama):
+    """The loop cycle keeps the context equal to a fresh prefill of everything committed.
+
+    A tiny random Llama is the target.  Each cycle it scores [anchor, drafts]
+    and hands over its hidden states at those positions; the drafts follow
+    the target's own continuation for a planned number of slots (0 .. B-1,
+    different per sequence) and then go wrong, so the accepted count is
+    known.  After verify_append_draft the caches must equal the prefill of
+    the target's features over the whole committed sequence (run again from
+    scratch), the next drafts must be those drafted on that prefill from the
+    bonus token, and the committed tokens must be the target's own greedy
+    output.  A wrong slot range, a position shift or a stale anchor fails.
+    """
+    transformers, ml = hf_llama
+    torch.manual_seed(1)
+    n_t_layers, H, V = 8, 32, 40
+    tcfg = transformers.LlamaConfig(hidden_size=H, intermediate_size=64, num_attention_heads=4,
+                                    num_key_value_heads=2, head_dim=8,
+                                    num_hidden_layers=n_t_layers, vocab_size=V,
+                                    rms_norm_eps=1e-6, initializer_range=0.5)
+    tcfg._attn_implementation = "eager"
+    target = transformers.LlamaForCausalLM(tcfg).double().eval()
+    ids = O.target_layer_ids(n_t_layers)
+    shape = _tiny_shape(hidden=H, vocab=V)
+    w = configs.make_weights(shape, 911)
+
+    def run(seq):
+        with torch.no_grad():
+            out = target(torch.tensor([seq]), output_hidden_states=True)
+        return out.logits[0].numpy(), [out.hidden_states[i][0].numpy() for i in ids]
+
+    B, n_new, N = 4, 40, 2
+    prompts = [[3, 14, 15, 9, 2, 6], [7, 1, 8, 2, 8]]
+    plain = [list(p) for p in prompts]
+    for b in range(N):
+        for _ in range(n_new):
+            plain[b].append(int(np.argmax(run(plain[b])[0][-1])))
+
+    seqs = [list(p) for p in prompts]
+    caches, anchors = [], []
+    for b in range(N):
+        lg, fs = run(seqs[b])
+        caches += O.prefill(w, shape, [fs])
+        anchors.append(int(np.argmax(lg[-1])))
+    plan = [[0, 3, 1, 2, 3, 0], [2, 0, 3, 3, 1, 2]]   # accepted drafts per cycle
+    for cyc in range(len(plan[0])):
+        drafts = np.zeros((N, B - 1), dtype=np.int64)
+        tls, feats = [], [[] for _ in ids]
+        for b in range(N):
+            P = len(seqs[b])
+            true = plain[b][P + 1:P + B]
+            a = plan[b][cyc]
+            drafts[b] = [true[j] if j < a else (true[j] + 1 + j) % V for j in range(B - 1)]
+            tl, tf = run(seqs[b] + [anchors[b]] + [int(t) for t in drafts[b]])
+            tls.append(tl[P:P + B])
+            for i, f in enumerate(tf):
+                feats[i].append(f[P:P + B])
+        feats = [np.concatenate(f) for f in feats]
+        st = O.verify_append_draft(w, shape, caches, np.stack(tls), drafts, feats, B)
+        np.testing.assert_array_equal(st["accept"], [plan[b][cyc] for b in range(N)])
+        fresh = []
+        for b in range(N):
+            seqs[b] += [anchors[b]] + [int(t) for t in drafts[b][:plan[b][cyc]]]
+            fresh += O.prefill(w, shape, [run(seqs[b])[1]])
+        # (the target's RMSNorm runs in float32 even on a float64 model, so
+        # its features for the same prefix differ by ~1e-8 between runs of
+        # different length; a wrong row or position differs by ~0.1)
+        for b in range(N):
+            assert st["caches"][b][0][0].shape[0] == len(seqs[b])
+            for (k1, v1), (k2, v2) in zip(st["caches"][b], fresh[b]):
+                np.testing.assert_allclose(k1, k2, rtol=0, atol=1e-6)
+                np.testing.assert_allclose(v1, v2, rtol=0, atol=1e-6)
+        again = O.draft_block(w, shape, fresh, st["bonus"], B)
+        np.testing.assert_array_equal(st["draft_ids"], again["draft_ids"])
+        caches, anchors = st["caches"], [int(x) for x in st["bonus"]]
+        for b in range(N):
+            assert seqs[b] + [anchors[b]] == plain[b][:len(seqs[b]) + 1]
+
+
 # ------------------------------------------------------------------ scale anchor
 
 def test_param_count_matches_2b_claim():
