@@ -440,6 +440,92 @@ def workload_long(torch, L, configs, dr, shape, repeats: int = 3) -> dict:
     return out
 
 
+def workload_resident(torch, L, configs, dr, shape, steps: int = 64) -> dict:
+    """Batch 1, ctx 2048, B 16: the verify -> append -> draft loop three ways.
+    host_sync: verify, read the accepted count on the host, fuse and inject
+    that many rows, draft (one device-to-host sync per step); resident: one
+    dflash_step_resident per step, no host read; graph: that step captured
+    once in a HIP graph and replayed.  Target logits and features are fixed
+    random tensors, so most drafts are rejected (one appended row per step)."""
+    CTX, B, H, V = 2048, BLOCK, shape.hidden, shape.vocab
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7001)
+    feats = [torch.randn((CTX, H), generator=g, device="cuda").to(torch.bfloat16)
+             for _ in range(shape.n_feat)]
+    ctx = torch.empty((CTX, H), dtype=torch.bfloat16, device="cuda")
+    len_max = CTX + (steps + 1) * B
+    cache = L.KVCache(shape, [len_max + B])
+    ws = dr.workspace(1, B, CTX)
+    dr.fuse_context(feats, ctx, ws)
+    dr.inject_kv(ctx, [CTX], cache, ws, pos_start=[0])
+    del feats, ctx
+    blk = [torch.randn((B, H), generator=g, device="cuda").to(torch.bfloat16)
+           for _ in range(shape.n_feat)]
+    logits = (torch.randn((1, B, V), generator=g, device="cuda") * 3).to(torch.bfloat16)
+    ctx_new = torch.empty((B, H), dtype=torch.bfloat16, device="cuda")
+    anchor0 = torch.from_numpy(configs.make_anchors(shape, 7001, 1)).cuda()
+    anchor = anchor0.clone()
+    draft = torch.empty((1, B - 1), dtype=torch.int32, device="cuda")
+    accept = torch.zeros(1, dtype=torch.int32, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dev_len = torch.full((1,), CTX, dtype=torch.int32, device="cuda")
+    vws = torch.empty(L.verify_workspace_size(1, B, V), dtype=torch.uint8, device="cuda")
+
+    def reset():
+        cache.seq_len[:] = CTX
+        dev_len.fill_(CTX)
+        anchor.copy_(anchor0)
+        status.zero_()
+        dr.draft_block(cache, B, anchor, draft, ws)
+        torch.cuda.synchronize()
+
+    def host_step():
+        L.verify_greedy(logits, draft, accept, anchor, vws)
+        n = int(accept.item()) + 1                   # device -> host
+        dr.fuse_context([f[:n] for f in blk], ctx_new, ws)
+        dr.inject_kv(ctx_new, [n], cache, ws)
+        dr.draft_block(cache, B, anchor, draft, ws)
+
+    def resident_step():
+        dr.step_resident(cache, B, dev_len, len_max, logits, blk, draft, anchor, accept, status,
+                         ws)
+
+    def timed(fn):
+        reset()
+        fn()                                          # one untimed step
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    out = {"workload": "qwen3-8b-shaped, batch 1, ctx 2048, B16: verify + append + draft loop",
+           "steps": steps}
+    out["host_sync_ms_per_step"] = round(timed(host_step), 4)
+    host_len = int(cache.seq_len[0])
+    out["resident_ms_per_step"] = round(timed(resident_step), 4)
+    res_len = int(dev_len.item())
+    reset()
+    resident_step()
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        resident_step()
+    torch.cuda.synchronize()
+
+    def replay():
+        gr.replay()
+    out["graph_ms_per_step"] = round(timed(replay), 4)
+    out["ctx_after"] = {"host_sync": host_len, "resident": res_len, "graph": int(dev_len.item())}
+    out["status"] = int(status.item())
+    del cache, gr
+    return out
+
+
 def workload_27b(torch, L, configs, reps: int) -> dict:
     """27B-target-shaped drafter (H 5120, 40/8 heads, FFN 17408), batch 8,
     context 4096 each, blocks of 8 and 16 slots."""
@@ -697,6 +783,9 @@ def main():
         t1 = time.time()
         workloads["training_layout"] = workload_training(torch, L, configs, dr, shape, 10)
         log(f"training layout done ({time.time() - t1:.1f}s)")
+        t1 = time.time()
+        workloads["resident_loop"] = workload_resident(torch, L, configs, dr, shape)
+        log(f"resident loop done ({time.time() - t1:.1f}s): {workloads['resident_loop']}")
         dr.close()
         del dr
         torch.cuda.empty_cache()

@@ -231,7 +231,7 @@ Layout layout(const dflash_handle* h, int max_batch, int max_block, int64_t max_
   const size_t M16 = (M + 15) / 16 * 16;
   L.u_off = off;    off += align_up(M16 * D.H * es);
   L.q_off = off;    off += align_up(M * D.qd * es);
-  L.o_off = off;    off += align_up(M * D.qd * es);
+  L.o_off = off;    off += align_up(M16 * D.qd * es);
   L.h_off = off;    off += align_up(M16 * D.F * es);
   // K-split partial slabs: O / down projections [ks][M][H], fusion [ks][T][H]
   size_t part = static_cast<size_t>(g.ks_o > g.ks_d ? g.ks_o : g.ks_d) * M * D.H * 4;
@@ -580,10 +580,16 @@ struct TrainSpec {
   float* loss;             // device [1]
 };
 
+// Committed lengths in device memory (device-resident step), at most max.
+struct DevLen {
+  const int32_t* len;
+  int max;
+};
+
 template <typename T>
 dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* anchors,
                          int32_t* draft, float* dbg_h, float* dbg_z, void* ws, hipStream_t st,
-                         const TrainSpec* tr = nullptr) {
+                         const TrainSpec* tr = nullptr, const DevLen* dl = nullptr) {
   const Dims D = dims(h->cfg);
   const int nb = tr ? tr->n : kv->batch, M = nb * B;
   const bool bf = h->cfg.dtype == DFLASH_BF16;
@@ -594,11 +600,16 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
   SeqTable seq{};
   seq.n = nb;
   int max_keys = 0;   // keys in the cache per entry (training: the context part only)
+  // (device lengths: the launch plan covers every length up to dl->max)
   for (int b = 0; b < nb; ++b) {
-    seq.len[b] = tr ? tr->len[b] : kv->seq_len[b];
+    seq.len[b] = tr ? tr->len[b] : (dl ? dl->max : kv->seq_len[b]);
     seq.off[b] = tr ? tr->off[b] : kv->seq_off[b];
     const int nk = seq.len[b] + (tr ? 0 : B);
     max_keys = nk > max_keys ? nk : max_keys;
+  }
+  if (dl) {
+    seq.dlen = dl->len;
+    seq.len_max = dl->max;
   }
   // training layout: the blocks' own K/V in the workspace, kTrainSlab rows each
   const int64_t capb = static_cast<int64_t>(nb) * kTrainSlab;
@@ -614,8 +625,8 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
   const int64_t pstride = static_cast<int64_t>(M) * D.H;   // one K-split slab
   // batches of blocks: the layer GEMMs and the LM head on the LDS-tiled GEMM
   const bool mid = bf && M >= kMidMinRows;
-  // u and h feed the weight-streaming GEMM (fragment-major) unless the
-  // LDS-tiled one takes this many rows
+  // u, h and the attention output feed the weight-streaming GEMM
+  // (fragment-major) unless the LDS-tiled one takes this many rows
   const bool frag = !mid;
   const MidPlan mp = mid_plan(D, M);
   const int ks_o = mid ? mp.ks_o : g.ks_o, ks_d = mid ? mp.ks_d : g.ks_d;
@@ -642,6 +653,7 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
   aa.ldq = D.qd;
   aa.cap = kv->cap_total;
   aa.o = ob;
+  aa.ofrag = frag ? 1 : 0;
   aa.part_o = at<float>(ws, L.ao_off);
   aa.part_ml = at<float2>(ws, L.aml_off);
   aa.B = B;
@@ -721,7 +733,7 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
       EpiPartialF32<T> e{static_cast<const T*>(w.wo), D.qd, part, D.H, M};
       // two pair tiles per step share each A fragment (measured faster here,
       // slower on the QKV, down and LM-head shapes)
-      DF_HIP(run_rows<T>(a_single<T>(ob, D.qd, D.qd, M), D.qd, g.tiles_o, 1, g.ks_o, e, st,
+      DF_HIP(run_rows<T>(a_frag<T>(ob, D.qd, M), D.qd, g.tiles_o, 1, g.ks_o, e, st,
                          NoPerLaunch{}, 4, 2));
     }
     DF_MARK(DFLASH_SEC_O_PROJ, l, true);
@@ -839,6 +851,44 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
   return DFLASH_OK;
 }
 
+// The device-resident step's fused context rows sit past everything the
+// fusion of those rows uses in the workspace.
+size_t step_ctx_off(const dflash_handle* h, int64_t rows) {
+  return align_up(layout(h, 1, 1, rows).total);
+}
+
+// verify -> append the accepted rows -> advance the lengths -> next draft,
+// every count and length read on the device (see dflash_step_resident).
+template <typename T>
+dflash_status step_impl(dflash_handle* h, dflash_kv* kv, int B, int32_t* dev_len, int len_max,
+                        const void* logits, bool logits_bf16, const void* const* feats,
+                        int32_t* draft, int32_t* anchor, int32_t* accept, int32_t* status,
+                        void* ws, hipStream_t st) {
+  const Dims D = dims(h->cfg);
+  const int nb = kv->batch, M = nb * B;
+  const Layout L = layout(h, nb, B, 1);
+  DF_HIP(launch_verify(logits, logits_bf16, draft, nb, B, D.V, accept, anchor,
+                       at<void>(ws, L.ver_off), st));
+  void* ctx = at<void>(ws, step_ctx_off(h, M));
+  dflash_status s = fuse_impl<T>(h, feats, M, ctx, ws, st);
+  if (s != DFLASH_OK) return s;
+  SeqTable seq{};
+  seq.n = nb;
+  for (int b = 0; b < nb; ++b) {
+    seq.len[b] = len_max;
+    seq.off[b] = kv->seq_off[b];
+  }
+  seq.dlen = dev_len;
+  seq.dcnt = accept;
+  seq.len_max = len_max;
+  seq.stride = B;
+  s = inject_impl<T>(h, ctx, seq, M, kv, ws, st);
+  if (s != DFLASH_OK) return s;
+  DF_HIP(launch_advance_lengths(dev_len, accept, nb, B, len_max, status, st));
+  const DevLen dl{dev_len, len_max};
+  return draft_impl<T>(h, kv, B, anchor, draft, nullptr, nullptr, ws, st, nullptr, &dl);
+}
+
 }  // namespace
 
 // ================================================================ C ABI
@@ -907,7 +957,11 @@ dflash_status dflash_workspace_size(const dflash_handle* h, int32_t max_batch, i
   if (!h || !bytes || max_batch < 1 || max_batch > DFLASH_MAX_BATCH || max_block < 2 ||
       max_block > DFLASH_MAX_BLOCK || max_tokens < 0)
     return DFLASH_ERR_INVALID_ARG;
-  *bytes = layout(h, max_batch, max_block, max_tokens).total;
+  const size_t es = h->cfg.dtype == DFLASH_BF16 ? 2 : 4;
+  const int64_t rows = static_cast<int64_t>(max_batch) * max_block;
+  // the device-resident step: its fusion's scratch, then its context rows
+  const size_t step = step_ctx_off(h, rows) + align_up(static_cast<size_t>(rows) * h->cfg.hidden * es);
+  *bytes = std::max(layout(h, max_batch, max_block, max_tokens).total, step);
   return DFLASH_OK;
 }
 
@@ -1020,6 +1074,38 @@ dflash_status dflash_train_forward(dflash_handle* h, const dflash_kv* kv, int32_
                                     ws, st, &tr)
              : draft_impl<float>(h, kvm, block_size, anchor_ids, nullptr, nullptr, dbg_logits, ws,
                                  st, &tr);
+}
+
+dflash_status dflash_step_resident(dflash_handle* h, dflash_kv* kv, int32_t block_size,
+                                   int32_t* dev_len, int32_t len_max, const void* target_logits,
+                                   dflash_dtype logits_dtype, const void* const* block_feats,
+                                   int32_t* draft_ids, int32_t* anchor_ids, int32_t* accept,
+                                   int32_t* status, void* ws, void* stream) {
+  if (!h || !dev_len || !target_logits || !block_feats || !draft_ids || !anchor_ids || !accept ||
+      !status || !ws)
+    return DFLASH_ERR_INVALID_ARG;
+  if (logits_dtype != DFLASH_F32 && logits_dtype != DFLASH_BF16) return DFLASH_ERR_INVALID_ARG;
+  if (block_size < 2 || block_size > DFLASH_MAX_BLOCK) return DFLASH_ERR_INVALID_ARG;
+  dflash_status s = check_kv(h, kv);
+  if (s != DFLASH_OK) return s;
+  const Dims D = dims(h->cfg);
+  if (D.G * block_size > 80) return DFLASH_ERR_UNSUPPORTED;
+  if (!aligned16(ws) || !aligned16(target_logits)) return DFLASH_ERR_INVALID_ARG;
+  for (int i = 0; i < h->cfg.n_feat_layers; ++i)
+    if (!block_feats[i] || !aligned16(block_feats[i])) return DFLASH_ERR_INVALID_ARG;
+  if (len_max < 0) return DFLASH_ERR_INVALID_ARG;
+  // every position the step can write, len_max + block_size - 1 at most,
+  // stays inside each sequence's slab
+  for (int b = 0; b < kv->batch; ++b)
+    if (static_cast<int64_t>(len_max) + block_size > kv->seq_cap[b]) return DFLASH_ERR_CAPACITY;
+  if ((len_max + block_size + 255) / 256 > kMaxAttnChunks * 64) return DFLASH_ERR_UNSUPPORTED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool lbf = logits_dtype == DFLASH_BF16;
+  return h->cfg.dtype == DFLASH_BF16
+             ? step_impl<uint16_t>(h, kv, block_size, dev_len, len_max, target_logits, lbf,
+                                   block_feats, draft_ids, anchor_ids, accept, status, ws, st)
+             : step_impl<float>(h, kv, block_size, dev_len, len_max, target_logits, lbf,
+                                block_feats, draft_ids, anchor_ids, accept, status, ws, st);
 }
 
 size_t dflash_stochastic_workspace_size(int32_t batch, int32_t block_size, int32_t vocab) {

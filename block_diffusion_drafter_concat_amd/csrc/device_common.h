@@ -148,7 +148,20 @@ struct SeqTable {
   int64_t off[kMaxBatch];     // start row of the sequence inside each head slab
   int32_t pos0[kMaxBatch];    // position of the first written row (inject)
   int32_t n;                  // sequences
+  // Device-resident step: the committed lengths live in device memory (dlen,
+  // clamped to [0, len_max]; len[] then holds len_max for the host's launch
+  // plan), and an injection's row m is slot m % stride of sequence m / stride,
+  // appended while that slot is <= dcnt[b] (accepted drafts after the anchor).
+  const int32_t* dlen;
+  const int32_t* dcnt;
+  int32_t len_max;
+  int32_t stride;
 };
+
+// Committed context rows of sequence b.
+__device__ __forceinline__ int seq_len_of(const SeqTable& t, int b) {
+  return t.dlen ? min(max(t.dlen[b], 0), t.len_max) : t.len[b];
+}
 
 // (max, sum of exp(x - max)) of a union of two value sets; an empty set has
 // max -inf.  The log-sum-exp is max + log(sum).
@@ -182,6 +195,20 @@ __device__ __forceinline__ int seq_of_row(const SeqTable& t, int row) {
   int b = 0;
   for (int s = 1; s < t.n; ++s) b = (row >= t.row0[s]) ? s : b;
   return b;
+}
+
+// Input row m of an injection: its sequence b and cache position pos; false
+// for a row the sequence does not append (device-resident step only).
+__device__ __forceinline__ bool inject_row(const SeqTable& t, int m, int& b, int& pos) {
+  if (t.dcnt) {
+    b = m / t.stride;
+    const int i = m - b * t.stride;
+    pos = seq_len_of(t, b) + i;
+    return i <= min(max(t.dcnt[b], 0), t.stride - 1);
+  }
+  b = seq_of_row(t, m);
+  pos = t.pos0[b] + (m - t.row0[b]);
+  return true;
 }
 
 }  // namespace dflash

@@ -145,13 +145,14 @@ struct EpiQKV {
                         float v1) const {
     if (!valid) return;
     const int b = m / B, j = m % B;
-    const int64_t row = seq.off[b] + seq.len[b] + j;
+    const int pos = seq_len_of(seq, b) + j;
+    const int64_t row = seq.off[b] + pos;
     if (tile < nq() + nk()) {
       const bool is_q = tile < nq();
       const RopePairTile pt = rope_pair_tile(is_q ? tile : tile - nq(), d);
       const int c = pt.i0 + i;
       float cs, sn;
-      rope_cos_sin(seq.len[b] + j, c, freq, cs, sn);
+      rope_cos_sin(pos, c, freq, cs, sn);
       const float o0 = v0 * cs - v1 * sn;
       const float o1 = v1 * cs + v0 * sn;
       T* dst = is_q ? q + static_cast<int64_t>(m) * ldq + pt.head * d
@@ -195,10 +196,9 @@ struct EpiInject {
   }
   __device__ void apply(State&, int, int tile, int, int m, int i, bool valid, float v0,
                         float v1) const {
-    if (!valid) return;
+    int b, pos;
+    if (!valid || !inject_row(seq, m, b, pos)) return;
     const int l = tile / (2 * kt()), t = tile % (2 * kt());
-    const int b = seq_of_row(seq, m);
-    const int pos = seq.pos0[b] + (m - seq.row0[b]);
     const int64_t row = seq.off[b] + pos;
     if (t < kt()) {
       const RopePairTile pt = rope_pair_tile(t, d);

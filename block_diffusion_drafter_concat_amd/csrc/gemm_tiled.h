@@ -512,16 +512,12 @@ struct TEpiInject {
     int* pos_t = static_cast<int*>(ext);
     int64_t* row_t = reinterpret_cast<int64_t*>(pos_t + 64);
     if (t < 64) {
-      const int m = min(s.row(t), s.M - 1);
-      int pos = 0;
-      int64_t off = 0;
-      for (int b = 0; b < seq.n; ++b)
-        if (m >= seq.row0[b]) {
-          pos = seq.pos0[b] + (m - seq.row0[b]);
-          off = seq.off[b];
-        }
+      // rows past M, and rows a sequence does not append, store nothing
+      const int m = s.row(t);
+      int b = 0, pos = 0;
+      const bool keep = m < s.M && inject_row(seq, m, b, pos);
       pos_t[t] = pos;
-      row_t[t] = off + pos;
+      row_t[t] = keep ? seq.off[b] + pos : -1;
     }
     __syncthreads();
     if ((s.part & 1) == 0) {
@@ -534,7 +530,7 @@ struct TEpiInject {
       if (s.n0 + col >= s.N) return;
       const double inv = freq.inv[c];
       for (int lr = t / pairs; lr < 64; lr += nt / pairs) {
-        if (s.row(lr) >= s.M) continue;
+        if (row_t[lr] < 0) continue;
         float cs, sn;
         rope_cos_sin(pos_t[lr], inv, cs, sn);
         const float x0 = s.at(lr, col), x1 = s.at(lr, col + half);
@@ -545,8 +541,8 @@ struct TEpiInject {
     } else {
       uint16_t* vt = vc[s.part >> 1];
       const int lr = t & 63;
-      if (s.row(lr) >= s.M) return;
       const int64_t r = row_t[lr];
+      if (r < 0) return;
       for (int col = t >> 6; col < s.bn && s.n0 + col < s.N; col += nt >> 6)
         stf(vt + static_cast<int64_t>(s.n0 + col) * cap + r, s.at(lr, col));
     }

@@ -66,14 +66,18 @@ __device__ __forceinline__ void mask_tail(Frag8<float>& f, int first, int end) {
   pack8(f, w);
 }
 
-// Output element (query row r, head dim d) of a kv head's G*B x D block goes
-// to o[(b*B + j) * ldq + (g*G + h) * D + d] with r = h*B + j.
+// Output element (query row r, head dim d) of a kv head's G*B x D block is
+// o[m, k] with m = b*B + j, k = (g*G + h) * D + d and r = h*B + j: row-major
+// (row stride ldq) or, for the output projection's weight-streaming GEMM,
+// fragment-major (four columns of one aligned run of 32 stay contiguous).
 template <typename T>
 __device__ __forceinline__ void store_out4(const AttnArgs& p, int b, int g, int r, int d,
                                            const float* v) {
   const int B = p.B, G = p.G, D = p.head_dim;
   const int h = r / B, j = r % B;
-  T* o = static_cast<T*>(p.o) + static_cast<int64_t>(b * B + j) * p.ldq + (g * G + h) * D + d;
+  const int m = b * B + j, k = (g * G + h) * D + d;
+  T* o = static_cast<T*>(p.o) + (p.ofrag ? frag_major(m, k, static_cast<int>(p.ldq))
+                                         : static_cast<int64_t>(m) * p.ldq + k);
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) stf(o + jj, v[jj]);
 }

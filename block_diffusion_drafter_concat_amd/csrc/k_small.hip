@@ -321,7 +321,7 @@ __global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict
                                                          int64_t cap, RopeFreq freq, SeqTable seq,
                                                          bool block_rows) {
   const int m = blockIdx.x, b = m / B, j = m % B;
-  const int pos = seq.len[b] + j;
+  const int pos = seq_len_of(seq, b) + j;
   // training layout: the block's K/V go to its own rows of the block buffer
   const int64_t row = block_rows ? static_cast<int64_t>(b) * kTrainSlab + j : seq.off[b] + pos;
   const int nq = qd + 2 * kvd, half = d / 2;
@@ -502,6 +502,34 @@ hipError_t launch_verify(const void* logits, bool bf16, const int32_t* drafts, i
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   verify_scan_kernel<<<batch, 64 * B, 0, st>>>(part, n_chunks, B, drafts, accept, bonus);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ lengths
+// Device-resident step: after the accepted rows of each sequence were
+// appended, len[b] += accept[b] + 1 (the anchor and its accepted drafts).  A
+// length that would pass len_max stays where it is and sets status[0] = 1, so
+// no later kernel of the loop indexes past the capacity the host checked.
+__global__ __launch_bounds__(64) void advance_lengths_kernel(int32_t* __restrict__ len,
+                                                             const int32_t* __restrict__ accept,
+                                                             int n, int B, int len_max,
+                                                             int32_t* __restrict__ status) {
+  const int b = blockIdx.x * 64 + threadIdx.x;
+  if (b >= n) return;
+  const int a = min(max(accept[b], 0), B - 1);
+  const int cur = min(max(len[b], 0), len_max);
+  const int nl = cur + a + 1;
+  if (nl > len_max) {
+    status[0] = 1;
+    len[b] = cur;
+  } else {
+    len[b] = nl;
+  }
+}
+
+hipError_t launch_advance_lengths(int32_t* len, const int32_t* accept, int n, int B, int len_max,
+                                  int32_t* status, hipStream_t st) {
+  advance_lengths_kernel<<<(n + 63) / 64, 64, 0, st>>>(len, accept, n, B, len_max, status);
   return hipGetLastError();
 }
 

@@ -57,6 +57,8 @@ hipError_t launch_lm_argmax_finalize(const float2* part, int n_wg, int rows, int
 
 // Greedy verify: per-chunk row argmax, then per-sequence prefix scan.
 size_t verify_ws_bytes(int batch, int B, int V);
+hipError_t launch_advance_lengths(int32_t* len, const int32_t* accept, int n, int B, int len_max,
+                                  int32_t* status, hipStream_t st);
 hipError_t launch_verify(const void* logits, bool bf16, const int32_t* drafts, int batch, int B,
                          int V, int32_t* accept, int32_t* bonus, void* ws, hipStream_t st);
 

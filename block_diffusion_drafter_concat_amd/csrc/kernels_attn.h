@@ -11,7 +11,8 @@ struct AttnArgs {
   const void* kc;       // layer K cache [n_kv][cap][D]
   const void* vc;       // layer V cache [n_kv][D][cap]
   int64_t cap;
-  void* o;              // [batch*B, n_q*D] attention output
+  void* o;              // [batch*B, n_q*D] attention output (row stride ldq)
+  int ofrag;            // 1: o stored fragment-major (frag_major(), row length ldq)
   float* part_o;        // [batch][n_kv][max_chunks][NQ][D/16][64 lanes][4] (C layout)
   float2* part_ml;      // [batch][n_kv][max_chunks][ceil16(G*B)]  (max, sum), base 2
   int B, G, n_kv;
@@ -44,12 +45,12 @@ struct KeySpan {
 };
 __device__ __forceinline__ int attn_n_chunks(const AttnArgs& p, int b) {
   const bool train = p.kb != nullptr;
-  const int n_ctx = p.seq.len[b] + (train ? 0 : p.B);
+  const int n_ctx = seq_len_of(p.seq, b) + (train ? 0 : p.B);
   return (n_ctx + p.chunk - 1) / p.chunk + (train ? 1 : 0);
 }
 __device__ __forceinline__ bool attn_key_span(const AttnArgs& p, int b, int c, KeySpan& s) {
   const bool train = p.kb != nullptr;
-  const int n_ctx = p.seq.len[b] + (train ? 0 : p.B);
+  const int n_ctx = seq_len_of(p.seq, b) + (train ? 0 : p.B);
   const int nck = (n_ctx + p.chunk - 1) / p.chunk;
   s.n_chunks = nck + (train ? 1 : 0);
   if (c >= s.n_chunks) return false;

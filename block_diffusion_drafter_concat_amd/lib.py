@@ -28,7 +28,7 @@ EXPORTS = ("dflash_target_layer_ids", "dflash_create", "dflash_destroy",
            "dflash_draft_block", "dflash_verify_greedy", "dflash_verify_workspace_size",
            "dflash_train_forward", "dflash_set_timing", "dflash_status_string",
            "dflash_stochastic_workspace_size", "dflash_sample_drafts",
-           "dflash_verify_stochastic")
+           "dflash_verify_stochastic", "dflash_step_resident")
 
 # dflash_section
 SECTIONS = {"fuse_gemm": 1, "fuse_norm": 2, "inject": 3, "embed": 4, "attn_norm": 5, "qkv": 6,
@@ -107,6 +107,9 @@ def load() -> C.CDLL:
     lib.dflash_train_forward.argtypes = [vp, C.POINTER(KV), i32, i32, pi32, pi32, vp, vp,
                                          C.c_float, vp, vp, vp, vp, vp]
     lib.dflash_train_forward.restype = C.c_int
+    lib.dflash_step_resident.argtypes = [vp, C.POINTER(KV), i32, vp, i32, vp, C.c_int,
+                                         C.POINTER(vp), vp, vp, vp, vp, vp, vp]
+    lib.dflash_step_resident.restype = C.c_int
     lib.dflash_stochastic_workspace_size.argtypes = [i32, i32, i32]
     lib.dflash_stochastic_workspace_size.restype = C.c_size_t
     lib.dflash_sample_drafts.argtypes = [vp, i32, i32, i32, C.c_float, vp, vp, vp, vp]
@@ -265,6 +268,23 @@ class Drafter:
             bs.ctypes.data_as(C.POINTER(C.c_int32)), ap.ctypes.data_as(C.POINTER(C.c_int32)),
             _ptr(anchor_ids), _ptr(labels), float(gamma), _ptr(slot_loss), _ptr(loss),
             _ptr(dbg_logits), _ptr(ws), _stream(stream)), "dflash_train_forward")
+
+
+    def step_resident(self, cache: "KVCache", block_size: int, dev_len, len_max: int,
+                      target_logits, block_feats, draft_ids, anchor_ids, accept, status, ws,
+                      stream=None) -> None:
+        """Verify, append and draft in one device-resident step.  dev_len int32
+        [N], target_logits [N, B, V] (float32 or bfloat16), block_feats: one
+        [N * B, H] tensor per fused target layer, draft_ids int32 [N, B-1]
+        (read, then overwritten), anchor_ids int32 [N] (overwritten with the
+        bonus tokens), accept int32 [N], status int32 [1] (all device)."""
+        torch = _torch()
+        dt = BF16 if target_logits.dtype == torch.bfloat16 else F32
+        arr = (C.c_void_p * len(block_feats))(*[_ptr(f) for f in block_feats])
+        _check(self.lib.dflash_step_resident(
+            self.handle, C.byref(cache.c), block_size, _ptr(dev_len), int(len_max),
+            _ptr(target_logits), dt, arr, _ptr(draft_ids), _ptr(anchor_ids), _ptr(accept),
+            _ptr(status), _ptr(ws), _stream(stream)), "dflash_step_resident")
 
 
 def verify_greedy(target_logits, draft_ids, accept, bonus, ws, stream=None) -> None:

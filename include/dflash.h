@@ -25,7 +25,8 @@
  * And, for the training layout, dflash_train_forward: several blocks per
  * sequence at sampled anchors, each seeing only the context before its
  * anchor, scored with the position-decayed cross-entropy (same page, 训练策略
- * 1 and 2).
+ * 1 and 2).  dflash_step_resident chains verify, append and the next draft
+ * on the device, with no host sync between cycles.
  *
  * Conventions shared by every call
  *   - Pointers marked (device) are HIP device memory; (host) is host memory.
@@ -276,6 +277,49 @@ dflash_status dflash_train_forward(dflash_handle *h, const dflash_kv *kv, int32_
                                    const int32_t *anchor_pos, const int32_t *anchor_ids,
                                    const int32_t *labels, float gamma, float *slot_loss,
                                    float *loss, float *dbg_logits, void *ws, void *stream);
+
+/* Device-resident step of the speculative loop: verify the current block,
+ * append the accepted rows to the context, draft the next block -- with no
+ * host read in between, so a caller can run step after step (or capture one
+ * step into a HIP graph and replay it) without a device-to-host sync per
+ * cycle.  The accepted count never leaves the GPU: the appended rows, the
+ * lengths and the next anchor are all taken from device memory
+ * (ai-stack.site, "DFlash：基于块扩散的闪存推测解码方法", 实践 5: memory
+ * pooled before decoding starts, verification kept on the GPU so no data
+ * crosses to the CPU; zhichai.net, "DFlash 的架构密码", 训练策略 1: the
+ * block after a verify starts at its bonus token).
+ *
+ * In stream order, for every sequence b (batch = kv->batch, B = block_size):
+ *   1. greedy verify: target_logits (device) [batch][B][vocab] of logits_dtype
+ *      against draft_ids (device) [batch][B-1] -> accept[b] (device) and the
+ *      bonus token, written to anchor_ids[b] (device), exactly as
+ *      dflash_verify_greedy;
+ *   2. fusion of block_feats (device) [n_feat_layers] pointers to
+ *      [batch * B][hidden] arrays in the handle's dtype: the target's hidden
+ *      states at the block's B positions (row b * B + j = slot j of b);
+ *   3. injection of slots 0 .. accept[b] of sequence b (the anchor and the
+ *      accepted drafts) at positions dev_len[b] + j;
+ *   4. dev_len[b] += accept[b] + 1;
+ *   5. draft of the next block after dev_len[b] with anchor_ids[b] as its
+ *      anchor -> draft_ids, exactly as dflash_draft_block.
+ *   dev_len (device) [batch]: committed context lengths; the caller sets them
+ *     (e.g. from kv->seq_len) before the first step.  kv->seq_len (host) is
+ *     neither read nor updated here; copy dev_len back to it when the loop
+ *     ends.
+ *   len_max: a host bound on every dev_len[b] during the loop; the launch
+ *     plan covers contexts up to it.  Each step adds at most B rows, so
+ *     (start length) + steps * B is always enough.  A step whose lengths
+ *     would pass len_max leaves them unchanged and sets status[0] = 1
+ *     (device int32, never cleared by the library); dev_len values outside
+ *     [0, len_max] are clamped.  Nothing is then written outside the slabs.
+ *   ws: from dflash_workspace_size(h, >= batch, >= B, any max_tokens).
+ * Returns DFLASH_ERR_CAPACITY if len_max + B > seq_cap[b] for some b,
+ * DFLASH_ERR_UNSUPPORTED past the attention limits of dflash_draft_block. */
+dflash_status dflash_step_resident(dflash_handle *h, dflash_kv *kv, int32_t block_size,
+                                   int32_t *dev_len, int32_t len_max, const void *target_logits,
+                                   dflash_dtype logits_dtype, const void *const *block_feats,
+                                   int32_t *draft_ids, int32_t *anchor_ids, int32_t *accept,
+                                   int32_t *status, void *ws, void *stream);
 
 /* Timing hook for profiling.  Sections of the launch sequence: */
 typedef enum {

@@ -353,7 +353,8 @@ def verify_append_draft(weights, shape, caches, target_logits, drafts, block_fea
     caches[b]: as in draft_block; target_logits [N, B, V]; drafts [N, B-1];
     block_feats: per fused target layer, [N*B, H] with row b*B + j = slot j
     of sequence b.  Returns accept [N], bonus [N], the new caches, the next
-    draft_ids [N, B-1] and their top-2 gaps.
+    draft_ids [N, B-1], their top-2 gaps, the block's logits [N, B, V] and
+    final hidden states [N, B, H].
     """
     B = int(block_size)
     accept, bonus = verify_greedy(target_logits, drafts)
@@ -363,7 +364,7 @@ def verify_append_draft(weights, shape, caches, target_logits, drafts, block_fea
         new.append(append_context(cache, weights, shape, [np.asarray(f)[rows] for f in block_feats]))
     d = draft_block(weights, shape, new, bonus, B)
     return {"accept": accept, "bonus": bonus, "caches": new, "draft_ids": d["draft_ids"],
-            "gap": d["gap"]}
+            "gap": d["gap"], "logits": d["logits"], "final_hidden": d["final_hidden"]}
 
 
 # ------------------------------------------- (N2) training-layout forward

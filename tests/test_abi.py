@@ -225,6 +225,41 @@ def test_train_forward_host_checks():
     assert lib.dflash_destroy(h) == L.OK
 
 
+def test_step_resident_host_checks():
+    """Rejected device-resident steps return before anything is enqueued (fake
+    device pointers); the host lengths are neither read for the plan nor written."""
+    lib = L.load()
+    shape = configs.TINY_F32
+    st, h, keep = _create(shape)
+    assert st == L.OK
+    p = C.c_void_p(_FAKE)
+    kv, k1 = _kv(shape, [40, 7], [64, 32])
+    feats = (C.c_void_p * shape.n_feat)(*[_FAKE + 4096 * i for i in range(shape.n_feat)])
+    bad_feats = (C.c_void_p * shape.n_feat)(*([_FAKE + 2] + [_FAKE] * (shape.n_feat - 1)))
+
+    def call(B=8, dl=p, lmax=24, lg=p, dt=0, ft=feats, d=p, a=p, acc=p, sts=p, ws=p, kvp=None):
+        return lib.dflash_step_resident(h, C.byref(kv) if kvp is None else kvp, B, dl, lmax, lg,
+                                        dt, ft, d, a, acc, sts, ws, None)
+
+    for kw in (dict(B=1), dict(B=17), dict(dl=None), dict(lmax=-1), dict(lg=None), dict(dt=5),
+               dict(ft=None), dict(ft=bad_feats), dict(d=None), dict(a=None), dict(acc=None),
+               dict(sts=None), dict(ws=None), dict(ws=C.c_void_p(_FAKE + 8)),
+               dict(lg=C.c_void_p(_FAKE + 4))):
+        assert call(**kw) == L.ERR_INVALID_ARG, kw
+    # len_max + B must fit every slab (32 rows for the second sequence)
+    assert call(lmax=25) == L.ERR_CAPACITY
+    assert call(B=16, lmax=17) == L.ERR_CAPACITY
+    assert lib.dflash_step_resident(h, None, 8, p, 24, p, 0, feats, p, p, p, p, p,
+                                    None) == L.ERR_INVALID_ARG
+    assert k1[4][0] == 40 and k1[4][1] == 7
+    # the workspace covers the step's fused rows past its fusion scratch
+    sz = [C.c_size_t(), C.c_size_t()]
+    assert lib.dflash_workspace_size(h, 2, 8, 1, C.byref(sz[0])) == L.OK
+    assert lib.dflash_workspace_size(h, 2, 8, 0, C.byref(sz[1])) == L.OK
+    assert sz[0].value == sz[1].value > 2 * 8 * shape.hidden * 4
+    assert lib.dflash_destroy(h) == L.OK
+
+
 def test_stochastic_host_checks():
     lib = L.load()
     p = C.c_void_p(_FAKE)
