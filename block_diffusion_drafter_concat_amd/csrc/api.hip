@@ -247,8 +247,8 @@ Layout layout(const dflash_handle* h, int max_batch, int max_block, int64_t max_
     }
   }
   {
-    // QKV on the weight-streaming split path: bf16 below the mid-M path, and
-    // every float32 training-layout call
+    // the training layout's QKV on the weight-streaming split path: bf16
+    // below the mid-M path, float32 at any row count
     const size_t ms = h->cfg.dtype == DFLASH_BF16 ? std::min(M, static_cast<size_t>(kMidMinRows - 1)) : M;
     qkvp = std::max(qkvp, static_cast<size_t>(g.ks_qkv) * ms * (D.qd + 2 * D.kvd) * 4);
   }
@@ -691,10 +691,9 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
       DF_HIP(launch_qkv_finish(true, qkvp, mp.ks_qkv, static_cast<int64_t>(M) * nq, M, D.qd,
                                D.kvd, D.d, B, qb, D.qd, kdst(l), vdst(l), dcap, freq, seq, st,
                                tr != nullptr));
-    } else if (bf || tr) {
-      // 192 tiles on the 8B shape fill 3/4 of the CUs: split K over workgroups,
-      // then sum the slabs and rotate in the finishing kernel (which also
-      // sends a training layout's block K/V to the block buffer)
+    } else if (tr) {
+      // training layout: split K over workgroups, then sum the slabs, rotate
+      // and send the block K/V to the block buffer in the finishing kernel
       const int nq = D.qd + 2 * D.kvd;
       EpiQKVPartF32<T> e{static_cast<const T*>(w.wq), static_cast<const T*>(w.wk),
                          static_cast<const T*>(w.wv), D.H, D.qd, D.kvd, qkvp, nq, M};
@@ -715,7 +714,10 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
       e.cap = kv->cap_total;
       e.freq = freq;
       e.seq = seq;
-      // few tiles and no K-split (the epilogue needs whole sums): 8 waves each
+      // no K split (the epilogue rotates whole sums and writes q and the
+      // cache rows itself): 8 waves per pair tile.  On the 8B shape (192
+      // tiles, 3/4 of the CUs) this measured 17.5 us against 19.5 us for
+      // four K-split slabs plus the finishing kernel.
       DF_HIP(run_rows<T>(a_frag<T>(u, D.H, M), D.H, g.tiles_qkv, 1, 1, e, st,
                          NoPerLaunch{}, 8));
     }
