@@ -734,9 +734,11 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
     } else {
       EpiPartialF32<T> e{static_cast<const T*>(w.wo), D.qd, part, D.H, M};
       // two pair tiles per step share each A fragment (measured faster here,
-      // slower on the QKV, down and LM-head shapes)
+      // slower on the QKV, down and LM-head shapes); 8 waves split each K
+      // slab (8B shape: 9.5 us against 10.2 us with 4 waves; 8 waves on the
+      // QKV, gate/up and down shapes measured no gain)
       DF_HIP(run_rows<T>(a_frag<T>(ob, D.qd, M), D.qd, g.tiles_o, 1, g.ks_o, e, st,
-                         NoPerLaunch{}, 4, 2));
+                         NoPerLaunch{}, 8, 2));
     }
     DF_MARK(DFLASH_SEC_O_PROJ, l, true);
     // feed-forward half: x += O partials; u = RMSNorm(x)

@@ -53,6 +53,24 @@ template <typename T> __device__ __forceinline__ float ldf(const T* p) {
 template <typename T> __device__ __forceinline__ void stf(T* p, float v) {
   *p = Store<T>::make(v);
 }
+// Four consecutive elements, one vector access: the address must be 16-byte
+// aligned for float and 8-byte aligned for bf16.
+template <typename T> __device__ __forceinline__ float4 ld4(const T* p);
+template <> __device__ __forceinline__ float4 ld4<float>(const float* p) {
+  return *reinterpret_cast<const float4*>(p);
+}
+template <> __device__ __forceinline__ float4 ld4<uint16_t>(const uint16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+template <typename T> __device__ __forceinline__ void st4(T* p, float4 v);
+template <> __device__ __forceinline__ void st4<float>(float* p, float4 v) {
+  *reinterpret_cast<float4*>(p) = v;
+}
+template <> __device__ __forceinline__ void st4<uint16_t>(uint16_t* p, float4 v) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(f32x2_to_bf16x2(v.x, v.y), f32x2_to_bf16x2(v.z, v.w));
+}
 
 // Eight consecutive k values of one row.
 template <typename T> struct Frag8;

@@ -36,7 +36,14 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ embed,
     }
     if (c < H) *reinterpret_cast<float4*>(dst + c) = make_float4(v[q][0], v[q][1], v[q][2], v[q][3]);
   }
-  // the first layer's attention RMSNorm of this row
+  // the first layer's attention RMSNorm of this row (gains loaded before the
+  // reduction, so their latency overlaps it)
+  float4 gq[PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int c = (q * 256 + threadIdx.x) * 4;
+    gq[q] = c < H ? ld4(gain + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
@@ -48,8 +55,8 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ embed,
     if (c < H) {
       // four columns of one aligned run of 32: contiguous in either layout
       T* o = u + (frag ? frag_major(m, c, H) : static_cast<int64_t>(m) * H + c);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) stf(o + e, v[q][e] * r * ldf(gain + c + e));
+      st4(o, make_float4(v[q][0] * r * gq[q].x, v[q][1] * r * gq[q].y, v[q][2] * r * gq[q].z,
+                         v[q][3] * r * gq[q].w));
     }
   }
 }
@@ -129,6 +136,12 @@ __global__ __launch_bounds__(256) void resid_rmsnorm_kernel(float* __restrict__ 
       *reinterpret_cast<float4*>(x + static_cast<int64_t>(m) * H + c) = a;
   }
   if (!out) return;
+  float4 gq[PER];   // gains, loaded before the reduction
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int c = (q * 256 + threadIdx.x) * 4;
+    gq[q] = c < H ? ld4(gain + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
@@ -139,10 +152,8 @@ __global__ __launch_bounds__(256) void resid_rmsnorm_kernel(float* __restrict__ 
     const int c = (q * 256 + threadIdx.x) * 4;
     if (c < H) {
       T* o = out + (frag ? frag_major(m, c, H) : static_cast<int64_t>(m) * H + c);
-      stf(o + 0, v[q].x * r * ldf(gain + c + 0));
-      stf(o + 1, v[q].y * r * ldf(gain + c + 1));
-      stf(o + 2, v[q].z * r * ldf(gain + c + 2));
-      stf(o + 3, v[q].w * r * ldf(gain + c + 3));
+      st4(o, make_float4(v[q].x * r * gq[q].x, v[q].y * r * gq[q].y, v[q].z * r * gq[q].z,
+                         v[q].w * r * gq[q].w));
     }
   }
 }
@@ -381,44 +392,71 @@ hipError_t launch_lm_argmax_finalize(const float2* part, int n_wg, int rows, int
 }
 
 // ------------------------------------------------------------------ verify
-// Stage 1: workgroup (chunk, row) finds the largest logit of one 8192-column
-// chunk of one target row and its lowest column.  Stage 2: one wave per
-// sequence combines the chunks of its B rows and scans for the first draft
-// that disagrees (zhichai.net, "DFlash 的架构密码", 训练策略 1; ai-stack.site,
+// Stage 1: workgroup (row, chunk) finds the largest logit of one column chunk
+// of one target row and its lowest column.  Stage 2: one wave per sequence
+// combines the chunks of its B rows and scans for the first draft that
+// disagrees (zhichai.net, "DFlash 的架构密码", 训练策略 1; ai-stack.site,
 // "DFlash：基于块扩散的闪存推测解码方法", 实践 2 and 实践 5).
-constexpr int kVerifyChunk = 8192;
+//
+// Stage 1 is a pure stream of the logits: chunks are sized so that the whole
+// grid is about one resident round (kVerifyWGs workgroups of 256 threads, 8
+// per CU), each thread's 16-byte loads go out in groups of kVerifyBurst
+// before any compare, and chunk boundaries are multiples of 8 columns, so a
+// 16-byte load never straddles two chunks or the row end when V % 8 == 0.
+#ifndef DFLASH_VERIFY_WGS
+#define DFLASH_VERIFY_WGS 2048
+#endif
+#ifndef DFLASH_VERIFY_BURST
+#define DFLASH_VERIFY_BURST 2
+#endif
+constexpr int kVerifyWGs = DFLASH_VERIFY_WGS;
+constexpr int kVerifyMinChunk = 2048;
+constexpr int kVerifyBurst = DFLASH_VERIFY_BURST;
 struct ArgPart {
   float v;
   int i;
 };
 
+// Columns per chunk for `rows` target rows of V columns (a multiple of 8).
+static int verify_chunk_cols(int rows, int V) {
+  const int target = max(1, (kVerifyWGs + rows - 1) / max(rows, 1));
+  int chunk = (V + target - 1) / target;
+  chunk = (chunk + 7) / 8 * 8;
+  return max(chunk, kVerifyMinChunk);
+}
+
 template <typename T, bool kVec>
 __global__ __launch_bounds__(256) void verify_chunk_kernel(const T* __restrict__ logits, int V,
+                                                           int chunk_cols,
                                                            ArgPart* __restrict__ part,
                                                            int n_chunks) {
-  const int chunk = blockIdx.x, row = blockIdx.y;
+  const int row = blockIdx.x / n_chunks, chunk = blockIdx.x - row * n_chunks;
   const T* r = logits + static_cast<int64_t>(row) * V;
-  const int c0 = chunk * kVerifyChunk;
-  const int c1 = min(V, c0 + kVerifyChunk);
+  const int c0 = chunk * chunk_cols;
+  const int c1 = min(V, c0 + chunk_cols);
   float best = -INFINITY;
   int bi = 0x7fffffff;
   constexpr int kPer = 16 / sizeof(T);
   if (kVec) {
     // every thread walks its columns in increasing order, so ">" keeps the lowest
-#pragma unroll 4
-    for (int c = c0 + threadIdx.x * kPer; c < c1; c += 256 * kPer) {
-      if (c + kPer <= c1) {
-        T buf[kPer];
-        *reinterpret_cast<uint4*>(buf) = *reinterpret_cast<const uint4*>(r + c);
+    for (int cb = c0 + static_cast<int>(threadIdx.x) * kPer; cb < c1;
+         cb += 256 * kPer * kVerifyBurst) {
+      uint4 buf[kVerifyBurst];
 #pragma unroll
-        for (int e = 0; e < kPer; ++e) {
-          const float v = Store<T>::load(buf[e]);
-          if (v > best) { best = v; bi = c + e; }
-        }
-      } else {
-        for (int e = c; e < c1; ++e) {
-          const float v = ldf(r + e);
-          if (v > best) { best = v; bi = e; }
+      for (int u = 0; u < kVerifyBurst; ++u) {
+        const int c = cb + u * 256 * kPer;
+        if (c < c1) buf[u] = *reinterpret_cast<const uint4*>(r + c);
+      }
+#pragma unroll
+      for (int u = 0; u < kVerifyBurst; ++u) {
+        const int c = cb + u * 256 * kPer;
+        if (c < c1) {
+          const T* e = reinterpret_cast<const T*>(&buf[u]);
+#pragma unroll
+          for (int q = 0; q < kPer; ++q) {
+            const float v = Store<T>::load(e[q]);
+            if (v > best) { best = v; bi = c + q; }
+          }
         }
       }
     }
@@ -441,7 +479,7 @@ __global__ __launch_bounds__(256) void verify_chunk_kernel(const T* __restrict__
   if (threadIdx.x == 0) {
     for (int w = 1; w < 4; ++w)
       if (better(sv[w], si[w], best, bi)) { best = sv[w]; bi = si[w]; }
-    part[static_cast<int64_t>(row) * n_chunks + chunk] = ArgPart{best, bi};
+    part[blockIdx.x] = ArgPart{best, bi};
   }
 }
 
@@ -479,25 +517,30 @@ __global__ __launch_bounds__(1024) void verify_scan_kernel(const ArgPart* __rest
   }
 }
 
+// rows * n_chunks <= rows * ceil(kVerifyWGs / rows) <= rows + kVerifyWGs, an
+// upper bound that grows with the row count (so a workspace sized for the
+// largest batch and block serves every smaller call).
 size_t verify_ws_bytes(int batch, int B, int V) {
-  const size_t n_chunks = (static_cast<size_t>(V) + kVerifyChunk - 1) / kVerifyChunk;
-  return static_cast<size_t>(batch) * B * n_chunks * sizeof(ArgPart);
+  (void)V;
+  return (static_cast<size_t>(batch) * B + kVerifyWGs) * sizeof(ArgPart);
 }
 
 hipError_t launch_verify(const void* logits, bool bf16, const int32_t* drafts, int batch, int B,
                          int V, int32_t* accept, int32_t* bonus, void* ws, hipStream_t st) {
-  const int n_chunks = (V + kVerifyChunk - 1) / kVerifyChunk;
+  const int rows = batch * B;
+  const int chunk = verify_chunk_cols(rows, V);
+  const int n_chunks = (V + chunk - 1) / chunk;
   ArgPart* part = static_cast<ArgPart*>(ws);
-  dim3 grid(n_chunks, batch * B);
-  const bool vec = (static_cast<size_t>(V) * (bf16 ? 2 : 4)) % 16 == 0;
+  const unsigned grid = static_cast<unsigned>(rows) * n_chunks;
+  const bool vec = V % 8 == 0;
   if (bf16) {
     auto p = static_cast<const uint16_t*>(logits);
-    if (vec) verify_chunk_kernel<uint16_t, true><<<grid, 256, 0, st>>>(p, V, part, n_chunks);
-    else verify_chunk_kernel<uint16_t, false><<<grid, 256, 0, st>>>(p, V, part, n_chunks);
+    if (vec) verify_chunk_kernel<uint16_t, true><<<grid, 256, 0, st>>>(p, V, chunk, part, n_chunks);
+    else verify_chunk_kernel<uint16_t, false><<<grid, 256, 0, st>>>(p, V, chunk, part, n_chunks);
   } else {
     auto p = static_cast<const float*>(logits);
-    if (vec) verify_chunk_kernel<float, true><<<grid, 256, 0, st>>>(p, V, part, n_chunks);
-    else verify_chunk_kernel<float, false><<<grid, 256, 0, st>>>(p, V, part, n_chunks);
+    if (vec) verify_chunk_kernel<float, true><<<grid, 256, 0, st>>>(p, V, chunk, part, n_chunks);
+    else verify_chunk_kernel<float, false><<<grid, 256, 0, st>>>(p, V, chunk, part, n_chunks);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
