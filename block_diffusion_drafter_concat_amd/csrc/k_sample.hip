@@ -114,6 +114,10 @@ __global__ __launch_bounds__(64) void gumbel_final_kernel(const SArg* __restrict
 // over one column chunk.  side 0: target rows [N*B][V] (bf16 or fp32); side 1:
 // drafter rows (fp32).  Thread t keeps columns c0 + 32 t .. +32 in registers
 // (16-byte loads): the chunk's max first, then one exponential per column.
+// Every exponential of this path (chunk sums, accept tests, sampling weights)
+// is the hardware one (exp2 of x * log2 e, relative error ~1e-6 for the
+// arguments that matter): with the library exponential the 78 M per-column
+// evaluations of a batch-16 call cost as much VALU time as the logits stream.
 template <typename T, bool kVecT, bool kVecD>
 __global__ __launch_bounds__(256) void lse_chunk_kernel(const T* __restrict__ tgt,
                                                        const float* __restrict__ drf, int V,
@@ -142,7 +146,7 @@ __global__ __launch_bounds__(256) void lse_chunk_kernel(const T* __restrict__ tg
   __syncthreads();
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) s += expf(x[i] - m);
+  for (int i = 0; i < 32; ++i) s += __expf(x[i] - m);
   s = wave_sum(s);
   if ((t & 63) == 0) red[t >> 6] = s;
   __syncthreads();
@@ -160,7 +164,7 @@ struct VerifyRec {
 };
 
 // One workgroup per sequence, wave j folds the chunks of target row j and
-// drafter row j; thread 0 walks the drafts.
+// drafter row j; thread k tests draft k; thread 0 walks the outcomes.
 template <typename T>
 __global__ __launch_bounds__(1024) void verify_walk_kernel(
     const T* __restrict__ tgt, const float* __restrict__ drf, const float2* __restrict__ part,
@@ -186,18 +190,26 @@ __global__ __launch_bounds__(1024) void verify_walk_kernel(
     }
   }
   __syncthreads();
-  if (threadIdx.x != 0) return;
+  // every draft's accept test at once (thread k takes draft k; a draft id
+  // outside [0, V) is never accepted and its loads use a clamped column), then
+  // thread 0 keeps the drafts up to the first rejection
+  __shared__ int s_ok[16];
   const int32_t* d = drafts + static_cast<int64_t>(n) * (B - 1);
   const float* rr = r + static_cast<int64_t>(n) * (B - 1);
-  int a = 0;
-  while (a < B - 1) {
-    const int x = d[a];
-    const float q = expf(ldf(tgt + (static_cast<int64_t>(n) * B + a) * V + x) * inv_t - s_mt[a]) / s_st[a];
-    const float p = expf(drf[(static_cast<int64_t>(n) * B + a + 1) * V + x] * inv_t - s_md[a + 1]) /
-                    s_sd[a + 1];
-    if (rr[a] * p < q) ++a;
-    else break;
+  if (threadIdx.x < B - 1) {
+    const int k = threadIdx.x;
+    const int x0 = d[k];
+    const int x = min(max(x0, 0), V - 1);
+    const float xt = ldf(tgt + (static_cast<int64_t>(n) * B + k) * V + x) * inv_t;
+    const float xd = drf[(static_cast<int64_t>(n) * B + k + 1) * V + x] * inv_t;
+    const float q = __expf(xt - s_mt[k]) / s_st[k];
+    const float p = __expf(xd - s_md[k + 1]) / s_sd[k + 1];
+    s_ok[k] = (x0 == x) && (rr[k] * p < q);
   }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  int a = 0;
+  while (a < B - 1 && s_ok[a]) ++a;
   accept[n] = a;
   VerifyRec v;
   v.a = a;
@@ -212,9 +224,9 @@ __global__ __launch_bounds__(1024) void verify_walk_kernel(
 // Weight of column c of sequence n's sampling row (see VerifyRec), from the
 // scaled logits xt (target row a) and xd (drafter row a + 1).
 __device__ __forceinline__ float sample_weight_x(const VerifyRec& v, float xt, float xd) {
-  const float q = expf(xt - v.mt) / v.st;
+  const float q = __expf(xt - v.mt) / v.st;
   if (!v.resid) return q;
-  return fmaxf(q - expf(xd - v.md) / v.sd, 0.f);
+  return fmaxf(q - __expf(xd - v.md) / v.sd, 0.f);
 }
 template <typename T>
 __device__ __forceinline__ float sample_weight(const T* __restrict__ tgt,
@@ -243,6 +255,26 @@ __device__ __forceinline__ float thread_run_sum(const T* tgt, const float* drf,
   return s;
 }
 
+// Inclusive prefix sum over the 256 threads of a workgroup in a fixed order:
+// a shuffle scan inside each wave, then the totals of the earlier waves added
+// left to right.  The chunk total of sample_sum_kernel and the running totals
+// of sample_pick_kernel both come from this one routine on the same values,
+// so thread 255's result is the chunk total bit for bit.
+__device__ __forceinline__ float block_incl_scan256(float x, float* s_wt /* [4] */) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_wt[w] = x;
+  __syncthreads();
+  float off = 0.f;
+  for (int k = 0; k < w; ++k) off += s_wt[k];
+  __syncthreads();
+  return off + x;
+}
+
 // Workgroup (chunk, sequence): total weight of the chunk.
 template <typename T, bool kVecT, bool kVecD>
 __global__ __launch_bounds__(256) void sample_sum_kernel(const T* __restrict__ tgt,
@@ -250,22 +282,22 @@ __global__ __launch_bounds__(256) void sample_sum_kernel(const T* __restrict__ t
                                                         const VerifyRec* __restrict__ rec, int B,
                                                         int V, float inv_t,
                                                         float* __restrict__ csum, int n_chunks) {
-  __shared__ float sv[256];
+  __shared__ float s_wt[4];
   const int chunk = blockIdx.x, n = blockIdx.y, t = threadIdx.x;
   const VerifyRec v = rec[n];
   const int c0 = chunk * kSampleChunk + t * 32;
-  sv[t] = c0 < V ? thread_run_sum<T, kVecT, kVecD>(tgt, drf, v, n, B, V, inv_t, c0) : 0.f;
-  __syncthreads();
-  if (t == 0) {
-    float s = 0.f;
-    for (int i = 0; i < 256; ++i) s += sv[i];
-    csum[static_cast<int64_t>(n) * n_chunks + chunk] = s;
-  }
+  const float x = c0 < V ? thread_run_sum<T, kVecT, kVecD>(tgt, drf, v, n, B, V, inv_t, c0) : 0.f;
+  const float incl = block_incl_scan256(x, s_wt);
+  if (t == 255) csum[static_cast<int64_t>(n) * n_chunks + chunk] = incl;
 }
 
 // One workgroup per sequence: the chunk where the running total passes
-// u * total, then the thread run, then the column.  A target past every
-// column of the chosen chunk (rounding between the two passes) takes the
+// u * total (thread 0, chunk sums in order), then the thread run (the first
+// run of positive weight whose running total passes the target, from the
+// workgroup scan), then the column (the first positive-weight column whose
+// running total inside the run passes it, from a wave scan).  A target past
+// every column of the chosen run (rounding between the two passes) takes the
+// run's last column of positive weight; past every run of the chunk, the
 // chunk's last column of positive weight.
 template <typename T, bool kVecT, bool kVecD>
 __global__ __launch_bounds__(256) void sample_pick_kernel(const T* __restrict__ tgt,
@@ -275,61 +307,80 @@ __global__ __launch_bounds__(256) void sample_pick_kernel(const T* __restrict__ 
                                                          const float* __restrict__ csum,
                                                          int n_chunks, const float* __restrict__ u,
                                                          int32_t* __restrict__ next_tok) {
-  __shared__ float sv[256];
+  constexpr int kRun = kSampleChunk / 256;   // columns per thread run
+  __shared__ float s_cs[256];
+  __shared__ float s_incl[256];
+  __shared__ float s_wt[4];
+  __shared__ int s_first[4], s_lastp[4];
   __shared__ int s_chunk;
   __shared__ float s_base, s_target;
-  const int n = blockIdx.x, t = threadIdx.x;
+  const int n = blockIdx.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const VerifyRec v = rec[n];
+  const float* cs = csum + static_cast<int64_t>(n) * n_chunks;
+  // chunk sums through LDS when they fit (one per thread), else read in place
+  const bool staged = n_chunks <= 256;
+  if (staged) s_cs[t] = t < n_chunks ? cs[t] : 0.f;
+  __syncthreads();
   if (t == 0) {
-    const float* cs = csum + static_cast<int64_t>(n) * n_chunks;
+    auto chunk_sum = [&](int c) { return staged ? s_cs[c] : cs[c]; };
     float tot = 0.f;
-    for (int c = 0; c < n_chunks; ++c) tot += cs[c];
+    for (int c = 0; c < n_chunks; ++c) tot += chunk_sum(c);
     const float target = u[n] * tot;
     float base = 0.f;
     int chosen = n_chunks - 1;
     for (int c = 0; c < n_chunks; ++c) {
-      if (base + cs[c] > target) { chosen = c; break; }
-      if (c < n_chunks - 1) base += cs[c];
+      if (base + chunk_sum(c) > target) { chosen = c; break; }
+      if (c < n_chunks - 1) base += chunk_sum(c);
     }
     // skip trailing empty chunks the fallback could land on
-    while (chosen > 0 && cs[chosen] <= 0.f) { --chosen; base -= cs[chosen]; }
+    while (chosen > 0 && chunk_sum(chosen) <= 0.f) { --chosen; base -= chunk_sum(chosen); }
     s_chunk = chosen;
     s_base = base;
     s_target = target;
   }
   __syncthreads();
   const int chunk = s_chunk;
-  const int c0 = chunk * kSampleChunk + t * 32;
-  sv[t] = c0 < V ? thread_run_sum<T, kVecT, kVecD>(tgt, drf, v, n, B, V, inv_t, c0) : 0.f;
+  const float base = s_base, target = s_target;
+  const int c0 = chunk * kSampleChunk + t * kRun;
+  const float x = c0 < V ? thread_run_sum<T, kVecT, kVecD>(tgt, drf, v, n, B, V, inv_t, c0) : 0.f;
+  const float incl = block_incl_scan256(x, s_wt);
+  s_incl[t] = incl;
+  // first run whose running total passes the target; last run of positive weight
+  const uint64_t hit = __ballot(x > 0.f && base + incl > target);
+  const uint64_t pos = __ballot(x > 0.f);
+  if (lane == 0) {
+    s_first[wv] = hit ? wv * 64 + __ffsll(static_cast<unsigned long long>(hit)) - 1 : 256;
+    s_lastp[wv] = pos ? wv * 64 + 63 - __clzll(static_cast<long long>(pos)) : -1;
+  }
   __syncthreads();
-  if (t == 0) {
-    float acc = s_base;
-    int run = -1, last_pos = -1;
-    for (int i = 0; i < 256; ++i) {
-      if (sv[i] > 0.f) last_pos = i;
-      if (run < 0 && acc + sv[i] > s_target) run = i;
-      if (run < 0) acc += sv[i];
-    }
+  if (t >= 64) return;
+  int run = min(min(s_first[0], s_first[1]), min(s_first[2], s_first[3]));
+  run = run < 256 ? run : -1;
+  const int last_pos = max(max(s_lastp[0], s_lastp[1]), max(s_lastp[2], s_lastp[3]));
+  // wave 0: lanes 0..31 weigh the columns of the chosen run, lanes 32..63
+  // those of the last run of positive weight
+  const int rsel = lane < kRun ? run : last_pos;
+  const int c = chunk * kSampleChunk + rsel * kRun + (lane % kRun);
+  const float w = (rsel >= 0 && c < V) ? sample_weight(tgt, drf, v, n, B, V, inv_t, c) : 0.f;
+  float wi = lane < kRun ? w : 0.f;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_up(wi, o, 64);
+    if (lane >= o) wi += y;
+  }
+  const float a2 = base + (run > 0 ? s_incl[run - 1] : 0.f);
+  const uint64_t chit = __ballot(lane < kRun && run >= 0 && w > 0.f && a2 + wi > target);
+  const uint64_t rpos = __ballot(lane < kRun && w > 0.f);
+  const uint64_t lpos = __ballot(lane >= kRun && w > 0.f);
+  if (lane == 0) {
     int col = -1;
     if (run >= 0) {
-      const int r0 = chunk * kSampleChunk + run * (kSampleChunk / 256);
-      const int r1 = min(V, r0 + kSampleChunk / 256);
-      float a2 = acc;
-      int lastc = -1;
-      for (int c = r0; c < r1; ++c) {
-        const float w = sample_weight(tgt, drf, v, n, B, V, inv_t, c);
-        if (w > 0.f) lastc = c;
-        if (a2 + w > s_target) { col = c; break; }
-        a2 += w;
-      }
-      if (col < 0) col = lastc;
+      const int r0 = chunk * kSampleChunk + run * kRun;
+      if (chit) col = r0 + __ffsll(static_cast<unsigned long long>(chit)) - 1;
+      else if (rpos) col = r0 + 63 - __clzll(static_cast<long long>(rpos));
     }
-    if (col < 0 && last_pos >= 0) {   // rounding left the target past the chunk
-      const int r0 = chunk * kSampleChunk + last_pos * (kSampleChunk / 256);
-      const int r1 = min(V, r0 + kSampleChunk / 256);
-      for (int c = r0; c < r1; ++c)
-        if (sample_weight(tgt, drf, v, n, B, V, inv_t, c) > 0.f) col = c;
-    }
+    if (col < 0 && last_pos >= 0 && lpos)   // rounding left the target past the chunk
+      col = chunk * kSampleChunk + last_pos * kRun + (63 - __clzll(static_cast<long long>(lpos))) - kRun;
     next_tok[n] = col < 0 ? 0 : col;
   }
 }

@@ -230,6 +230,7 @@ size_t dflash_verify_workspace_size(int32_t batch, int32_t block_size, int32_t v
  *   drafter row j; accept[n] = drafts kept (a); next_token[n] = the smallest
  *   column whose cumulative weight exceeds u[n] * total, the weights being
  *   (q_a - p_{a+1})_+ after a rejection and q_{B-1} after B-1 acceptances.
+ *   A draft id outside [0, vocab) is never accepted.
  *   target_logits: device [batch][B][vocab] in `dtype`, 16-byte aligned;
  *   draft_logits: device fp32 [batch][B][vocab]; r_accept: device fp32
  *   [batch][B-1] in [0, 1); u_sample: device fp32 [batch] in [0, 1);
