@@ -483,15 +483,19 @@ __global__ __launch_bounds__(256) void verify_chunk_kernel(const T* __restrict__
   }
 }
 
-// One workgroup per sequence, wave j folds the chunks of row j.
+// One workgroup per sequence, wave j folds the chunks of row j into the
+// target's token t_j and compares it with draft j (loaded before the fold, so
+// its latency overlaps); thread 0 then counts the leading matches.
 __global__ __launch_bounds__(1024) void verify_scan_kernel(const ArgPart* __restrict__ part,
                                                            int n_chunks, int B,
                                                            const int32_t* __restrict__ drafts,
                                                            int32_t* __restrict__ accept,
                                                            int32_t* __restrict__ bonus) {
   __shared__ int s_t[16];
+  __shared__ int s_match[16];
   const int b = blockIdx.x, j = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (j < B) {
+    const int dj = j < B - 1 ? drafts[static_cast<int64_t>(b) * (B - 1) + j] : -1;
     float best = -INFINITY;
     int bi = 0x7fffffff;
     const ArgPart* p = part + static_cast<int64_t>(b * B + j) * n_chunks;
@@ -505,13 +509,15 @@ __global__ __launch_bounds__(1024) void verify_scan_kernel(const ArgPart* __rest
       const int oi = __shfl_xor(bi, o, 64);
       if (better(ov, oi, best, bi)) { best = ov; bi = oi; }
     }
-    if (lane == 0) s_t[j] = bi;
+    if (lane == 0) {
+      s_t[j] = bi;
+      s_match[j] = j < B - 1 && bi == dj;
+    }
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    const int32_t* d = drafts + static_cast<int64_t>(b) * (B - 1);
     int a = 0;
-    while (a < B - 1 && s_t[a] == d[a]) ++a;
+    while (a < B - 1 && s_match[a]) ++a;
     accept[b] = a;
     bonus[b] = s_t[a];
   }

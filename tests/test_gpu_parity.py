@@ -85,6 +85,20 @@ def test_verify_ragged_and_degenerate(torch, V, B, dtype):
     _verify_case(torch, lg, drafts, dtype)
 
 
+def test_verify_many_rows_one_chunk_per_row(torch):
+    """2560 target rows (batch 160, B = 16): the first stage then takes every
+    row as a single chunk; V = 4096 (vector loads) with coarse values (ties)."""
+    N, B, V = 160, 16, 4096
+    g = np.random.default_rng(4096)
+    lg = np.round(g.standard_normal((N, B, V)) * 2).astype(np.float32)
+    drafts = g.integers(0, V, size=(N, B - 1))
+    for n in range(N):                 # matching prefixes of every length 0..15
+        for j in range(n % B):
+            drafts[n, j] = int(np.argmax(lg[n, j]))
+    got = _verify_case(torch, lg, drafts, "bf16")
+    assert set(got.tolist()) == set(range(B))
+
+
 # ------------------------------------------------------------------ fuse + inject
 
 def _fuse(torch, dr, shape, feats_np):

@@ -111,6 +111,32 @@ def test_verify_stochastic_matches_oracle(torch, N, B, V, T, dtype):
     print(f"accept {acc.tolist()} exempt {exempt}/{N}", flush=True)
 
 
+def test_verify_stochastic_rejects_out_of_range_drafts(torch):
+    """A draft id outside [0, V) is never accepted: with the drafter equal to the
+    target every in-range draft would be kept, so the accept count stops at the
+    first bad id (ids -1 and V at different positions)."""
+    N, B, V, T = 3, 8, 1000, 1.0
+    tl = synth.values((N, B, V), "f32", 73, synth.STREAM_LOGITS, "oor_t", std=2.0)
+    dl = np.empty_like(tl)
+    dl[:, 1:] = tl[:, :-1]
+    dl[:, 0] = tl[:, 0]
+    drafts = np.argmax(tl[:, :-1], axis=2).astype(np.int32)   # each row's mode
+    drafts[0, 0] = -1
+    drafts[1, 3] = V
+    drafts[2, 6] = V + 12345
+    r = np.full((N, B - 1), 0.5, dtype=np.float32)
+    u = np.full((N,), 0.5, dtype=np.float32)
+    ws = torch.empty(L.stochastic_workspace_size(N, B, V), dtype=torch.uint8, device="cuda")
+    acc = torch.full((N,), -1, dtype=torch.int32, device="cuda")
+    nxt = torch.full((N,), -1, dtype=torch.int32, device="cuda")
+    L.verify_stochastic(_t(torch, tl), _t(torch, dl), _t(torch, drafts, np.int32), T,
+                        _t(torch, r), _t(torch, u), acc, nxt, ws)
+    torch.cuda.synchronize()
+    assert acc.cpu().numpy().tolist() == [0, 3, 6]
+    n_ = nxt.cpu().numpy()
+    assert ((n_ >= 0) & (n_ < V)).all()
+
+
 def test_stochastic_path_is_lossless_on_device(torch):
     """20000 one-draft blocks: drafts sampled on the device from p, verified on
     the device against q; the first emitted token follows q."""
