@@ -409,6 +409,29 @@ hipError_t launch_tiled(const AOperand<uint16_t>& A, int N, int K, int parts, in
   return launch_tiled_cfg<kPreBM, kPreBN, 2, 4>(A, N, K, parts, ksplit, epi, st);
 }
 
+// LM head of a batch of blocks on the tiled GEMM.  One workgroup per compute
+// unit fits (LDS), so 256-column tiles run in rounds of kCUs tiles; when the
+// last round would be short, the vocabulary rows past the whole rounds go to
+// a second launch of 128-column tiles, which takes half as long per tile
+// (used when those fill at most one round).  `make(n_base, part_base)` builds
+// the epilogue of one launch.
+constexpr int kCUs = 256;   // compute units of the MI355X
+struct LmSplit {
+  int whole;     // 256-column tiles of the first launch (all of them when not split)
+  int n_tail;    // vocabulary rows of the second launch (0: not split)
+  int n_parts;   // per-row partials of both launches
+};
+inline LmSplit lm_split(int M, int V) {
+  const int bm = M <= 64 ? 64 : M <= 128 ? 128 : 256;
+  const int tm = (M + bm - 1) / bm;
+  const int ct = (V + 255) / 256;
+  const int whole = (tm * ct / kCUs) * kCUs / tm;   // 256-column tiles in whole rounds
+  const int n_tail = V - whole * 256;
+  const int ct_tail = (n_tail + 127) / 128;
+  if (whole < 1 || n_tail <= 0 || tm * ct_tail > kCUs) return LmSplit{ct, 0, ct};
+  return LmSplit{whole, n_tail, whole + ct_tail};
+}
+
 // A batch of blocks (M = 64 .. 256 rows): the row tile covers M.
 template <int BN, class Epi>
 hipError_t launch_mid(const AOperand<uint16_t>& A, int N, int K, int ksplit, const Epi& epi,
@@ -416,6 +439,17 @@ hipError_t launch_mid(const AOperand<uint16_t>& A, int N, int K, int ksplit, con
   if (A.M <= 64) return launch_tiled_cfg<64, BN, 1, 4>(A, N, K, 1, ksplit, epi, st);
   if (A.M <= 128) return launch_tiled_cfg<128, BN, 2, 4>(A, N, K, 1, ksplit, epi, st);
   return launch_tiled_cfg<256, BN, 2, 4>(A, N, K, 1, ksplit, epi, st);
+}
+
+// LM head over rows A (M = A.M) on the tiled GEMM, split as lm_split says.
+template <class MakeEpi>
+hipError_t launch_lm_tiled(const AOperand<uint16_t>& A, int V, int K, MakeEpi make,
+                           hipStream_t st) {
+  const LmSplit sp = lm_split(A.M, V);
+  if (sp.n_tail == 0) return launch_mid<256>(A, V, K, 1, make(0, 0), st);
+  hipError_t e = launch_mid<256>(A, sp.whole * 256, K, 1, make(0, 0), st);
+  if (e != hipSuccess) return e;
+  return launch_mid<128>(A, sp.n_tail, K, 1, make(sp.whole * 256, sp.whole), st);
 }
 
 struct NoPerLaunch {
@@ -790,10 +824,13 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
     DF_MARK(DFLASH_SEC_LM_GEMM, -1, false);
     if (mid) {
       // many block rows: the LDS-tiled GEMM, 256 vocabulary rows per tile
-      n_parts = (D.V + 255) / 256;
-      TEpiLoss e{static_cast<const uint16_t*>(h->w.lm_head), D.H, D.V, n_parts, B, lpart,
-                 tr->labels, dbg_z};
-      DF_HIP(launch_mid<256>(a16(u, D.H), D.V, D.H, 1, e, st));
+      n_parts = lm_split(M, D.V).n_parts;
+      const int np = n_parts;
+      auto make = [&](int n_base, int part_base) {
+        return TEpiLoss{static_cast<const uint16_t*>(h->w.lm_head), D.H, D.V, np, B, lpart,
+                        tr->labels, dbg_z, n_base, part_base};
+      };
+      DF_HIP(launch_lm_tiled(a16(u, D.H), D.V, D.H, make, st));
     }
     for (int m0 = 0; !mid && m0 < M; m0 += kMaxRowsPerLaunch) {
       AOperand<T> Ai = A;
@@ -821,10 +858,13 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
     EpiLMHead<T, 8> e8{static_cast<const T*>(h->w.lm_head), D.H, D.V, g.wg_lm, lm_part, dbg_z};
     const AOperand<T> A = a_frag<T>(u, D.H, M);
     if (mid) {
-      const int n_parts = (D.V + 255) / 256;
-      TEpiArgmax e{static_cast<const uint16_t*>(h->w.lm_head), D.H, D.V, n_parts, lm_part, dbg_z};
+      const int n_parts = lm_split(M, D.V).n_parts;
+      auto make = [&](int n_base, int part_base) {
+        return TEpiArgmax{static_cast<const uint16_t*>(h->w.lm_head), D.H, D.V, n_parts, lm_part,
+                          dbg_z, n_base, part_base};
+      };
       DF_MARK(DFLASH_SEC_LM_GEMM, -1, false);
-      DF_HIP(launch_mid<256>(a16(u, D.H), D.V, D.H, 1, e, st));
+      DF_HIP(launch_lm_tiled(a16(u, D.H), D.V, D.H, make, st));
       DF_MARK(DFLASH_SEC_LM_GEMM, -1, true);
       DF_HIP(launch_lm_argmax_finalize(lm_part, n_parts, M, B, draft, st));
     }

@@ -415,12 +415,15 @@ struct TEpiSwiGLUPair {
 // LM head of a batch of blocks: per row, the largest logit among the tile's
 // columns and its lowest column index -> part[m][tile] (value, index bits),
 // reduced over tiles by the finalize kernel; optionally every logit.
+// A launch may cover vocabulary rows [n_base, V) only (the tail of a split
+// LM head); its tile i writes partial part_base + i of each row.
 struct TEpiArgmax {
   const uint16_t* W;
   int K, V, n_parts;
   float2* part;
   float* dbg;   // [M][V] or null
-  __device__ WRows wrows(int, int n, int) const { return wrows_single(W, K, n, V); }
+  int n_base, part_base;
+  __device__ WRows wrows(int, int n, int) const { return wrows_single(W, K, n_base + n, V); }
   __device__ void store(const TiledSlice& s, void*, int t, int nt) const {
     const int lane = t & 63, wave = t >> 6, nw = nt >> 6;
     for (int lr = wave; lr < 64; lr += nw) {   // one wave per row
@@ -429,7 +432,7 @@ struct TEpiArgmax {
       float best = -INFINITY;
       int bi = 0x7fffffff;
       for (int c = lane; c < s.bn; c += 64) {
-        const int n = s.n0 + c;
+        const int n = n_base + s.n0 + c;
         if (n >= V) break;
         const float v = s.at(lr, c);
         if (dbg) dbg[static_cast<int64_t>(m) * V + n] = v;
@@ -442,7 +445,8 @@ struct TEpiArgmax {
         if (better(ov, oi, best, bi)) { best = ov; bi = oi; }
       }
       if (lane == 0)
-        part[static_cast<int64_t>(m) * n_parts + s.tile_n] = make_float2(best, __int_as_float(bi));
+        part[static_cast<int64_t>(m) * n_parts + part_base + s.tile_n] =
+            make_float2(best, __int_as_float(bi));
     }
   }
 };
@@ -457,7 +461,8 @@ struct TEpiLoss {
   float4* part;
   const int32_t* labels;
   float* dbg;   // [M][V] or null
-  __device__ WRows wrows(int, int n, int) const { return wrows_single(W, K, n, V); }
+  int n_base, part_base;   // as in TEpiArgmax
+  __device__ WRows wrows(int, int n, int) const { return wrows_single(W, K, n_base + n, V); }
   __device__ void store(const TiledSlice& s, void*, int t, int nt) const {
     const int lane = t & 63, wave = t >> 6, nw = nt >> 6;
     for (int lr = wave; lr < 64; lr += nw) {   // one wave per row
@@ -467,7 +472,7 @@ struct TEpiLoss {
       const int lab = j > 0 ? labels[(m / B) * (B - 1) + j - 1] : -1;
       float mx = -INFINITY, zl = -INFINITY;
       for (int c = lane; c < s.bn; c += 64) {
-        const int n = s.n0 + c;
+        const int n = n_base + s.n0 + c;
         if (n >= V) break;
         const float v = s.at(lr, c);
         if (dbg) dbg[static_cast<int64_t>(m) * V + n] = v;
@@ -481,12 +486,13 @@ struct TEpiLoss {
       }
       float sm = 0.f;
       for (int c = lane; c < s.bn; c += 64) {
-        if (s.n0 + c >= V) break;
+        if (n_base + s.n0 + c >= V) break;
         sm += expf(s.at(lr, c) - mx);
       }
       sm = wave_sum(sm);
       if (lane == 0)
-        part[static_cast<int64_t>(m) * n_parts + s.tile_n] = make_float4(mx, sm, zl, 0.f);
+        part[static_cast<int64_t>(m) * n_parts + part_base + s.tile_n] =
+            make_float4(mx, sm, zl, 0.f);
     }
   }
 };

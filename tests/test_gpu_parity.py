@@ -6,6 +6,8 @@ draft ids bit-exact wherever the oracle's top-2 logit gap is at least 1e-2
 (float32) or max(1e-2, 2 x the measured max logit difference) (bf16), and a
 near-argmax of the oracle's logits elsewhere (see gpu_util.draft_compare).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -251,6 +253,26 @@ def test_small_bf16_batch_of_blocks(torch, nb, B):
     ids, hid, z = _draft(torch, dr, shape, cache, B, anchors, ws)
     res = O.draft_block(w, shape, caches, anchors, B)
     draft_compare(shape, res, ids, hid, z, f"small-bf16 batch {nb} x B{B}")
+
+
+def test_small_bf16_batch_lm_head_split(torch):
+    """144 block rows against a 76900-token vocabulary: the LM head's 301
+    column tiles of 256 overflow one round of the 256 compute units, so the
+    rows past the first 256 tiles run as a second launch of 128-column tiles
+    (argmax partials of both launches, one finalize)."""
+    shape = dataclasses.replace(small_bf16_shape(), vocab=76900)
+    w = configs.make_weights(shape, 52)
+    dr = L.Drafter(shape, w)
+    nb, B = 9, 16
+    lens = [int(v) for v in synth.integers((nb,), 0, 300, 52, synth.STREAM_INDICES, "split_lens")]
+    caches = synthetic_cache(shape, 52, lens)
+    cache = L.KVCache(shape, [n + 32 for n in lens])
+    upload_cache(cache, caches)
+    anchors = configs.make_anchors(shape, 52, nb)
+    ws = dr.workspace(nb, B, 1)
+    ids, hid, z = _draft(torch, dr, shape, cache, B, anchors, ws)
+    res = O.draft_block(w, shape, caches, anchors, B)
+    draft_compare(shape, res, ids, hid, z, f"small-bf16 V=76900 batch {nb} x B{B}")
 
 
 def test_autoregressive_stand_in_steps(torch):

@@ -6,6 +6,8 @@ the logits of every slot, the per-slot cross-entropy and the weighted loss.
 The cross-entropy is 1-Lipschitz in each of log-sum-exp and the label logit,
 so |loss error| <= 2 max|logit error| bounds the loss comparison.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -85,6 +87,15 @@ def test_train_forward_matches_oracle(torch, which):
     wid = {"tiny": 61, "small": 62, "small_few_rows": 65}[which]
     want, z, slot, loss = _run(torch, shape, wid, lens, B, gamma, per_seq=per_seq)
     _check(shape, want, z, slot, loss, which)
+
+
+def test_train_forward_lm_head_split(torch):
+    """144 block rows against a 76900-token vocabulary: the cross-entropy
+    partials come from two LM-head launches (256-column tiles, then the tail on
+    128-column tiles)."""
+    shape = dataclasses.replace(small_bf16_shape(), vocab=76900)
+    want, z, slot, loss = _run(torch, shape, 66, [300, 0, 77], 16, 5.0)
+    _check(shape, want, z, slot, loss, "lm head split")
 
 
 def test_train_forward_anchor_extremes_and_shared_context(torch):
