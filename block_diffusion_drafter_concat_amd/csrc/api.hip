@@ -585,14 +585,26 @@ dflash_status inject_impl(dflash_handle* h, const void* ctx, const SeqTable& seq
     te.freq = epi.freq;
     te.seq = seq;
     const AOperand<uint16_t> At = a_single<uint16_t>(ctx, D.H, D.H, total);
-    // 256 x 256 tiles, or 256 x 128 when the former would not cover the 256
-    // compute units twice (the last partial round then weighs less)
-    const int64_t big_tiles = static_cast<int64_t>((total + kPreBM - 1) / kPreBM) *
-                              ((D.kvd + kPreBN - 1) / kPreBN) * 2 * D.L;
-    if (big_tiles < 512)
-      DF_HIP((launch_tiled_cfg<kPreBM, 128, 2, 4>(At, D.kvd, D.H, 2 * D.L, 1, te, st)));
-    else
-      DF_HIP(launch_tiled(At, D.kvd, D.H, 2 * D.L, 1, te, st));
+    // 256 x 256 tiles when they cover the 256 compute units at least twice.
+    // Fewer: the parts (layer, K or V) that fill whole rounds on 256 x 256
+    // tiles, the rest on 256 x 128 tiles in a second launch when those fit in
+    // one round (a short last round then costs half a tile's time: 2048 rows,
+    // 320 tiles = 8 parts in one round + 2 parts as 128 half tiles); else
+    // everything on 256 x 128 tiles.
+    const int parts = 2 * D.L;
+    const int64_t per_part = static_cast<int64_t>((total + kPreBM - 1) / kPreBM) *
+                             ((D.kvd + kPreBN - 1) / kPreBN);
+    const int64_t big_tiles = per_part * parts;
+    const int pa = static_cast<int>(big_tiles / kCUs * kCUs / per_part);
+    if (big_tiles >= 2 * kCUs) {
+      DF_HIP(launch_tiled(At, D.kvd, D.H, parts, 1, te, st));
+    } else if (pa >= 1 && pa < parts && (parts - pa) * per_part * 2 <= kCUs) {
+      DF_HIP(launch_tiled(At, D.kvd, D.H, pa, 1, te, st));
+      te.part_base = pa;
+      DF_HIP((launch_tiled_cfg<kPreBM, 128, 2, 4>(At, D.kvd, D.H, parts - pa, 1, te, st)));
+    } else {
+      DF_HIP((launch_tiled_cfg<kPreBM, 128, 2, 4>(At, D.kvd, D.H, parts, 1, te, st)));
+    }
   } else {
     DF_HIP(run_rows<T>(a_single<T>(ctx, D.H, D.H, total), D.H, g.tiles_inj, 1, 1, epi, st,
                        NoPerLaunch{}));

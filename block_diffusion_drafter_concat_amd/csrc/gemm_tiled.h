@@ -501,6 +501,7 @@ struct TEpiLoss {
 // 1: V); its N = Hkv * d columns are that layer's k (or v) projection.  K
 // gets RoPE at the row's position (the pair partner of column c is c + d/2);
 // V is stored transposed.  A tile's columns hold whole heads (bn % d == 0).
+// A launch may cover parts [part_base, part_base + gridDim.y) only.
 struct TEpiInject {
   const uint16_t* wk[kMaxLayers];
   const uint16_t* wv[kMaxLayers];
@@ -510,7 +511,9 @@ struct TEpiInject {
   int64_t cap;
   RopeFreq freq;
   SeqTable seq;
+  int part_base;
   __device__ WRows wrows(int part, int n, int N) const {
+    part += part_base;
     return wrows_single((part & 1) ? wv[part >> 1] : wk[part >> 1], K, n, N);
   }
   __device__ void store(const TiledSlice& s, void* ext, int t, int nt) const {
@@ -526,8 +529,9 @@ struct TEpiInject {
       row_t[t] = keep ? seq.off[b] + pos : -1;
     }
     __syncthreads();
-    if ((s.part & 1) == 0) {
-      uint16_t* kd = kc[s.part >> 1];
+    const int part = s.part + part_base;
+    if ((part & 1) == 0) {
+      uint16_t* kd = kc[part >> 1];
       const int half = d / 2, pairs = s.bn / 2;
       const int q = t % pairs;                  // RoPE pair of the tile
       const int hl = q / half, c = q % half;    // head inside the tile, pair index
@@ -545,7 +549,7 @@ struct TEpiInject {
         stf(dst + half, x1 * cs + x0 * sn);
       }
     } else {
-      uint16_t* vt = vc[s.part >> 1];
+      uint16_t* vt = vc[part >> 1];
       const int lr = t & 63;
       const int64_t r = row_t[lr];
       if (r < 0) return;
