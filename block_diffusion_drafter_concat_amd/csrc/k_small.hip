@@ -324,6 +324,7 @@ hipError_t launch_lm_loss(const float4* part, int n_wg, int rows, int B, float g
 // transposed; with block_rows, to rows b * kTrainSlab + j of a training
 // layout's block buffer instead).  grid.x runs over rows; the grid.y
 // workgroups of a row split its columns (few rows still spread over the GPU).
+constexpr int kQkvMaxSplit = 8;   // K-split slabs the finishing kernel sums
 template <typename T>
 __global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict__ part, int ks,
                                                          int64_t slab, int qd, int kvd, int d,
@@ -343,11 +344,20 @@ __global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict
   for (int p = blockIdx.y * 256 + threadIdx.x; p < total; p += gridDim.y * 256) {
     if (p < n_pairs) {
       const int c = p % half, col = (p / half) * d + c;   // [q heads | k heads] columns
-      float x0 = 0.f, x1 = 0.f;
-      for (int s = 0; s < ks; ++s) {
-        x0 += pr[s * slab + col];
-        x1 += pr[s * slab + col + half];
+      // every slab's value is loaded before the sums (in slab order) start
+      float a0[kQkvMaxSplit], a1[kQkvMaxSplit];
+#pragma unroll
+      for (int s = 0; s < kQkvMaxSplit; ++s) {
+        a0[s] = s < ks ? pr[s * slab + col] : 0.f;
+        a1[s] = s < ks ? pr[s * slab + col + half] : 0.f;
       }
+      float x0 = 0.f, x1 = 0.f;
+#pragma unroll
+      for (int s = 0; s < kQkvMaxSplit; ++s)
+        if (s < ks) {
+          x0 += a0[s];
+          x1 += a1[s];
+        }
       float cs, sn;
       rope_cos_sin(pos, c, freq, cs, sn);
       T* dst = col < qd ? q + static_cast<int64_t>(m) * ldq + col
@@ -356,8 +366,13 @@ __global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict
       stf(dst + half, x1 * cs + x0 * sn);
     } else {
       const int cv = p - n_pairs;
+      float a[kQkvMaxSplit];
+#pragma unroll
+      for (int s = 0; s < kQkvMaxSplit; ++s) a[s] = s < ks ? pr[s * slab + qd + kvd + cv] : 0.f;
       float x = 0.f;
-      for (int s = 0; s < ks; ++s) x += pr[s * slab + qd + kvd + cv];
+#pragma unroll
+      for (int s = 0; s < kQkvMaxSplit; ++s)
+        if (s < ks) x += a[s];
       stf(vc + static_cast<int64_t>(cv) * cap + row, x);
     }
   }
@@ -368,6 +383,7 @@ hipError_t launch_qkv_finish(bool bf16, const float* part, int ks, int64_t slab,
                              int64_t cap, const RopeFreq& freq, const SeqTable& seq,
                              hipStream_t st, bool block_rows) {
   if (rows <= 0) return hipSuccess;
+  if (ks < 1 || ks > kQkvMaxSplit) return hipErrorInvalidValue;
   // enough workgroups to cover the GPU when rows are few
   const int total = (qd + kvd) / 2 + kvd;
   const dim3 grid(rows, std::max(1, std::min((total + 255) / 256, 1024 / rows)));
