@@ -159,7 +159,7 @@ __global__ __launch_bounds__(WM * WN * 64) void tiled_gemm_kernel(AOperand<uint1
   constexpr int LA = BM / 16 / NWAVES, LW = BN / 16 / NWAVES;   // loads per wave per stage
   static_assert(LA * 16 * NWAVES == BM && LW * 16 * NWAVES == BN, "whole load instructions");
   constexpr int STAGE = (BM + BN) * kTBK;   // elements of one ring slot
-  constexpr int NS = tiled_stages(BM, BN);  // ring slots; NS - 2 stages in flight
+  constexpr int NS = tiled_stages(BM, BN);  // ring slots; NS - 1 stages in flight
   const int lrow = lane >> 2;
   const int gchunk = (lane & 3) ^ ((lane >> 3) & 3);
   const uint32_t a_voff = static_cast<uint32_t>(lrow * A.lda * 2 + gchunk * 16);
@@ -261,18 +261,20 @@ __global__ __launch_bounds__(WM * WN * 64) void tiled_gemm_kernel(AOperand<uint1
   };
   // vmcnt(n) for n < 64 (lgkmcnt and expcnt not waited)
   constexpr int kVm = LA + LW;   // this wave's loads per stage
-  static_assert(kVm * (tiled_stages(BM, BN) - 2) < 64, "vmcnt field");
+  static_assert(kVm * (tiled_stages(BM, BN) - 1) < 64, "vmcnt field");
 
-  // Pipeline.  Before step st: stages st+1 .. st+NS-2 in flight, fragments
-  // of st in registers.  Step st: wait for stage st+1 (the later ones stay in
+  // Pipeline.  Before step st: stages st+1 .. st+NS-1 in flight, fragments
+  // of st in registers (read from slot st % NS during step st-1, and waited
+  // for there).  Step st: wait for stage st+1 (the later ones stay in
   // flight), barrier (stage st+1 complete; every wave is past its reads of
-  // slot (st-1) % NS), load stage st+NS-1 into that slot, read the fragments
-  // of st+1, run the MFMAs of st, then wait for the fragment reads -- so
-  // values that cross the loop edge are always complete.
-  constexpr int kAhead = NS - 2;                     // stages in flight after a wait
+  // slot st % NS), load stage st+NS into that slot, read the fragments of
+  // st+1, run the MFMAs of st, then wait for the fragment reads -- so values
+  // that cross the loop edge are always complete.  Every slot but the one
+  // just freed holds a stage in flight or unread: NS-1 stages of prefetch.
+  constexpr int kAhead = NS - 1;                     // stages in flight before a wait
 #pragma unroll
-  for (int q = 0; q < NS - 1; ++q) issue();
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * kVm));   // stage 0 landed
+  for (int q = 0; q < NS; ++q) issue();
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * kVm));   // stage 0 landed
   __builtin_amdgcn_s_barrier();
   Frags f0, f1;
   // ring slot of the stage whose fragments are read next (stays on the last
