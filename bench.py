@@ -699,10 +699,30 @@ def main():
     blocks_per_s = BATCH * K / (gpu_ms / 1e3)
     log(f"timed: {K} steps, {ms_per_step:.3f} ms/step (wall {wall * 1e3 / K:.3f} ms/step)")
 
+
     # ---- kernel-timing pass: HIP events around each section, same steps
     if args.no_timing_pass:
         print(json.dumps({"value": round(blocks_per_s, 2), "ms_per_step": ms_per_step}))
         return
+
+    # ---- spread: 5 more repeats of the same K steps, timed the same way
+    rep_ms = []
+    for r in range(5):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(W, W + K):
+            step(i)
+        b.record()
+        torch.cuda.synchronize()
+        rep_ms.append(a.elapsed_time(b) / K)
+    repeats = {"repeats": 5, "steps_each": K,
+               "ms_per_step_median": round(float(np.median(rep_ms)), 4),
+               "ms_per_step_p10": round(float(np.percentile(rep_ms, 10)), 4),
+               "ms_per_step_p90": round(float(np.percentile(rep_ms, 90)), 4)}
+    log(f"repeats: {repeats}")
+
     sections = [("lm_head", -1), ("lm_gemm", -1), ("fuse_gemm", -1), ("inject", -1),
                 ("embed", -1), ("final_norm", -1)]
     for l in range(shape.n_layers):
@@ -814,6 +834,7 @@ def main():
         "draft_tokens_per_s": round(blocks_per_s * (BLOCK - 1), 1),
         "roofline": roofline,
         "step_roofline": step_roof,
+        "spread": repeats,
         "kernels": kernels,
         "prefill_mfma": prefill,
         "graph": graph,
