@@ -51,6 +51,10 @@ def parse():
                     help="skip the per-section timing pass (for counter collection)")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the batch-16 / long-context / 27B-shaped kernel measurements")
+    ap.add_argument("--kernel-probe", action="store_true",
+                    help="only run the kernels whose counters the profiles report (2048-row "
+                         "prefill fusion and injection, batch-16 ragged draft, 35K-context "
+                         "draft, batch-16 greedy verify), three calls each, and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, 5 times "
                          "(scale reference for HBM byte counters) and exit")
@@ -66,6 +70,54 @@ def calibrate_copy(mib: int) -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}), flush=True)
+
+
+def kernel_probe(torch, L, configs) -> None:
+    """Three calls each of the kernels the counter profiles cover, on the
+    Qwen3-8B-shaped drafter with device-drawn weights: the 2048-row prefill
+    fusion and injection (MFMA-bound), a batch-16 ragged draft and a 35K-context
+    draft (block attention), and a batch-16 greedy verify."""
+    shape = configs.QWEN3_8B_LIKE
+    dr = L.Drafter(shape, device_weights(torch, shape, 11))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(12)
+    feats = [torch.randn((CTX, shape.hidden), generator=g, device="cuda").to(torch.bfloat16)
+             for _ in range(shape.n_feat)]
+    ctx = torch.empty((CTX, shape.hidden), dtype=torch.bfloat16, device="cuda")
+    cache = L.KVCache(shape, [CTX + 64])
+    ws = dr.workspace(1, BLOCK, CTX)
+    for _ in range(3):
+        dr.fuse_context(feats, ctx, ws)
+        dr.inject_kv(ctx, [CTX], cache, ws, pos_start=[0])
+    torch.cuda.synchronize()
+    log("probe: prefill done")
+    del feats, ctx, cache, ws
+    for lens, seed in ((list(configs.qwen3_8b_b16_ragged().ctx), 3001), ([35000], 3002)):
+        cache = L.KVCache(shape, [n + 64 for n in lens])
+        fill_cache(torch, cache, lens, seed)
+        nb = len(lens)
+        anchors = torch.from_numpy(configs.make_anchors(shape, 2, nb)).cuda()
+        draft = torch.empty((nb, BLOCK - 1), dtype=torch.int32, device="cuda")
+        ws = dr.workspace(nb, BLOCK, 1)
+        for _ in range(3):
+            dr.draft_block(cache, BLOCK, anchors, draft, ws)
+        torch.cuda.synchronize()
+        log(f"probe: draft of {nb} sequence(s) done")
+        del cache, ws
+    nb = 16
+    logits = torch.randn((nb, BLOCK, shape.vocab), generator=g, device="cuda").to(torch.bfloat16)
+    drafts = torch.randint(0, shape.vocab, (nb, BLOCK - 1), generator=g, device="cuda",
+                           dtype=torch.int32)
+    acc = torch.empty(nb, dtype=torch.int32, device="cuda")
+    bon = torch.empty(nb, dtype=torch.int32, device="cuda")
+    vws = torch.empty(L.verify_workspace_size(nb, BLOCK, shape.vocab), dtype=torch.uint8,
+                      device="cuda")
+    for _ in range(3):
+        L.verify_greedy(logits, drafts, acc, bon, vws)
+    torch.cuda.synchronize()
+    dr.close()
+    log("probe: verify done")
+    print(json.dumps({"kernel_probe": "done"}), flush=True)
 
 
 def lm_head_traffic():
@@ -629,6 +681,9 @@ def main():
         calibrate_copy(args.calibrate_copy)
         return
     L.load()
+    if args.kernel_probe:
+        kernel_probe(torch, L, configs)
+        return
     shape = configs.QWEN3_8B_LIKE
     wid = 2
     K, W = args.steps, args.warmup
