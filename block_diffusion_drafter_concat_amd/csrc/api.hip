@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <functional>
 #include <atomic>
 #include <new>
 
@@ -95,6 +96,80 @@ int attn_chunk(const int32_t* keys, int nb, int n_kv, int max_keys, int max_c) {
     }
   }
   return best;
+}
+
+// Longest-first order for a ragged batch (host-held lengths, inference).
+// Workgroups go, in grid order, to the first of kAttnConcurrent free places;
+// listing every full chunk first and then the partial last chunks, largest
+// first, is a longest-first list schedule, in which the short jobs fill the
+// gaps the long ones leave.  attn_lpt_cost() is that schedule's makespan in
+// keys (a workgroup costs its keys + kAttnWgOverhead): after the full chunks
+// the places sit at two load levels; the partial chunks then go one by one to
+// the least loaded place (a heap).  *n_items = (sequence, chunk) entries.
+double attn_lpt_cost(const int32_t* keys, int nb, int n_kv, int chunk, int* n_items) {
+  int64_t full = 0;
+  int items = 0, np = 0;
+  int part[DFLASH_MAX_BATCH];
+  for (int b = 0; b < nb; ++b) {
+    const int nf = keys[b] / chunk, r = keys[b] - nf * chunk;
+    full += nf;
+    items += nf + (r > 0 ? 1 : 0);
+    if (r > 0) part[np++] = r;
+  }
+  *n_items = items;
+  std::sort(part, part + np, std::greater<int>());
+  const int64_t F = full * n_kv, S = kAttnConcurrent;
+  const double job = chunk + kAttnWgOverhead;
+  const int64_t q = F / S, rem = F % S;
+  double load[kAttnConcurrent];   // a min-heap of the places' loads
+  for (int64_t i = 0; i < S; ++i) load[i] = static_cast<double>(i < rem ? q + 1 : q) * job;
+  std::make_heap(load, load + S, std::greater<double>());
+  for (int k = 0; k < np; ++k)
+    for (int g = 0; g < n_kv; ++g) {
+      std::pop_heap(load, load + S, std::greater<double>());
+      load[S - 1] += part[k] + kAttnWgOverhead;
+      std::push_heap(load, load + S, std::greater<double>());
+    }
+  return *std::max_element(load, load + S);
+}
+
+// For a ragged batch: the chunk length (a multiple of 128, at most max_c
+// chunks per entry, at most kAttnOrderMax entries) that minimises that
+// makespan, and the order (full chunks by sequence, then the partial ones by
+// size, largest first, ties by sequence).  Near-uniform batches keep the grid
+// order and attn_chunk's choice.
+void attn_plan_order(const int32_t* keys, int nb, int n_kv, int max_keys, int max_c, int* chunk,
+                     AttnArgs* aa) {
+  int min_keys = max_keys;
+  for (int b = 0; b < nb; ++b) min_keys = std::min(min_keys, static_cast<int>(keys[b]));
+  if (4 * static_cast<int64_t>(max_keys) <= 5 * static_cast<int64_t>(min_keys)) return;
+  int lo = 128;
+  while ((max_keys + lo - 1) / lo > max_c) lo += 128;
+  const int hi = std::max(lo, (max_keys + 127) / 128 * 128);
+  int best = -1;
+  double best_cost = 0.0;
+  for (int c = hi; c >= lo; c -= 128) {
+    int items = 0;
+    const double cost = attn_lpt_cost(keys, nb, n_kv, c, &items);
+    if (items > kAttnOrderMax) continue;
+    if (best < 0 || cost < best_cost) {
+      best = c;
+      best_cost = cost;
+    }
+  }
+  if (best < 0) return;
+  *chunk = best;
+  int n = 0;
+  for (int b = 0; b < nb; ++b)
+    for (int c = 0; c < keys[b] / best; ++c) aa->order[n++] = static_cast<uint16_t>(b * 128 + c);
+  int idx[DFLASH_MAX_BATCH];
+  int np = 0;
+  for (int b = 0; b < nb; ++b)
+    if (keys[b] % best) idx[np++] = b;
+  std::stable_sort(idx, idx + np, [&](int x, int y) { return keys[x] % best > keys[y] % best; });
+  for (int k = 0; k < np; ++k)
+    aa->order[n++] = static_cast<uint16_t>(idx[k] * 128 + keys[idx[k]] / best);
+  aa->n_order = n;
 }
 
 // Rows per launch of the weight-streaming GEMM.
@@ -693,8 +768,10 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
   const int max_c = static_cast<int>(
       std::max<int64_t>(1, std::min<int64_t>(kMaxAttnChunks, attn_slots(nb, D.Hkv) / (nb * D.Hkv))));
   // (training: one chunk of every entry holds its block's keys)
-  const int chunk = attn_chunk(keys, nb, D.Hkv, max_keys, tr ? max_c - 1 : max_c);
+  int chunk = attn_chunk(keys, nb, D.Hkv, max_keys, tr ? max_c - 1 : max_c);
   AttnArgs aa{};
+  // ragged inference batches with host-held lengths: longest-first order
+  if (!tr && !dl) attn_plan_order(keys, nb, D.Hkv, max_keys, max_c, &chunk, &aa);
   aa.q = qb;
   aa.ldq = D.qd;
   aa.cap = kv->cap_total;

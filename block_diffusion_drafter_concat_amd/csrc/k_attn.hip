@@ -90,7 +90,8 @@ __global__ __launch_bounds__(NQ * 64) void block_attn_kernel(AttnArgs p) {
   constexpr int DT = D / 16;   // 16-row tiles of O^T
   constexpr int QR = NQ * 16;  // query rows (padded)
 
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  int c, g, b;
+  attn_wg_coords(p, c, g, b);
   const int qt = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r16 = lane & 15, kg = lane >> 4;
   const int B = p.B, G = p.G, GB = G * B;
@@ -265,7 +266,8 @@ __global__ __launch_bounds__(NQ * 64) void block_attn_dma_kernel(AttnArgs p) {
   static_assert(PERW * (NSLOT - 2) < 64, "vmcnt range");
   extern __shared__ __align__(16) uint16_t lds_ring[];
 
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  int c, g, b;
+  attn_wg_coords(p, c, g, b);
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6), qt = wave;
   const int r16 = lane & 15, kg = lane >> 4;
@@ -573,7 +575,7 @@ static hipError_t launch_attn_t(const AttnArgs& a, int nq, dim3 grid, int batch,
 hipError_t launch_block_attention(bool bf16, int head_dim, const AttnArgs& a, int batch,
                                   hipStream_t st) {
   const int nq = (a.G * a.B + 15) / 16;
-  dim3 grid(a.max_chunks, a.n_kv, batch);
+  const dim3 grid = a.n_order > 0 ? dim3(a.n_order * a.n_kv) : dim3(a.max_chunks, a.n_kv, batch);
   if (bf16) {
     if (head_dim == 128) return launch_attn_t<uint16_t, 128>(a, nq, grid, batch, st);
     if (head_dim == 64) return launch_attn_t<uint16_t, 64>(a, nq, grid, batch, st);

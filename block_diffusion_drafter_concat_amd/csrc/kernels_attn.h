@@ -5,6 +5,9 @@
 
 namespace dflash {
 
+// Longest-first order: at most this many (sequence, chunk) entries.
+constexpr int kAttnOrderMax = 256;
+
 struct AttnArgs {
   const void* q;        // [batch*B, n_q*D] block queries after RoPE
   int64_t ldq;          // row stride of q and o, elements
@@ -29,7 +32,28 @@ struct AttnArgs {
   const void* kb;
   const void* vb;
   int64_t capb;
+  // Longest-first order (n_order > 0): a 1-D grid of n_order * n_kv
+  // workgroups; workgroup w takes entry order[w / n_kv] = b * 128 + c (chunk c
+  // of sequence b) and kv head w % n_kv.  Otherwise grid (chunk, kv head, b).
+  int n_order;
+  uint16_t order[kAttnOrderMax];
 };
+
+// The (chunk, kv head, sequence) of this workgroup.
+__device__ __forceinline__ void attn_wg_coords(const AttnArgs& p, int& c, int& g, int& b) {
+  if (p.n_order > 0) {
+    const int w = blockIdx.x;
+    const int it = w / p.n_kv;
+    g = w - it * p.n_kv;
+    const int e = p.order[it];
+    b = e >> 7;
+    c = e & 127;
+  } else {
+    c = blockIdx.x;
+    g = blockIdx.y;
+    b = blockIdx.z;
+  }
+}
 
 // The keys workgroup c of entry b reads: a range of one source's rows.
 // Inference: keys [0, len + B) of the cache slab, in chunks.  Training
