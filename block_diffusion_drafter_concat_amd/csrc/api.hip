@@ -43,7 +43,7 @@ inline dflash_status hip_status(hipError_t e) { return e == hipSuccess ? DFLASH_
   } while (0)
 
 // Attention split: chunks per (sequence, kv head) at most kMaxAttnChunks, and
-// at most kAttnSlotBudget partial slots over the whole batch (or one chunk
+// at most kAttnSlotBudget partial slots over the whole batch (or two chunks
 // per (sequence, kv head) if the batch is larger).  The bf16 block-attention
 // kernel fits three workgroups on a compute unit, so kAttnConcurrent (3 x 256
 // CUs) of them run at once; attn_chunk() picks the chunk length.
@@ -53,7 +53,9 @@ constexpr int kAttnConcurrent = 768;
 constexpr int kAttnWgOverhead = 64;   // fixed cost of a workgroup, in keys
 int64_t attn_slots(int batch, int n_kv) {
   const int64_t all = static_cast<int64_t>(batch) * n_kv;
-  return std::min<int64_t>(all * kMaxAttnChunks, std::max<int64_t>(kAttnSlotBudget, all));
+  // at least two per entry: a training-layout block always has its own chunk
+  // besides at least one context chunk
+  return std::min<int64_t>(all * kMaxAttnChunks, std::max<int64_t>(kAttnSlotBudget, 2 * all));
 }
 // Keys per attention workgroup: a multiple of 128, at most max_c chunks per
 // (sequence, kv head), chosen to minimise an estimated makespan in units of
@@ -106,15 +108,21 @@ int attn_chunk(const int32_t* keys, int nb, int n_kv, int max_keys, int max_c) {
 // keys (a workgroup costs its keys + kAttnWgOverhead): after the full chunks
 // the places sit at two load levels; the partial chunks then go one by one to
 // the least loaded place (a heap).  *n_items = (sequence, chunk) entries.
-double attn_lpt_cost(const int32_t* keys, int nb, int n_kv, int chunk, int* n_items) {
+// extra > 0 (training layout): every entry has one more chunk of `extra` keys
+// (its block's own keys) after its context chunks.
+double attn_lpt_cost(const int32_t* keys, int nb, int n_kv, int chunk, int extra, int* n_items) {
   int64_t full = 0;
   int items = 0, np = 0;
-  int part[DFLASH_MAX_BATCH];
+  int part[2 * DFLASH_MAX_BATCH];
   for (int b = 0; b < nb; ++b) {
     const int nf = keys[b] / chunk, r = keys[b] - nf * chunk;
     full += nf;
     items += nf + (r > 0 ? 1 : 0);
     if (r > 0) part[np++] = r;
+    if (extra > 0) {
+      ++items;
+      part[np++] = extra;
+    }
   }
   *n_items = items;
   std::sort(part, part + np, std::greater<int>());
@@ -135,11 +143,13 @@ double attn_lpt_cost(const int32_t* keys, int nb, int n_kv, int chunk, int* n_it
 
 // For a ragged batch: the chunk length (a multiple of 128, at most max_c
 // chunks per entry, at most kAttnOrderMax entries) that minimises that
-// makespan, and the order (full chunks by sequence, then the partial ones by
-// size, largest first, ties by sequence).  Near-uniform batches keep the grid
-// order and attn_chunk's choice.
-void attn_plan_order(const int32_t* keys, int nb, int n_kv, int max_keys, int max_c, int* chunk,
-                     AttnArgs* aa) {
+// makespan, and the order (full chunks by sequence, then the partial ones --
+// and the block chunks of the training layout -- by size, largest first, ties
+// by sequence).  Near-uniform batches keep the grid order and attn_chunk's
+// choice.
+void attn_plan_order(const int32_t* keys, int nb, int n_kv, int max_keys, int max_c, int extra,
+                     int* chunk, AttnArgs* aa) {
+  if (max_c < 1) return;
   int min_keys = max_keys;
   for (int b = 0; b < nb; ++b) min_keys = std::min(min_keys, static_cast<int>(keys[b]));
   if (4 * static_cast<int64_t>(max_keys) <= 5 * static_cast<int64_t>(min_keys)) return;
@@ -150,7 +160,7 @@ void attn_plan_order(const int32_t* keys, int nb, int n_kv, int max_keys, int ma
   double best_cost = 0.0;
   for (int c = hi; c >= lo; c -= 128) {
     int items = 0;
-    const double cost = attn_lpt_cost(keys, nb, n_kv, c, &items);
+    const double cost = attn_lpt_cost(keys, nb, n_kv, c, extra, &items);
     if (items > kAttnOrderMax) continue;
     if (best < 0 || cost < best_cost) {
       best = c;
@@ -162,13 +172,19 @@ void attn_plan_order(const int32_t* keys, int nb, int n_kv, int max_keys, int ma
   int n = 0;
   for (int b = 0; b < nb; ++b)
     for (int c = 0; c < keys[b] / best; ++c) aa->order[n++] = static_cast<uint16_t>(b * 128 + c);
-  int idx[DFLASH_MAX_BATCH];
+  // the rest: (size, entry, chunk), largest first, then by entry
+  struct Rest {
+    int size, b, c;
+  };
+  Rest rest[2 * DFLASH_MAX_BATCH];
   int np = 0;
-  for (int b = 0; b < nb; ++b)
-    if (keys[b] % best) idx[np++] = b;
-  std::stable_sort(idx, idx + np, [&](int x, int y) { return keys[x] % best > keys[y] % best; });
-  for (int k = 0; k < np; ++k)
-    aa->order[n++] = static_cast<uint16_t>(idx[k] * 128 + keys[idx[k]] / best);
+  for (int b = 0; b < nb; ++b) {
+    const int nf = keys[b] / best, r = keys[b] - nf * best;
+    if (r > 0) rest[np++] = Rest{r, b, nf};
+    if (extra > 0) rest[np++] = Rest{extra, b, nf + (r > 0 ? 1 : 0)};
+  }
+  std::stable_sort(rest, rest + np, [](const Rest& x, const Rest& y) { return x.size > y.size; });
+  for (int k = 0; k < np; ++k) aa->order[n++] = static_cast<uint16_t>(rest[k].b * 128 + rest[k].c);
   aa->n_order = n;
 }
 
@@ -770,8 +786,15 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
   // (training: one chunk of every entry holds its block's keys)
   int chunk = attn_chunk(keys, nb, D.Hkv, max_keys, tr ? max_c - 1 : max_c);
   AttnArgs aa{};
-  // ragged inference batches with host-held lengths: longest-first order
-  if (!tr && !dl) attn_plan_order(keys, nb, D.Hkv, max_keys, max_c, &chunk, &aa);
+  // ragged batches with host-held lengths: longest-first order (training
+  // layout: entries' context keys, plus one chunk of their B block keys)
+  if (tr) {
+    int32_t ctx_keys[DFLASH_MAX_BATCH];
+    for (int b = 0; b < nb; ++b) ctx_keys[b] = seq.len[b];
+    attn_plan_order(ctx_keys, nb, D.Hkv, std::max(max_keys, 1), max_c - 1, B, &chunk, &aa);
+  } else if (!dl) {
+    attn_plan_order(keys, nb, D.Hkv, max_keys, max_c, 0, &chunk, &aa);
+  }
   aa.q = qb;
   aa.ldq = D.qd;
   aa.cap = kv->cap_total;
