@@ -419,15 +419,9 @@ hipError_t launch_lm_argmax_finalize(const float2* part, int n_wg, int rows, int
 // per CU), each thread's 16-byte loads go out in groups of kVerifyBurst
 // before any compare, and chunk boundaries are multiples of 8 columns, so a
 // 16-byte load never straddles two chunks or the row end when V % 8 == 0.
-#ifndef DFLASH_VERIFY_WGS
-#define DFLASH_VERIFY_WGS 2048
-#endif
-#ifndef DFLASH_VERIFY_BURST
-#define DFLASH_VERIFY_BURST 2
-#endif
-constexpr int kVerifyWGs = DFLASH_VERIFY_WGS;
+constexpr int kVerifyWGs = 2048;
 constexpr int kVerifyMinChunk = 2048;
-constexpr int kVerifyBurst = DFLASH_VERIFY_BURST;
+constexpr int kVerifyBurst = 2;
 struct ArgPart {
   float v;
   int i;
