@@ -155,10 +155,17 @@ void attn_plan_order(const int32_t* keys, int nb, int n_kv, int max_keys, int ma
   if (4 * static_cast<int64_t>(max_keys) <= 5 * static_cast<int64_t>(min_keys)) return;
   int lo = 128;
   while ((max_keys + lo - 1) / lo > max_c) lo += 128;
+  // fewer than kAttnOrderMax entries needs chunk >= sum(keys) / kAttnOrderMax
+  int64_t total = 0;
+  for (int b = 0; b < nb; ++b) total += keys[b];
+  const int64_t need = (total + kAttnOrderMax - 1) / kAttnOrderMax;
+  lo = std::max<int64_t>(lo, (need + 127) / 128 * 128);
   const int hi = std::max(lo, (max_keys + 127) / 128 * 128);
+  // at most 64 candidates, evenly spaced (host time stays well under a ms)
+  const int step = std::max(128, ((hi - lo) / 64 + 127) / 128 * 128);
   int best = -1;
   double best_cost = 0.0;
-  for (int c = hi; c >= lo; c -= 128) {
+  for (int c = hi; c >= lo; c -= step) {
     int items = 0;
     const double cost = attn_lpt_cost(keys, nb, n_kv, c, extra, &items);
     if (items > kAttnOrderMax) continue;
