@@ -275,6 +275,25 @@ def test_small_bf16_batch_lm_head_split(torch):
     draft_compare(shape, res, ids, hid, z, f"small-bf16 V=76900 batch {nb} x B{B}")
 
 
+def test_small_bf16_ragged_batch_attention_order_near_capacity(torch):
+    """48 sequences with contexts 54..2477 and B = 4 (M = 192 block rows): the
+    longest-first attention order is planned with chunks as small as 256 keys,
+    where the order table holds up to 254 of its 256 (sequence, chunk) entries."""
+    shape = small_bf16_shape()
+    w = configs.make_weights(shape, 53)
+    dr = L.Drafter(shape, w)
+    nb, B = 48, 4
+    lens = [int(v) for v in synth.integers((nb,), 0, 2500, 53, synth.STREAM_INDICES, "order_lens")]
+    caches = synthetic_cache(shape, 53, lens)
+    cache = L.KVCache(shape, [n + 32 for n in lens])
+    upload_cache(cache, caches)
+    anchors = configs.make_anchors(shape, 53, nb)
+    ws = dr.workspace(nb, B, 1)
+    ids, hid, z = _draft(torch, dr, shape, cache, B, anchors, ws)
+    res = O.draft_block(w, shape, caches, anchors, B)
+    draft_compare(shape, res, ids, hid, z, f"small-bf16 ragged {nb} x B{B}")
+
+
 def test_autoregressive_stand_in_steps(torch):
     """The autoregressive stand-in used for the draft-latency comparison: a
     1-layer drafter run as 2-slot passes, each pass's draft anchoring the
