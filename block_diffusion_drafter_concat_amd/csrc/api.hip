@@ -487,14 +487,10 @@ hipError_t launch_tiled_cfg(const AOperand<uint16_t>& A, int N, int K, int parts
   if (A.frag) return hipErrorInvalidValue;   // reads row-major slabs only
   auto kern = &tiled_gemm_kernel<BM, BN, WM, WN, Epi>;
   constexpr size_t lds = tiled_lds_bytes(BM, BN);
-  static std::atomic<bool> attr_set{false};
-  if (!attr_set.load()) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    attr_set.store(true);
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t e = set_dynamic_lds_once(lds_set, reinterpret_cast<const void*>(kern),
+                                            static_cast<int>(lds));
+  if (e != hipSuccess) return e;
   const int tm = (A.M + BM - 1) / BM, tn = (N + BN - 1) / BN;
   kern<<<dim3(tm * tn, parts, ksplit), WM * WN * 64, lds, st>>>(A, N, K, tm, tn, epi);
   return hipGetLastError();

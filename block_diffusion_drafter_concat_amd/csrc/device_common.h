@@ -14,7 +14,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace dflash {
+
+// Raise a kernel's dynamic-LDS limit to `bytes` on the current device, once
+// per device (the attribute is per device; `done` holds one bit per device
+// id below 64, larger ids set it on every launch).
+inline hipError_t set_dynamic_lds_once(std::atomic<uint64_t>& done, const void* kern, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (uint64_t{1} << dev) : 0;
+  if (bit && (done.load() & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit);
+  return e;
+}
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -542,13 +542,9 @@ static hipError_t launch_attn_nq(const AttnArgs& a, dim3 grid, int batch, hipStr
     constexpr int NS = attn_dma_slots<D>();
     constexpr int lds = NS * 2 * 32 * D * 2;
     auto kern = &block_attn_dma_kernel<D, NQ, NS>;
-    static std::atomic<bool> attr_set{false};
-    if (!attr_set.load()) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-      if (e != hipSuccess) return e;
-      attr_set.store(true);
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t e0 = set_dynamic_lds_once(lds_set, reinterpret_cast<const void*>(kern), lds);
+    if (e0 != hipSuccess) return e0;
     kern<<<grid, NQ * 64, lds, st>>>(a);
   } else {
     block_attn_kernel<T, D, NQ><<<grid, NQ * 64, 0, st>>>(a);
