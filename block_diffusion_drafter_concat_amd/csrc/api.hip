@@ -589,6 +589,9 @@ dflash_status check_kv(const dflash_handle* h, const dflash_kv* kv) {
   if (!kv || !kv->k || !kv->v || !kv->seq_off || !kv->seq_cap || !kv->seq_len)
     return DFLASH_ERR_INVALID_ARG;
   if (kv->batch < 1 || kv->batch > DFLASH_MAX_BATCH || kv->cap_total <= 0) return DFLASH_ERR_INVALID_ARG;
+  // one kv head's slab (cap_total rows of head_dim values) must be addressable
+  // by the 32-bit byte offsets of the attention kernel's buffer loads
+  if (kv->cap_total * h->cfg.head_dim >= (int64_t{1} << 30)) return DFLASH_ERR_UNSUPPORTED;
   for (int l = 0; l < h->cfg.n_layers; ++l)
     if (!kv->k[l] || !kv->v[l] || !aligned16(kv->k[l]) || !aligned16(kv->v[l]))
       return DFLASH_ERR_INVALID_ARG;
@@ -981,7 +984,7 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
       DF_MARK(DFLASH_SEC_LM_GEMM, -1, false);
       DF_HIP(launch_lm_tiled(a16(u, D.H), D.V, D.H, make, st));
       DF_MARK(DFLASH_SEC_LM_GEMM, -1, true);
-      DF_HIP(launch_lm_argmax_finalize(lm_part, n_parts, M, B, draft, st));
+      DF_HIP(launch_lm_argmax_finalize(lm_part, n_parts, M, B, anchors, D.V, draft, st));
     }
     // one launch covers M: the LM-GEMM timing point (if set) is recorded by
     // that dispatch; otherwise around the launches
@@ -1003,7 +1006,7 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
     }
     if (!mid) {
       if (!one) DF_MARK(DFLASH_SEC_LM_GEMM, -1, true);
-      DF_HIP(launch_lm_argmax_finalize(lm_part, n_wg, M, B, draft, st));
+      DF_HIP(launch_lm_argmax_finalize(lm_part, n_wg, M, B, anchors, D.V, draft, st));
     }
   }
   DF_MARK(DFLASH_SEC_LM_HEAD, -1, true);
@@ -1333,6 +1336,13 @@ dflash_status dflash_verify_greedy(const void* target_logits, dflash_dtype dtype
   return hip_status(launch_verify(target_logits, dtype == DFLASH_BF16, draft_ids, batch,
                                   block_size, vocab, accept, bonus, ws,
                                   static_cast<hipStream_t>(stream)));
+}
+
+dflash_status dflash_debug_bf16_round(const float* in, uint16_t* out, int64_t n, int32_t packed,
+                                      void* stream) {
+  if (!in || !out || n < 0 || (packed != 0 && packed != 1)) return DFLASH_ERR_INVALID_ARG;
+  if (!aligned16(in) || !aligned16(out) || (packed && n % 2)) return DFLASH_ERR_INVALID_ARG;
+  return hip_status(launch_bf16_round(in, out, n, packed, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

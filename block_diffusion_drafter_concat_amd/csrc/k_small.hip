@@ -196,6 +196,8 @@ hipError_t launch_resid_rmsnorm(bool bf16, float* x, const float* part, int n_sp
 // column) partials of the LM-head GEMM into the draft id of that slot.
 __global__ __launch_bounds__(256) void lm_argmax_finalize_kernel(const float2* __restrict__ part,
                                                                  int n_wg, int B,
+                                                                 const int32_t* __restrict__ anchors,
+                                                                 int V,
                                                                  int32_t* __restrict__ draft) {
   __shared__ float sv[4];
   __shared__ int si[4];
@@ -229,7 +231,10 @@ __global__ __launch_bounds__(256) void lm_argmax_finalize_kernel(const float2* _
   if (threadIdx.x == 0) {
     for (int w = 1; w < 4; ++w)
       if (better(sv[w], si[w], best, bi)) { best = sv[w]; bi = si[w]; }
-    draft[(m / B) * (B - 1) + (j - 1)] = bi;
+    // a block whose anchor lies outside [0, V) was embedded from a clamped
+    // row; its drafts are refused (-1) rather than passed off as a draft
+    const int32_t a = anchors ? anchors[m / B] : 0;
+    draft[(m / B) * (B - 1) + (j - 1)] = (a >= 0 && a < V) ? bi : -1;
   }
 }
 
@@ -400,10 +405,11 @@ hipError_t launch_qkv_finish(bool bf16, const float* part, int ks, int64_t slab,
   return hipGetLastError();
 }
 
-hipError_t launch_lm_argmax_finalize(const float2* part, int n_wg, int rows, int B, int32_t* draft,
+hipError_t launch_lm_argmax_finalize(const float2* part, int n_wg, int rows, int B,
+                                     const int32_t* anchors, int V, int32_t* draft,
                                      hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  lm_argmax_finalize_kernel<<<rows, 256, 0, st>>>(part, n_wg, B, draft);
+  lm_argmax_finalize_kernel<<<rows, 256, 0, st>>>(part, n_wg, B, anchors, V, draft);
   return hipGetLastError();
 }
 
@@ -592,4 +598,34 @@ hipError_t launch_advance_lengths(int32_t* len, const int32_t* accept, int n, in
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ bf16 rounding
+// The float32 -> bf16 rounding every kernel here stores with, exposed for
+// its test: packed = 0 takes the scalar conversion (f32_to_bf16), packed = 1
+// the pair conversion (f32x2_to_bf16x2) on elements (2i, 2i+1).
+__global__ __launch_bounds__(256) void bf16_round_kernel(const float* __restrict__ in,
+                                                         uint16_t* __restrict__ out, int64_t n,
+                                                         int packed) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  if (packed) {
+    const float2* in2 = reinterpret_cast<const float2*>(in);
+    uint32_t* out2 = reinterpret_cast<uint32_t*>(out);
+    for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n / 2; i += stride) {
+      const float2 v = in2[i];
+      out2[i] = f32x2_to_bf16x2(v.x, v.y);
+    }
+  } else {
+    for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += stride) out[i] = f32_to_bf16(in[i]);
+  }
+}
+
+hipError_t launch_bf16_round(const float* in, uint16_t* out, int64_t n, int packed,
+                             hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int64_t work = packed ? n / 2 : n;
+  const unsigned grid = static_cast<unsigned>(std::min<int64_t>((work + 255) / 256, 8192));
+  bf16_round_kernel<<<grid, 256, 0, st>>>(in, out, n, packed);
+  return hipGetLastError();
+}
+
 }  // namespace dflash
+

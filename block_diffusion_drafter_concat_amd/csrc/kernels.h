@@ -51,8 +51,10 @@ hipError_t launch_verify_stochastic(const void* target_logits, bool bf16, const 
                                     float temperature, const float* r, const float* u,
                                     int32_t* accept, int32_t* next_tok, void* ws, hipStream_t st);
 
-// Draft ids from the LM head's per-workgroup (value, index) partials [rows][n_wg].
-hipError_t launch_lm_argmax_finalize(const float2* part, int n_wg, int rows, int B, int32_t* draft,
+// Draft ids from the LM head's per-workgroup (value, index) partials [rows][n_wg];
+// the drafts of a block whose anchor (anchors[row / B]) is outside [0, V) are -1.
+hipError_t launch_lm_argmax_finalize(const float2* part, int n_wg, int rows, int B,
+                                     const int32_t* anchors, int V, int32_t* draft,
                                      hipStream_t st);
 
 // Greedy verify: per-chunk row argmax, then per-sequence prefix scan.
@@ -61,5 +63,9 @@ hipError_t launch_advance_lengths(int32_t* len, const int32_t* accept, int n, in
                                   int32_t* status, hipStream_t st);
 hipError_t launch_verify(const void* logits, bool bf16, const int32_t* drafts, int batch, int B,
                          int V, int32_t* accept, int32_t* bonus, void* ws, hipStream_t st);
+
+// float32 -> bf16 with the library's own rounding (scalar or pair conversion).
+hipError_t launch_bf16_round(const float* in, uint16_t* out, int64_t n, int packed,
+                             hipStream_t st);
 
 }  // namespace dflash

@@ -28,7 +28,7 @@ EXPORTS = ("dflash_target_layer_ids", "dflash_create", "dflash_destroy",
            "dflash_draft_block", "dflash_verify_greedy", "dflash_verify_workspace_size",
            "dflash_train_forward", "dflash_set_timing", "dflash_status_string",
            "dflash_stochastic_workspace_size", "dflash_sample_drafts",
-           "dflash_verify_stochastic", "dflash_step_resident")
+           "dflash_verify_stochastic", "dflash_step_resident", "dflash_debug_bf16_round")
 
 # dflash_section
 SECTIONS = {"fuse_gemm": 1, "fuse_norm": 2, "inject": 3, "embed": 4, "attn_norm": 5, "qkv": 6,
@@ -117,6 +117,8 @@ def load() -> C.CDLL:
     lib.dflash_verify_stochastic.argtypes = [vp, C.c_int, vp, vp, i32, i32, i32, C.c_float, vp,
                                              vp, vp, vp, vp, vp]
     lib.dflash_verify_stochastic.restype = C.c_int
+    lib.dflash_debug_bf16_round.argtypes = [vp, vp, i64, i32, vp]
+    lib.dflash_debug_bf16_round.restype = C.c_int
     lib.dflash_set_timing.argtypes = [vp, C.POINTER(TimingPoint), i32]
     lib.dflash_set_timing.restype = C.c_int
     lib.dflash_status_string.argtypes = [C.c_int]
@@ -325,6 +327,13 @@ def verify_stochastic(target_logits, draft_logits, draft_ids, temperature: float
                                            _ptr(r_accept), _ptr(u_sample), _ptr(accept),
                                            _ptr(next_token), _ptr(ws), _stream(stream)),
            "dflash_verify_stochastic")
+
+
+def debug_bf16_round(inp, out, packed: bool = False, stream=None) -> None:
+    """out (int16 / bfloat16 device tensor) = the library's bf16 rounding of
+    inp (float32 device tensor), by its scalar or its pair conversion."""
+    _check(load().dflash_debug_bf16_round(_ptr(inp), _ptr(out), int(inp.numel()), int(packed),
+                                          _stream(stream)), "dflash_debug_bf16_round")
 
 
 class KVCache:

@@ -117,7 +117,9 @@ typedef struct {
  * dflash_draft_block uses rows [seq_len[b], seq_len[b] + B) of each sequence as
  * scratch for the block's own K/V, so seq_cap[b] >= seq_len[b] + B is needed
  * there; those rows hold nothing committed.  dflash_inject_kv updates the host
- * array seq_len. */
+ * array seq_len.  cap_total * head_dim must stay below 2^30 (the attention
+ * kernel addresses one kv head's slab with 32-bit byte offsets); larger
+ * caches give DFLASH_ERR_UNSUPPORTED. */
 typedef struct {
   void *const *k;            /* (host) array [n_layers] of device pointers */
   void *const *v;            /* (host) array [n_layers] of device pointers */
@@ -177,8 +179,10 @@ dflash_status dflash_inject_kv(dflash_handle *h, const void *ctx, const int32_t 
  * attends to every slot; a block also sees its own sequence's committed
  * context and nothing else.  Draft j is the lowest-index argmax of slot j's
  * logits through the shared LM head.
- *   anchor_ids        (device) int32 [batch]; an id outside [0, vocab) is
- *                     clamped into range
+ *   anchor_ids        (device) int32 [batch]; a block whose anchor is outside
+ *                     [0, vocab) gets draft ids -1 (its rows are computed
+ *                     from a clamped embedding row, so nothing is read out
+ *                     of bounds, and its drafts are refused)
  *   draft_ids         (device) int32 [batch, B-1]
  *   dbg_final_hidden  (device) float [batch*B, H] or NULL: residual stream after
  *                     the last layer
@@ -354,6 +358,16 @@ typedef struct {
  * last.  The handle copies up to 32 points; n = 0 clears the hook.  For
  * profiling tools (the recorded events add stream markers, no other work). */
 dflash_status dflash_set_timing(dflash_handle *h, const dflash_timing_point *points, int32_t n);
+
+/* The float32 -> bf16 rounding (to nearest, ties to even; NaN stays NaN) that
+ * every kernel of the library applies where it stores bf16, exposed so that
+ * its rounding can be tested on every input.  out[i] = bf16 bits of in[i],
+ * i < n; packed = 0 uses the scalar conversion, packed = 1 the pair
+ * conversion (n even).  in, out: device, 16-byte aligned; enqueued on
+ * `stream`.  DFLASH_ERR_INVALID_ARG for null or misaligned pointers, n < 0,
+ * an odd n with packed = 1 or packed outside {0, 1}. */
+dflash_status dflash_debug_bf16_round(const float *in, uint16_t *out, int64_t n, int32_t packed,
+                                      void *stream);
 
 const char *dflash_status_string(dflash_status s);
 

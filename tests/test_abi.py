@@ -11,6 +11,8 @@ import oracle as O
 from block_diffusion_drafter_concat_amd import configs
 from block_diffusion_drafter_concat_amd import lib as L
 
+from conftest import gpu_available
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH),
@@ -20,7 +22,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH),
 def _declared_functions():
     src = open(os.path.join(ROOT, "include", "dflash.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(dflash_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(dflash_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_every_declared_symbol_is_exported():
@@ -286,3 +288,57 @@ def test_stochastic_host_checks():
                dict(acc=None), dict(nxt=None), dict(ws=None), dict(dtype=5), dict(T=0.0),
                dict(B=1), dict(ws=C.c_void_p(_FAKE + 4))):
         assert verify(**kw) == L.ERR_INVALID_ARG, kw
+
+
+def test_cache_slab_offset_bound():
+    """One kv head's slab must be addressable with 32-bit byte offsets:
+    cap_total * head_dim >= 2^30 is refused before anything is enqueued."""
+    lib = L.load()
+    shape = configs.QWEN3_8B_LIKE
+    st, h, keep = _create(shape)
+    assert st == L.OK
+    ws = C.c_void_p(_FAKE)
+    ids = C.c_void_p(_FAKE + 256)
+    big = (1 << 30) // shape.head_dim           # rows: exactly at the bound
+    kv, k1 = _kv(shape, [100], [big])
+    assert lib.dflash_draft_block(h, C.byref(kv), 16, ids, ids, None, None, ws, None) == \
+        L.ERR_UNSUPPORTED
+    n_new = (C.c_int32 * 1)(1)
+    assert lib.dflash_inject_kv(h, ids, None, n_new, C.byref(kv), ws, None) == L.ERR_UNSUPPORTED
+    assert k1[4][0] == 100
+    lib.dflash_destroy(h)
+
+
+def test_debug_bf16_round_host_checks():
+    lib = L.load()
+    p = C.c_void_p(_FAKE)
+    assert lib.dflash_debug_bf16_round(None, p, 8, 0, None) == L.ERR_INVALID_ARG
+    assert lib.dflash_debug_bf16_round(p, C.c_void_p(_FAKE + 2), 8, 0, None) == L.ERR_INVALID_ARG
+    assert lib.dflash_debug_bf16_round(p, p, 7, 1, None) == L.ERR_INVALID_ARG
+    assert lib.dflash_debug_bf16_round(p, p, -1, 0, None) == L.ERR_INVALID_ARG
+    assert lib.dflash_debug_bf16_round(p, p, 8, 2, None) == L.ERR_INVALID_ARG
+    assert lib.dflash_debug_bf16_round(p, p, 0, 0, None) == L.OK      # nothing to do
+
+
+@pytest.mark.skipif(gpu_available(), reason="the calls below pass device addresses that only a "
+                                            "machine without a GPU never dereferences")
+def test_launch_without_a_device_returns_hip_error():
+    """Calls whose arguments pass every host check reach their first launch;
+    with no HIP device that launch fails, and the call returns DFLASH_ERR_HIP
+    (and an inject leaves the host lengths alone)."""
+    lib = L.load()
+    p = C.c_void_p(_FAKE)
+    assert lib.dflash_verify_greedy(p, L.BF16, p, 2, 8, 1024, p, p, p, None) == L.ERR_HIP
+    assert lib.dflash_sample_drafts(p, 1, 8, 1024, C.c_float(0.7), p, p, p, None) == L.ERR_HIP
+    assert lib.dflash_debug_bf16_round(p, p, 64, 1, None) == L.ERR_HIP
+    shape = configs.TINY_F32
+    st, h, keep = _create(shape)
+    assert st == L.OK
+    feats = (C.c_void_p * 5)(*[_FAKE + i * 4096 for i in range(5)])
+    assert lib.dflash_fuse_context(h, feats, 4, p, p, None) == L.ERR_HIP
+    kv, k1 = _kv(shape, [10], [64])
+    n_new = (C.c_int32 * 1)(3)
+    assert lib.dflash_inject_kv(h, p, None, n_new, C.byref(kv), p, None) == L.ERR_HIP
+    assert k1[4][0] == 10
+    assert lib.dflash_draft_block(h, C.byref(kv), 8, p, p, None, None, p, None) == L.ERR_HIP
+    lib.dflash_destroy(h)

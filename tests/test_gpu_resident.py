@@ -13,8 +13,8 @@ draft that the two sides break differently then cannot change later steps.
 
 Bars: accept counts, bonus tokens (the next anchors) and device lengths
 bit-exact; the step's draft ids as in gpu_util.draft_compare (bit-exact
-where the oracle's top-2 logit gap clears a gate set by the measured logit
-difference, a near-argmax elsewhere), with the GPU logits and final hidden
+where the oracle's top-2 logit gap clears a fixed gate derived from the
+oracle's bf16 noise floor, a near-argmax elsewhere), with the GPU logits and final hidden
 states of the same state taken from a debug dflash_draft_block run; cache
 rows within 1e-4 (float32) or 2e-2 (bf16) max relative error per tensor.
 """
