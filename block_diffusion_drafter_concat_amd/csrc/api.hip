@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <functional>
 #include <atomic>
+#include <mutex>
 #include <new>
 
 #include <hip/hip_ext.h>
@@ -1053,6 +1054,38 @@ dflash_status step_impl(dflash_handle* h, dflash_kv* kv, int B, int32_t* dev_len
 
 }  // namespace
 
+// ------------------------------------------------------------- static scratch
+// The workspace of dflash_draft_block_noalloc, for callers that cannot
+// allocate: one array per device (each device that runs the call holds its
+// own copy until the process ends).  In host code the array's name is only a
+// stand-in for the device symbol; every use goes through the device address
+// hipGetSymbolAddress returns, looked up once per device with that device
+// current.  Nothing in a draft's workspace needs clearing (every slot read is
+// written earlier in the same call), so the array keeps whatever the last
+// call left; calls that overlap on one device race on it.
+static __device__ __align__(256) unsigned char scratch[DFLASH_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];
+
+dflash_status scratch_address(void** out) {
+  int dev = -1;
+  DF_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return DFLASH_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    DF_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return DFLASH_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return DFLASH_OK;
+}
+}  // namespace
+
 // ================================================================ C ABI
 
 extern "C" {
@@ -1076,6 +1109,7 @@ const char* dflash_status_string(dflash_status s) {
     case DFLASH_ERR_CAPACITY: return "cache capacity exceeded";
     case DFLASH_ERR_UNSUPPORTED: return "unsupported shape";
     case DFLASH_ERR_HIP: return "HIP runtime error";
+    case DFLASH_ERR_SCRATCH: return "needs more scratch than the static buffer holds";
   }
   return "unknown status";
 }
@@ -1196,6 +1230,23 @@ dflash_status dflash_draft_block(dflash_handle* h, dflash_kv* kv, int32_t block_
                                     dbg_logits, ws, st)
              : draft_impl<float>(h, kv, block_size, anchor_ids, draft_ids, dbg_final_hidden,
                                  dbg_logits, ws, st);
+}
+
+dflash_status dflash_draft_block_noalloc(dflash_handle* h, dflash_kv* kv, int32_t block_size,
+                                         const int32_t* anchor_ids, int32_t* draft_ids,
+                                         float* dbg_final_hidden, float* dbg_logits,
+                                         void* stream) {
+  if (!h || !anchor_ids || !draft_ids) return DFLASH_ERR_INVALID_ARG;
+  if (block_size < 2 || block_size > DFLASH_MAX_BLOCK) return DFLASH_ERR_INVALID_ARG;
+  dflash_status s = check_kv(h, kv);
+  if (s != DFLASH_OK) return s;
+  if (layout(h, kv->batch, block_size, 1).total > DFLASH_NOALLOC_SCRATCH_BYTES)
+    return DFLASH_ERR_SCRATCH;
+  void* ws = nullptr;
+  s = scratch_address(&ws);
+  if (s != DFLASH_OK) return s;
+  return dflash_draft_block(h, kv, block_size, anchor_ids, draft_ids, dbg_final_hidden,
+                            dbg_logits, ws, stream);
 }
 
 dflash_status dflash_train_forward(dflash_handle* h, const dflash_kv* kv, int32_t n_blocks,

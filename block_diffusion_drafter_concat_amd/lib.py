@@ -20,7 +20,8 @@ DFLASH_MAX_BLOCK = 16
 DFLASH_MAX_LAYERS = 16
 DFLASH_MAX_FEAT = 6
 
-OK, ERR_INVALID_ARG, ERR_CAPACITY, ERR_UNSUPPORTED, ERR_HIP = range(5)
+OK, ERR_INVALID_ARG, ERR_CAPACITY, ERR_UNSUPPORTED, ERR_HIP, ERR_SCRATCH = range(6)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 F32, BF16 = 0, 1
 
 EXPORTS = ("dflash_target_layer_ids", "dflash_create", "dflash_destroy",
@@ -28,7 +29,8 @@ EXPORTS = ("dflash_target_layer_ids", "dflash_create", "dflash_destroy",
            "dflash_draft_block", "dflash_verify_greedy", "dflash_verify_workspace_size",
            "dflash_train_forward", "dflash_set_timing", "dflash_status_string",
            "dflash_stochastic_workspace_size", "dflash_sample_drafts",
-           "dflash_verify_stochastic", "dflash_step_resident", "dflash_debug_bf16_round")
+           "dflash_verify_stochastic", "dflash_step_resident", "dflash_debug_bf16_round",
+           "dflash_draft_block_noalloc")
 
 # dflash_section
 SECTIONS = {"fuse_gemm": 1, "fuse_norm": 2, "inject": 3, "embed": 4, "attn_norm": 5, "qkv": 6,
@@ -100,6 +102,8 @@ def load() -> C.CDLL:
     lib.dflash_inject_kv.restype = C.c_int
     lib.dflash_draft_block.argtypes = [vp, C.POINTER(KV), i32, vp, vp, vp, vp, vp, vp]
     lib.dflash_draft_block.restype = C.c_int
+    lib.dflash_draft_block_noalloc.argtypes = [vp, C.POINTER(KV), i32, vp, vp, vp, vp, vp]
+    lib.dflash_draft_block_noalloc.restype = C.c_int
     lib.dflash_verify_greedy.argtypes = [vp, C.c_int, vp, i32, i32, i32, vp, vp, vp, vp]
     lib.dflash_verify_greedy.restype = C.c_int
     lib.dflash_verify_workspace_size.argtypes = [i32, i32, i32]
@@ -256,6 +260,13 @@ class Drafter:
                                            _ptr(dbg_logits), _ptr(ws), _stream(stream)),
                "dflash_draft_block")
 
+    def draft_block_noalloc(self, cache: "KVCache", block_size: int, anchors, draft_ids,
+                            dbg_hidden=None, dbg_logits=None, stream=None) -> None:
+        """draft_block on the library's static per-device scratch (no workspace)."""
+        _check(self.lib.dflash_draft_block_noalloc(self.handle, C.byref(cache.c), block_size,
+                                                   _ptr(anchors), _ptr(draft_ids),
+                                                   _ptr(dbg_hidden), _ptr(dbg_logits),
+                                                   _stream(stream)), "dflash_draft_block_noalloc")
 
     def train_forward(self, cache: "KVCache", block_size: int, block_seq, anchor_pos, anchor_ids,
                       labels, gamma: float, slot_loss, loss, ws, dbg_logits=None,

@@ -59,13 +59,16 @@ extern "C" {
 #define DFLASH_MAX_BLOCK 16      /* block slots B, anchor included */
 #define DFLASH_MAX_LAYERS 16     /* drafter layers */
 #define DFLASH_MAX_FEAT 6        /* fused target layers */
+#define DFLASH_NOALLOC_SCRATCH_BYTES (64u << 20)   /* static scratch per device */
 
 typedef enum {
   DFLASH_OK = 0,
   DFLASH_ERR_INVALID_ARG = 1,  /* null pointer, bad size, misaligned pointer */
   DFLASH_ERR_CAPACITY = 2,     /* a cache write would pass a sequence's capacity */
   DFLASH_ERR_UNSUPPORTED = 3,  /* shape the kernels do not cover (see dflash_config) */
-  DFLASH_ERR_HIP = 4           /* a HIP runtime call or launch failed */
+  DFLASH_ERR_HIP = 4,          /* a HIP runtime call or launch failed */
+  DFLASH_ERR_SCRATCH = 5       /* dflash_draft_block_noalloc: the call needs more scratch
+                                  than DFLASH_NOALLOC_SCRATCH_BYTES */
 } dflash_status;
 
 typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
@@ -197,6 +200,24 @@ dflash_status dflash_draft_block(dflash_handle *h, dflash_kv *kv, int32_t block_
                                  float *dbg_final_hidden, float *dbg_logits, void *ws,
                                  void *stream);
 
+/* dflash_draft_block without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, kernels and results as
+ * dflash_draft_block; the scratch is a library-owned static device array of
+ * DFLASH_NOALLOC_SCRATCH_BYTES (64 MiB) per device -- the current device's
+ * copy is used, so `stream` must belong to the current device.  A call whose
+ * workspace exceeds it (one sequence of 16 slots needs 37 MiB at the
+ * Qwen3-8B shape and 46 MiB at the 27B shape; the chunk partials of block
+ * attention grow with the batch, so larger batches at those shapes do not
+ * fit) returns DFLASH_ERR_SCRATCH before anything is enqueued.  Nothing is allocated:
+ * no hipMalloc, no hipFree.  Every call on a device shares that device's
+ * array, so calls that overlap on one device (two streams, two threads) race
+ * on it; serialise them.  The first call on a device looks up the array's
+ * device address (DFLASH_ERR_HIP if that fails). */
+dflash_status dflash_draft_block_noalloc(dflash_handle *h, dflash_kv *kv, int32_t block_size,
+                                         const int32_t *anchor_ids, int32_t *draft_ids,
+                                         float *dbg_final_hidden, float *dbg_logits,
+                                         void *stream);
 /* Greedy verification of one block per sequence.  t_j = lowest-index argmax of
  * target row j; accept[b] = the largest a <= B-1 with t_j == draft[b][j] for
  * all j < a; bonus[b] = t_a.  a + 1 tokens are committed (anchor and a drafts)

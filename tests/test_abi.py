@@ -341,4 +341,29 @@ def test_launch_without_a_device_returns_hip_error():
     assert lib.dflash_inject_kv(h, p, None, n_new, C.byref(kv), p, None) == L.ERR_HIP
     assert k1[4][0] == 10
     assert lib.dflash_draft_block(h, C.byref(kv), 8, p, p, None, None, p, None) == L.ERR_HIP
+    # the no-allocation draft fails at its first device call (the scratch lookup)
+    assert lib.dflash_draft_block_noalloc(h, C.byref(kv), 8, p, p, None, None, None) == L.ERR_HIP
+    lib.dflash_destroy(h)
+
+
+def test_noalloc_draft_host_checks():
+    """The no-allocation draft refuses a call whose workspace exceeds the
+    static scratch before it touches the device, and checks its arguments
+    like dflash_draft_block."""
+    lib = L.load()
+    shape = configs.QWEN3_8B_LIKE
+    st, h, keep = _create(shape)
+    assert st == L.OK
+    p = C.c_void_p(_FAKE)
+    kv, k1 = _kv(shape, [10] * 4, [64] * 4)         # 4 sequences: > 64 MiB of scratch
+    assert lib.dflash_draft_block_noalloc(h, C.byref(kv), 16, p, p, None, None, None) == \
+        L.ERR_SCRATCH
+    kv1, k2 = _kv(shape, [60], [64])
+    assert lib.dflash_draft_block_noalloc(h, C.byref(kv1), 1, p, p, None, None, None) == \
+        L.ERR_INVALID_ARG
+    assert lib.dflash_draft_block_noalloc(h, C.byref(kv1), 16, None, p, None, None, None) == \
+        L.ERR_INVALID_ARG
+    assert lib.dflash_draft_block_noalloc(h, None, 16, p, p, None, None, None) == \
+        L.ERR_INVALID_ARG
+    assert L.status_string(L.ERR_SCRATCH).startswith("needs more scratch")
     lib.dflash_destroy(h)
