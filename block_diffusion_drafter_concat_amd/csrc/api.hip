@@ -423,6 +423,7 @@ hipError_t launch_skinny_nw(const AOperand<T>& A, int K, int n_tiles, int tiles_
   if (A.slab_k % 32 != 0 || static_cast<int64_t>(K) * A.slab_k >= (int64_t{1} << 40))
     return hipErrorInvalidValue;
   const int mc = A.mc;
+  const bool slabs = A.slab_k < K;   // the fusion input: several feature slabs along K
   pt = skinny_pt(pt, mc);
   dim3 grid(skinny_wgs(n_tiles, tiles_per_wg, pt), ksplit);
   // with timing events, the dispatch records them itself (the span is the
@@ -432,14 +433,20 @@ hipError_t launch_skinny_nw(const AOperand<T>& A, int K, int n_tiles, int tiles_
   Epi e_arg = epi;
   void* argv[] = {&a_arg, &k_arg, &nt_arg, &tpw_arg, &e_arg};
   hipError_t ext = hipSuccess;
-#define DF_SK(MT, U, PT)                                                                        \
+#define DF_SK2(MT, U, PT, SL)                                                                   \
   do {                                                                                          \
     if (ev0)                                                                                    \
-      ext = hipExtLaunchKernel(reinterpret_cast<const void*>(&skinny_gemm_kernel<T, MT, U, NW, PT, Epi>), \
-                               grid, dim3(NW * 64), argv, 0, st, ev0, ev1, 0);                  \
+      ext = hipExtLaunchKernel(                                                                 \
+          reinterpret_cast<const void*>(&skinny_gemm_kernel<T, MT, U, NW, PT, Epi, SL>), grid,   \
+          dim3(NW * 64), argv, 0, st, ev0, ev1, 0);                                             \
     else                                                                                        \
-      skinny_gemm_kernel<T, MT, U, NW, PT, Epi><<<grid, NW * 64, 0, st>>>(A, K, n_tiles,         \
-                                                                          tiles_per_wg, epi);   \
+      skinny_gemm_kernel<T, MT, U, NW, PT, Epi, SL><<<grid, NW * 64, 0, st>>>(A, K, n_tiles,     \
+                                                                              tiles_per_wg, epi); \
+  } while (0)
+#define DF_SK(MT, U, PT)                  \
+  do {                                    \
+    if (slabs) DF_SK2(MT, U, PT, true);   \
+    else DF_SK2(MT, U, PT, false);        \
   } while (0)
   if (mc <= 16) {
     if (pt == 2) {
@@ -460,6 +467,7 @@ hipError_t launch_skinny_nw(const AOperand<T>& A, int K, int n_tiles, int tiles_
     return hipErrorInvalidValue;
   }
 #undef DF_SK
+#undef DF_SK2
   if (ext != hipSuccess) return ext;
   return hipGetLastError();
 }

@@ -14,10 +14,11 @@
 //     MFMA B fragments (16 bytes per lane, 64 contiguous bytes per row and
 //     instruction), double-buffered U steps deep to keep bytes in flight.
 //   - A (the small activation matrix) is read from L2 in A-fragment layout and
-//     may be split over several slabs along K (the fusion input needs no
-//     concatenation copy).  The slab of a 32-column step is picked with
+//     may be split over several slabs along K (SLABS; the fusion input needs
+//     no concatenation copy).  The slab of a 32-column step is picked with
 //     scalar arithmetic, so its pointer is one scalar load, not a per-lane
-//     load that every A fragment would wait behind.  An A written by the
+//     load that every A fragment would wait behind; a one-slab A (SLABS =
+//     false) needs no pick at all.  An A written by the
 //     drafter's own kernels is stored fragment-major (frag_major()): each
 //     fragment load is then one contiguous 16 x 32 run instead of 16 row
 //     pieces, which measured 10-15% faster on the M = 16 shapes.
@@ -45,7 +46,7 @@ struct AOperand {
   int m0, mc;         // this launch covers rows [m0, m0 + mc), mc <= 16 * MT
 };
 
-template <typename T, int MT, int U, int NW, int PT, class Epi>
+template <typename T, int MT, int U, int NW, int PT, class Epi, bool SLABS>
 __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(AOperand<T> A, int K, int n_tiles,
                                                               int tiles_per_wg, Epi epi) {
   __shared__ float red[NW][2][256];
@@ -62,6 +63,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(AOperand<T> A, int
   // elements between two 32-column steps of one row: 32 row-major, one
   // 16 x 32 chunk fragment-major
   const int kstep = A.frag ? 512 : 32;
+  const T* aslab0 = A.slab[0];
   int64_t aoff[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -108,8 +110,11 @@ __global__ __launch_bounds__(NW * 64) void skinny_gemm_kernel(AOperand<T> A, int
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int kk = kbeg + k + u * 32;
-        const int sl = static_cast<int>((static_cast<uint64_t>(kk) * slab_magic) >> 40);
-        const T* as = A.slab[sl] + static_cast<int64_t>((kk - sl * A.slab_k) >> 5) * kstep;
+        // one slab (every A but the fusion input): no slab pick, so no scalar
+        // load of the slab pointer sits on the step's critical path
+        const int sl = SLABS ? static_cast<int>((static_cast<uint64_t>(kk) * slab_magic) >> 40) : 0;
+        const T* as = (SLABS ? A.slab[sl] : aslab0) +
+                      static_cast<int64_t>((kk - sl * A.slab_k) >> 5) * kstep;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) ld_frag(a[buf][mt][u], as + aoff[mt]);
       }
