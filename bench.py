@@ -900,6 +900,18 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (as lscpu reports it), from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
 def cpu_baseline(shape, w, feats, new_feats_np, tau, logits, budget: float) -> dict:
     """Time the oracle's step (same workload) on the host, untuned."""
     import oracle as O
@@ -926,6 +938,7 @@ def cpu_baseline(shape, w, feats, new_feats_np, tau, logits, budget: float) -> d
         if el >= budget or done >= 50:
             break
     return {"value": round(done / el, 4), "unit": "blocks/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{done} oracle steps of the same workload (fuse+inject of the step's new "
                       f"rows, one 16-slot block through 5 layers at ctx 2048, LM-head argmax, "
                       f"verify), float64 numpy, {el:.1f}s"}
