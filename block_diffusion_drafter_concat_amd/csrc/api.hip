@@ -254,7 +254,9 @@ MidPlan mid_plan(const Dims& D, int M) {
   p.ks_qkv = mid_ksplit((nq + 127) / 128, D.H, nq * D.H * 2, static_cast<int64_t>(M) * nq * 4);
   // the residual-norm kernel sums up to 8 slabs for H <= 4096, 4 above
   const int max_rn = D.H <= 4096 ? 8 : 4;
-  p.ks_o = mid_ksplit((D.H + 127) / 128, D.qd, static_cast<int64_t>(D.H) * D.qd * 2,
+  // the O projection takes 128-row tiles above 128 rows (launch_mid_o)
+  const int tm_o = M > 128 ? (M + 127) / 128 : 1;
+  p.ks_o = mid_ksplit(tm_o * ((D.H + 127) / 128), D.qd, static_cast<int64_t>(D.H) * D.qd * 2,
                       static_cast<int64_t>(M) * D.H * 4, max_rn);
   p.ks_d = mid_ksplit((D.H + 127) / 128, D.F, static_cast<int64_t>(D.H) * D.F * 2,
                       static_cast<int64_t>(M) * D.H * 4, max_rn);
@@ -542,6 +544,19 @@ hipError_t launch_mid(const AOperand<uint16_t>& A, int N, int K, int ksplit, con
   if (A.M <= 64) return launch_tiled_cfg<64, BN, 1, 4>(A, N, K, 1, ksplit, epi, st);
   if (A.M <= 128) return launch_tiled_cfg<128, BN, 2, 4>(A, N, K, 1, ksplit, epi, st);
   return launch_tiled_cfg<256, BN, 2, 4>(A, N, K, 1, ksplit, epi, st);
+}
+
+// The O projection of a batch of blocks: above 128 rows, 128-row tiles (two
+// or more row tiles share each W column tile through L2 -- tiles go to XCDs
+// in groups of row tiles -- and the grid grows with them).  Measured at 256
+// block rows: 20.5 against 26.8 us per layer on 256-row tiles; at 1024 rows
+// 51 against 71 us.  The gate/up and down projections measured slower that
+// way (81 -> 100 and 51 -> 63 us at 256 rows) and keep the row tile = M.
+template <class Epi>
+hipError_t launch_mid_o(const AOperand<uint16_t>& A, int N, int K, int ksplit, const Epi& epi,
+                        hipStream_t st) {
+  if (A.M <= 128) return launch_mid<128>(A, N, K, ksplit, epi, st);
+  return launch_tiled_cfg<128, 128, 2, 4>(A, N, K, 1, ksplit, epi, st);
 }
 
 // LM head over rows A (M = A.M) on the tiled GEMM, split as lm_split says.
@@ -876,11 +891,11 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
       e.freq = freq;
       e.seq = seq;
       // no K split (the epilogue rotates whole sums and writes q and the
-      // cache rows itself): 8 waves per pair tile.  On the 8B shape (192
-      // tiles, 3/4 of the CUs) this measured 17.5 us against 19.5 us for
-      // four K-split slabs plus the finishing kernel.
+      // cache rows itself): 4 waves per pair tile.  On the 8B shape (192
+      // tiles, 3/4 of the CUs) this measured 16.0 us, against 16.9 us with 8
+      // waves and 19.5 us for four K-split slabs plus the finishing kernel.
       DF_HIP(run_rows<T>(a_frag<T>(u, D.H, M), D.H, g.tiles_qkv, 1, 1, e, st,
-                         NoPerLaunch{}, 8));
+                         NoPerLaunch{}, 4));
     }
     DF_MARK(DFLASH_SEC_QKV, l, true);
     aa.kc = kv->k[l];
@@ -891,7 +906,7 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
     DF_MARK(DFLASH_SEC_O_PROJ, l, false);
     if (mid) {
       TEpiStoreF32 e{static_cast<const uint16_t*>(w.wo), D.qd, part, D.H, M};
-      DF_HIP(launch_mid<128>(a16(ob, D.qd), D.H, D.qd, ks_o, e, st));
+      DF_HIP(launch_mid_o(a16(ob, D.qd), D.H, D.qd, ks_o, e, st));
     } else {
       EpiPartialF32<T> e{static_cast<const T*>(w.wo), D.qd, part, D.H, M};
       // two pair tiles per step share each A fragment (measured faster here,

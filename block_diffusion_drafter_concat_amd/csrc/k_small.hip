@@ -327,41 +327,48 @@ hipError_t launch_lm_loss(const float4* part, int n_wg, int rows, int B, float g
 // block position len[b] + j (pairs (c, c + d/2) of a head), store q to its
 // buffer and k, v to the layer's cache at row off[b] + len[b] + j (V
 // transposed; with block_rows, to rows b * kTrainSlab + j of a training
-// layout's block buffer instead).  grid.x runs over rows; the grid.y
-// workgroups of a row split its columns (few rows still spread over the GPU).
+// layout's block buffer instead).
+//   - q/k part: the first rows * ry workgroups, ry per row splitting its
+//     rotation pairs (few rows still spread over the GPU);
+//   - v part: one workgroup per (block, 64 value columns).  The transposed V
+//     cache keeps a column's positions contiguous, so the tile goes through
+//     LDS: loaded along columns (coalesced slab reads), stored along the
+//     block's slots (one 32-byte run per column for B = 16) instead of one
+//     scattered 2-byte store per value.
 constexpr int kQkvMaxSplit = 8;   // K-split slabs the finishing kernel sums
+constexpr int kQkvVCols = 64;     // value columns per v-part workgroup
 template <typename T>
 __global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict__ part, int ks,
                                                          int64_t slab, int qd, int kvd, int d,
-                                                         int B, T* __restrict__ q, int64_t ldq,
+                                                         int B, int rows, int ry,
+                                                         T* __restrict__ q, int64_t ldq,
                                                          T* __restrict__ kc, T* __restrict__ vc,
                                                          int64_t cap, RopeFreq freq, SeqTable seq,
                                                          bool block_rows) {
-  const int m = blockIdx.x, b = m / B, j = m % B;
-  const int pos = seq_len_of(seq, b) + j;
-  // training layout: the block's K/V go to its own rows of the block buffer
-  const int64_t row = block_rows ? static_cast<int64_t>(b) * kTrainSlab + j : seq.off[b] + pos;
   const int nq = qd + 2 * kvd, half = d / 2;
-  const float* pr = part + static_cast<int64_t>(m) * nq;
-  // flat work index: rotation pairs of the q and k columns, then v columns;
-  // grid.y workgroups share a row's work
-  const int n_pairs = (qd + kvd) / 2, total = n_pairs + kvd;
-  for (int p = blockIdx.y * 256 + threadIdx.x; p < total; p += gridDim.y * 256) {
-    if (p < n_pairs) {
-      const int c = p % half, col = (p / half) * d + c;   // [q heads | k heads] columns
+  const int wg = blockIdx.x;
+  if (wg < rows * ry) {
+    const int m = wg / ry, yy = wg % ry, b = m / B, j = m % B;
+    const int pos = seq_len_of(seq, b) + j;
+    // training layout: the block's K/V go to its own rows of the block buffer
+    const int64_t row = block_rows ? static_cast<int64_t>(b) * kTrainSlab + j : seq.off[b] + pos;
+    const float* pr = part + static_cast<int64_t>(m) * nq;
+    const int n_pairs = (qd + kvd) / 2;   // rotation pairs of [q heads | k heads]
+    for (int p = yy * 256 + threadIdx.x; p < n_pairs; p += ry * 256) {
+      const int c = p % half, col = (p / half) * d + c;
       // every slab's value is loaded before the sums (in slab order) start
       float a0[kQkvMaxSplit], a1[kQkvMaxSplit];
 #pragma unroll
-      for (int s = 0; s < kQkvMaxSplit; ++s) {
-        a0[s] = s < ks ? pr[s * slab + col] : 0.f;
-        a1[s] = s < ks ? pr[s * slab + col + half] : 0.f;
+      for (int s2 = 0; s2 < kQkvMaxSplit; ++s2) {
+        a0[s2] = s2 < ks ? pr[s2 * slab + col] : 0.f;
+        a1[s2] = s2 < ks ? pr[s2 * slab + col + half] : 0.f;
       }
       float x0 = 0.f, x1 = 0.f;
 #pragma unroll
-      for (int s = 0; s < kQkvMaxSplit; ++s)
-        if (s < ks) {
-          x0 += a0[s];
-          x1 += a1[s];
+      for (int s2 = 0; s2 < kQkvMaxSplit; ++s2)
+        if (s2 < ks) {
+          x0 += a0[s2];
+          x1 += a1[s2];
         }
       float cs, sn;
       rope_cos_sin(pos, c, freq, cs, sn);
@@ -369,18 +376,37 @@ __global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict
                         : kc + (static_cast<int64_t>((col - qd) / d) * cap + row) * d + c;
       stf(dst, x0 * cs - x1 * sn);
       stf(dst + half, x1 * cs + x0 * sn);
-    } else {
-      const int cv = p - n_pairs;
-      float a[kQkvMaxSplit];
-#pragma unroll
-      for (int s = 0; s < kQkvMaxSplit; ++s) a[s] = s < ks ? pr[s * slab + qd + kvd + cv] : 0.f;
+    }
+    return;
+  }
+  // v part: block b, value columns [c0, c0 + 64)
+  __shared__ float tile[16][kQkvVCols + 1];
+  const int vt = wg - rows * ry, n_ct = (kvd + kQkvVCols - 1) / kQkvVCols;
+  const int b = vt / n_ct, c0 = (vt % n_ct) * kQkvVCols;
+  const int t = threadIdx.x;
+  {
+    const int col = t % kQkvVCols, jr = t / kQkvVCols;   // 4 slots per pass
+    for (int j = jr; j < B; j += 256 / kQkvVCols) {
       float x = 0.f;
+      if (c0 + col < kvd) {
+        const float* pr = part + static_cast<int64_t>(b * B + j) * nq + qd + kvd + c0 + col;
+        float a[kQkvMaxSplit];
 #pragma unroll
-      for (int s = 0; s < kQkvMaxSplit; ++s)
-        if (s < ks) x += a[s];
-      stf(vc + static_cast<int64_t>(cv) * cap + row, x);
+        for (int s2 = 0; s2 < kQkvMaxSplit; ++s2) a[s2] = s2 < ks ? pr[s2 * slab] : 0.f;
+#pragma unroll
+        for (int s2 = 0; s2 < kQkvMaxSplit; ++s2)
+          if (s2 < ks) x += a[s2];
+      }
+      tile[j][col] = x;
     }
   }
+  __syncthreads();
+  const int64_t row0 = block_rows ? static_cast<int64_t>(b) * kTrainSlab
+                                  : seq.off[b] + seq_len_of(seq, b);
+  const int j = t % 16, cr = t / 16;   // 16 columns per pass
+  if (j < B)
+    for (int col = cr; col < kQkvVCols && c0 + col < kvd; col += 16)
+      stf(vc + static_cast<int64_t>(c0 + col) * cap + row0 + j, tile[j][col]);
 }
 
 hipError_t launch_qkv_finish(bool bf16, const float* part, int ks, int64_t slab, int rows, int qd,
@@ -388,16 +414,18 @@ hipError_t launch_qkv_finish(bool bf16, const float* part, int ks, int64_t slab,
                              int64_t cap, const RopeFreq& freq, const SeqTable& seq,
                              hipStream_t st, bool block_rows) {
   if (rows <= 0) return hipSuccess;
-  if (ks < 1 || ks > kQkvMaxSplit) return hipErrorInvalidValue;
-  // enough workgroups to cover the GPU when rows are few
-  const int total = (qd + kvd) / 2 + kvd;
-  const dim3 grid(rows, std::max(1, std::min((total + 255) / 256, 1024 / rows)));
+  if (ks < 1 || ks > kQkvMaxSplit || B > 16 || rows % B) return hipErrorInvalidValue;
+  // enough q/k workgroups to cover the GPU when rows are few
+  const int n_pairs = (qd + kvd) / 2;
+  const int ry = std::max(1, std::min((n_pairs + 255) / 256, 1024 / rows));
+  const int n_vwg = (rows / B) * ((kvd + kQkvVCols - 1) / kQkvVCols);
+  const dim3 grid(rows * ry + n_vwg);
   if (bf16)
     qkv_finish_kernel<uint16_t><<<grid, 256, 0, st>>>(
-        part, ks, slab, qd, kvd, d, B, static_cast<uint16_t*>(q), ldq,
+        part, ks, slab, qd, kvd, d, B, rows, ry, static_cast<uint16_t*>(q), ldq,
         static_cast<uint16_t*>(kc), static_cast<uint16_t*>(vc), cap, freq, seq, block_rows);
   else
-    qkv_finish_kernel<float><<<grid, 256, 0, st>>>(part, ks, slab, qd, kvd, d, B,
+    qkv_finish_kernel<float><<<grid, 256, 0, st>>>(part, ks, slab, qd, kvd, d, B, rows, ry,
                                                    static_cast<float*>(q), ldq,
                                                    static_cast<float*>(kc),
                                                    static_cast<float*>(vc), cap, freq, seq,
