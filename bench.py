@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-pack", action="store_true",
+                    help="leave the weights row-major (no dflash_pack_weights copy)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-timing-pass", action="store_true",
                     help="skip the per-section timing pass (for counter collection)")
@@ -78,7 +80,7 @@ def kernel_probe(torch, L, configs) -> None:
     fusion and injection (MFMA-bound), a batch-16 ragged draft and a 35K-context
     draft (block attention), and a batch-16 greedy verify."""
     shape = configs.QWEN3_8B_LIKE
-    dr = L.Drafter(shape, device_weights(torch, shape, 11))
+    dr = packed(torch, L.Drafter(shape, device_weights(torch, shape, 11)))
     g = torch.Generator(device="cuda")
     g.manual_seed(12)
     feats = [torch.randn((CTX, shape.hidden), generator=g, device="cuda").to(torch.bfloat16)
@@ -279,6 +281,18 @@ def kernel_report(shape, kern_ms: dict, M: int, kv_rows: int) -> dict:
             e.update({"bytes": kb[k], "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
         out[k] = e
     return out
+
+
+PACK = True   # pack the bf16 GEMM weights for the LDS-tiled GEMMs (--no-pack: off)
+
+
+def packed(torch, dr):
+    """dr with its fragment-major weight copy bound (bit-identical results;
+    faster loads on the LDS-tiled GEMMs of batches, prefill and training)."""
+    if PACK and dr.shape.dtype == "bf16":
+        dr.pack_weights(torch.empty(dr.packed_weights_size(), dtype=torch.uint8, device="cuda"))
+        torch.cuda.synchronize()
+    return dr
 
 
 def device_weights(torch, shape, seed: int) -> dict:
@@ -583,7 +597,7 @@ def workload_27b(torch, L, configs, reps: int) -> dict:
     context 4096 each, blocks of 8 and 16 slots."""
     shape = configs.TARGET_27B_LIKE
     w = device_weights(torch, shape, 5001)
-    dr = L.Drafter(shape, w)
+    dr = packed(torch, L.Drafter(shape, w))
     wl = configs.target27b_b8()
     lens = list(wl.ctx)
     cache = L.KVCache(shape, [n + 64 for n in lens])
@@ -661,7 +675,9 @@ def step_bytes(shape, n_new: int) -> dict:
 
 
 def main():
+    global PACK
     args = parse()
+    PACK = not args.no_pack
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: the library has no multi-GPU path "
@@ -690,7 +706,7 @@ def main():
 
     t0 = time.time()
     w = configs.make_weights(shape, wid)
-    dr = L.Drafter(shape, w)
+    dr = packed(torch, L.Drafter(shape, w))
     log(f"weights ready in {time.time() - t0:.1f}s")
 
     # prefill (untimed): fuse and inject the 2048-token context
@@ -884,7 +900,7 @@ def main():
                    "layers": shape.n_layers, "hidden": shape.hidden, "heads": "32q/8kv x 128",
                    "ffn": shape.ffn, "vocab": shape.vocab, "batch": BATCH, "ctx": CTX,
                    "block": BLOCK, "mean_new_tokens_per_step": round(mean_n, 2),
-                   "launch": "eager"},
+                   "launch": "eager", "packed_weights": PACK},
         "tokens_per_s": round(blocks_per_s * BLOCK, 1),
         "draft_tokens_per_s": round(blocks_per_s * (BLOCK - 1), 1),
         "roofline": roofline,

@@ -28,6 +28,12 @@ struct dflash_handle {
   dflash_layer_weights layers[DFLASH_MAX_LAYERS];
   dflash_timing_point timing[32];
   int n_timing;
+  // fragment-major copies of the bf16 GEMM weights in caller memory
+  // (dflash_pack_weights): the LDS-tiled GEMMs read these while `packed`
+  bool packed;
+  dflash_layer_weights pk_layers[DFLASH_MAX_LAYERS];   // wq, wk, wv, wo, wg, wu, wd
+  const void* pk_fc;
+  const void* pk_lm;
 };
 
 namespace {
@@ -492,10 +498,11 @@ hipError_t run_rows(AOperand<T> A, int K, int n_tiles, int tiles_per_wg, int ksp
   }
   return hipSuccess;
 }
+// wfrag: the epilogue's W pointers are packed (fragment-major) weights.
 template <int BM, int BN, int WM, int WN, class Epi>
 hipError_t launch_tiled_cfg(const AOperand<uint16_t>& A, int N, int K, int parts, int ksplit,
-                            const Epi& epi, hipStream_t st) {
-  if (A.frag) return hipErrorInvalidValue;   // reads row-major slabs only
+                            const Epi& epi, hipStream_t st, bool wfrag) {
+  if (A.frag && A.slab_k != K) return hipErrorInvalidValue;   // fragment-major: one slab
   auto kern = &tiled_gemm_kernel<BM, BN, WM, WN, Epi>;
   constexpr size_t lds = tiled_lds_bytes(BM, BN);
   static std::atomic<uint64_t> lds_set{0};
@@ -503,15 +510,16 @@ hipError_t launch_tiled_cfg(const AOperand<uint16_t>& A, int N, int K, int parts
                                             static_cast<int>(lds));
   if (e != hipSuccess) return e;
   const int tm = (A.M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-  kern<<<dim3(tm * tn, parts, ksplit), WM * WN * 64, lds, st>>>(A, N, K, tm, tn, epi);
+  kern<<<dim3(tm * tn, parts, ksplit), WM * WN * 64, lds, st>>>(A, N, K, tm, tn, wfrag ? 1 : 0,
+                                                                 epi);
   return hipGetLastError();
 }
 
 // Prefill fusion / injection: 256 x 256 tiles.
 template <class Epi>
 hipError_t launch_tiled(const AOperand<uint16_t>& A, int N, int K, int parts, int ksplit,
-                        const Epi& epi, hipStream_t st) {
-  return launch_tiled_cfg<kPreBM, kPreBN, 2, 4>(A, N, K, parts, ksplit, epi, st);
+                        const Epi& epi, hipStream_t st, bool wfrag) {
+  return launch_tiled_cfg<kPreBM, kPreBN, 2, 4>(A, N, K, parts, ksplit, epi, st, wfrag);
 }
 
 // LM head of a batch of blocks on the tiled GEMM.  One workgroup per compute
@@ -540,10 +548,10 @@ inline LmSplit lm_split(int M, int V) {
 // A batch of blocks (M = 64 .. 256 rows): the row tile covers M.
 template <int BN, class Epi>
 hipError_t launch_mid(const AOperand<uint16_t>& A, int N, int K, int ksplit, const Epi& epi,
-                      hipStream_t st) {
-  if (A.M <= 64) return launch_tiled_cfg<64, BN, 1, 4>(A, N, K, 1, ksplit, epi, st);
-  if (A.M <= 128) return launch_tiled_cfg<128, BN, 2, 4>(A, N, K, 1, ksplit, epi, st);
-  return launch_tiled_cfg<256, BN, 2, 4>(A, N, K, 1, ksplit, epi, st);
+                      hipStream_t st, bool wfrag) {
+  if (A.M <= 64) return launch_tiled_cfg<64, BN, 1, 4>(A, N, K, 1, ksplit, epi, st, wfrag);
+  if (A.M <= 128) return launch_tiled_cfg<128, BN, 2, 4>(A, N, K, 1, ksplit, epi, st, wfrag);
+  return launch_tiled_cfg<256, BN, 2, 4>(A, N, K, 1, ksplit, epi, st, wfrag);
 }
 
 // The O projection of a batch of blocks: above 128 rows, 128-row tiles (two
@@ -554,20 +562,20 @@ hipError_t launch_mid(const AOperand<uint16_t>& A, int N, int K, int ksplit, con
 // way (81 -> 100 and 51 -> 63 us at 256 rows) and keep the row tile = M.
 template <class Epi>
 hipError_t launch_mid_o(const AOperand<uint16_t>& A, int N, int K, int ksplit, const Epi& epi,
-                        hipStream_t st) {
-  if (A.M <= 128) return launch_mid<128>(A, N, K, ksplit, epi, st);
-  return launch_tiled_cfg<128, 128, 2, 4>(A, N, K, 1, ksplit, epi, st);
+                        hipStream_t st, bool wfrag) {
+  if (A.M <= 128) return launch_mid<128>(A, N, K, ksplit, epi, st, wfrag);
+  return launch_tiled_cfg<128, 128, 2, 4>(A, N, K, 1, ksplit, epi, st, wfrag);
 }
 
 // LM head over rows A (M = A.M) on the tiled GEMM, split as lm_split says.
 template <class MakeEpi>
 hipError_t launch_lm_tiled(const AOperand<uint16_t>& A, int V, int K, MakeEpi make,
-                           hipStream_t st) {
+                           hipStream_t st, bool wfrag) {
   const LmSplit sp = lm_split(A.M, V);
-  if (sp.n_tail == 0) return launch_mid<256>(A, V, K, 1, make(0, 0), st);
-  hipError_t e = launch_mid<256>(A, sp.whole * 256, K, 1, make(0, 0), st);
+  if (sp.n_tail == 0) return launch_mid<256>(A, V, K, 1, make(0, 0), st, wfrag);
+  hipError_t e = launch_mid<256>(A, sp.whole * 256, K, 1, make(0, 0), st, wfrag);
   if (e != hipSuccess) return e;
-  return launch_mid<128>(A, sp.n_tail, K, 1, make(sp.whole * 256, sp.whole), st);
+  return launch_mid<128>(A, sp.n_tail, K, 1, make(sp.whole * 256, sp.whole), st, wfrag);
 }
 
 struct NoPerLaunch {
@@ -658,8 +666,8 @@ dflash_status fuse_impl(dflash_handle* h, const void* const* feats, int64_t n_to
     AOperand<uint16_t> At{};
     for (int i = 0; i < 6; ++i) At.slab[i] = reinterpret_cast<const uint16_t*>(A.slab[i]);
     At.lda = A.lda; At.slab_k = A.slab_k; At.M = A.M; At.m0 = 0; At.mc = A.M;
-    TEpiStoreF32 te{static_cast<const uint16_t*>(h->w.fc), K, Y, D.H, T_};
-    DF_HIP(launch_tiled(At, D.H, K, 1, ks, te, st));
+    TEpiStoreF32 te{static_cast<const uint16_t*>(h->packed ? h->pk_fc : h->w.fc), K, Y, D.H, T_};
+    DF_HIP(launch_tiled(At, D.H, K, 1, ks, te, st, h->packed));
   } else {
     EpiPartialF32<T> epi{static_cast<const T*>(h->w.fc), K, Y, D.H, T_};
     DF_HIP(run_rows<T>(A, K, g.tiles_fc, 1, ks, epi, st, NoPerLaunch{}));
@@ -695,8 +703,8 @@ dflash_status inject_impl(dflash_handle* h, const void* ctx, const SeqTable& seq
   if (sizeof(T) == 2 && total >= kTiledMinRows) {
     TEpiInject te{};
     for (int l = 0; l < D.L; ++l) {
-      te.wk[l] = reinterpret_cast<const uint16_t*>(epi.wk[l]);
-      te.wv[l] = reinterpret_cast<const uint16_t*>(epi.wv[l]);
+      te.wk[l] = static_cast<const uint16_t*>(h->packed ? h->pk_layers[l].wk : h->layers[l].wk);
+      te.wv[l] = static_cast<const uint16_t*>(h->packed ? h->pk_layers[l].wv : h->layers[l].wv);
       te.kc[l] = reinterpret_cast<uint16_t*>(epi.kc[l]);
       te.vc[l] = reinterpret_cast<uint16_t*>(epi.vc[l]);
     }
@@ -717,14 +725,15 @@ dflash_status inject_impl(dflash_handle* h, const void* ctx, const SeqTable& seq
                              ((D.kvd + kPreBN - 1) / kPreBN);
     const int64_t big_tiles = per_part * parts;
     const int pa = static_cast<int>(big_tiles / kCUs * kCUs / per_part);
+    const bool pk = h->packed;
     if (big_tiles >= 2 * kCUs) {
-      DF_HIP(launch_tiled(At, D.kvd, D.H, parts, 1, te, st));
+      DF_HIP(launch_tiled(At, D.kvd, D.H, parts, 1, te, st, pk));
     } else if (pa >= 1 && pa < parts && (parts - pa) * per_part * 2 <= kCUs) {
-      DF_HIP(launch_tiled(At, D.kvd, D.H, pa, 1, te, st));
+      DF_HIP(launch_tiled(At, D.kvd, D.H, pa, 1, te, st, pk));
       te.part_base = pa;
-      DF_HIP((launch_tiled_cfg<kPreBM, 128, 2, 4>(At, D.kvd, D.H, parts - pa, 1, te, st)));
+      DF_HIP((launch_tiled_cfg<kPreBM, 128, 2, 4>(At, D.kvd, D.H, parts - pa, 1, te, st, pk)));
     } else {
-      DF_HIP((launch_tiled_cfg<kPreBM, 128, 2, 4>(At, D.kvd, D.H, parts, 1, te, st)));
+      DF_HIP((launch_tiled_cfg<kPreBM, 128, 2, 4>(At, D.kvd, D.H, parts, 1, te, st, pk)));
     }
   } else {
     DF_HIP(run_rows<T>(a_single<T>(ctx, D.H, D.H, total), D.H, g.tiles_inj, 1, 1, epi, st,
@@ -792,14 +801,17 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
   const int64_t pstride = static_cast<int64_t>(M) * D.H;   // one K-split slab
   // batches of blocks: the layer GEMMs and the LM head on the LDS-tiled GEMM
   const bool mid = bf && M >= kMidMinRows;
-  // u, h and the attention output feed the weight-streaming GEMM
-  // (fragment-major) unless the LDS-tiled one takes this many rows
-  const bool frag = !mid;
+  // u, h and the attention output are stored fragment-major for either GEMM
+  // (one contiguous 1 KB block per 16 rows x 32 columns an operand load reads)
+  const bool frag = true;
+  // the LDS-tiled GEMMs read the packed weights when the caller made them
+  const bool pk = h->packed;
   const MidPlan mp = mid_plan(D, M);
   const int ks_o = mid ? mp.ks_o : g.ks_o, ks_d = mid ? mp.ks_d : g.ks_d;
   float* qkvp = at<float>(ws, L.qkvp_off);
-  auto a16 = [&](const void* p, int K) {
-    return a_single<uint16_t>(p, K, K, M);
+  auto a16 = [&](const void* p, int K) { return a_frag<uint16_t>(p, K, M); };
+  auto w16 = [&](const void* raw, const void* packed) {
+    return static_cast<const uint16_t*>(pk ? packed : raw);
   };
 
   // block embedding fused with layer 0's attention RMSNorm
@@ -851,6 +863,7 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
   int pending = 0;   // K-split slabs of the last projection, not yet added to x
   for (int l = 0; l < D.L; ++l) {
     const dflash_layer_weights& w = h->layers[l];
+    const dflash_layer_weights& wp = h->pk_layers[l];
     // attention half: x += (down partials of the previous layer); u = RMSNorm(x)
     if (l > 0) {
       DF_MARK(DFLASH_SEC_ATTN_NORM, l, false);
@@ -861,9 +874,9 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
     DF_MARK(DFLASH_SEC_QKV, l, false);
     if (mid) {
       const int nq = D.qd + 2 * D.kvd;
-      TEpiQKVParts e{static_cast<const uint16_t*>(w.wq), static_cast<const uint16_t*>(w.wk),
-                     static_cast<const uint16_t*>(w.wv), D.H, D.qd, D.kvd, qkvp, nq, M};
-      DF_HIP(launch_mid<128>(a16(u, D.H), nq, D.H, mp.ks_qkv, e, st));
+      TEpiQKVParts e{w16(w.wq, wp.wq), w16(w.wk, wp.wk), w16(w.wv, wp.wv), D.H, D.qd, D.kvd,
+                     qkvp, nq, M};
+      DF_HIP(launch_mid<128>(a16(u, D.H), nq, D.H, mp.ks_qkv, e, st, pk));
       DF_HIP(launch_qkv_finish(true, qkvp, mp.ks_qkv, static_cast<int64_t>(M) * nq, M, D.qd,
                                D.kvd, D.d, B, qb, D.qd, kdst(l), vdst(l), dcap, freq, seq, st,
                                tr != nullptr));
@@ -905,8 +918,8 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
     DF_MARK(DFLASH_SEC_ATTENTION, l, true);
     DF_MARK(DFLASH_SEC_O_PROJ, l, false);
     if (mid) {
-      TEpiStoreF32 e{static_cast<const uint16_t*>(w.wo), D.qd, part, D.H, M};
-      DF_HIP(launch_mid_o(a16(ob, D.qd), D.H, D.qd, ks_o, e, st));
+      TEpiStoreF32 e{w16(w.wo, wp.wo), D.qd, part, D.H, M};
+      DF_HIP(launch_mid_o(a16(ob, D.qd), D.H, D.qd, ks_o, e, st, pk));
     } else {
       EpiPartialF32<T> e{static_cast<const T*>(w.wo), D.qd, part, D.H, M};
       // two pair tiles per step share each A fragment (measured faster here,
@@ -923,9 +936,9 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
     DF_MARK(DFLASH_SEC_FFN_NORM, l, true);
     DF_MARK(DFLASH_SEC_GATE_UP, l, false);
     if (mid) {
-      TEpiSwiGLUPair e{static_cast<const uint16_t*>(w.wg), static_cast<const uint16_t*>(w.wu),
-                       D.H, D.F, 128, reinterpret_cast<uint16_t*>(hb), D.F};
-      DF_HIP(launch_mid<128>(a16(u, D.H), 2 * D.F, D.H, 1, e, st));
+      TEpiSwiGLUPair e{w16(w.wg, wp.wg), w16(w.wu, wp.wu), D.H, D.F, 128,
+                       reinterpret_cast<uint16_t*>(hb), D.F, 1};
+      DF_HIP(launch_mid<128>(a16(u, D.H), 2 * D.F, D.H, 1, e, st, pk));
     } else {
       EpiSwiGLU<T> e{static_cast<const T*>(w.wg), static_cast<const T*>(w.wu), D.H, hb, D.F, 1};
       DF_HIP(run_rows<T>(a_frag<T>(u, D.H, M), D.H, g.tiles_gu, 1, 1, e, st, NoPerLaunch{}));
@@ -933,8 +946,8 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
     DF_MARK(DFLASH_SEC_GATE_UP, l, true);
     DF_MARK(DFLASH_SEC_DOWN, l, false);
     if (mid) {
-      TEpiStoreF32 e{static_cast<const uint16_t*>(w.wd), D.F, part, D.H, M};
-      DF_HIP(launch_mid<128>(a16(hb, D.F), D.H, D.F, ks_d, e, st));
+      TEpiStoreF32 e{w16(w.wd, wp.wd), D.F, part, D.H, M};
+      DF_HIP(launch_mid<128>(a16(hb, D.F), D.H, D.F, ks_d, e, st, pk));
     } else {
       EpiPartialF32<T> e{static_cast<const T*>(w.wd), D.F, part, D.H, M};
       DF_HIP(run_rows<T>(a_frag<T>(hb, D.F, M), D.F, g.tiles_d, 1, g.ks_d, e, st,
@@ -969,10 +982,10 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
       n_parts = lm_split(M, D.V).n_parts;
       const int np = n_parts;
       auto make = [&](int n_base, int part_base) {
-        return TEpiLoss{static_cast<const uint16_t*>(h->w.lm_head), D.H, D.V, np, B, lpart,
-                        tr->labels, dbg_z, n_base, part_base};
+        return TEpiLoss{w16(h->w.lm_head, h->pk_lm), D.H, D.V, np, B, lpart, tr->labels, dbg_z,
+                        n_base, part_base};
       };
-      DF_HIP(launch_lm_tiled(a16(u, D.H), D.V, D.H, make, st));
+      DF_HIP(launch_lm_tiled(a16(u, D.H), D.V, D.H, make, st, pk));
     }
     for (int m0 = 0; !mid && m0 < M; m0 += kMaxRowsPerLaunch) {
       AOperand<T> Ai = A;
@@ -1002,11 +1015,11 @@ dflash_status draft_impl(dflash_handle* h, dflash_kv* kv, int B, const int32_t* 
     if (mid) {
       const int n_parts = lm_split(M, D.V).n_parts;
       auto make = [&](int n_base, int part_base) {
-        return TEpiArgmax{static_cast<const uint16_t*>(h->w.lm_head), D.H, D.V, n_parts, lm_part,
-                          dbg_z, n_base, part_base};
+        return TEpiArgmax{w16(h->w.lm_head, h->pk_lm), D.H, D.V, n_parts, lm_part, dbg_z, n_base,
+                          part_base};
       };
       DF_MARK(DFLASH_SEC_LM_GEMM, -1, false);
-      DF_HIP(launch_lm_tiled(a16(u, D.H), D.V, D.H, make, st));
+      DF_HIP(launch_lm_tiled(a16(u, D.H), D.V, D.H, make, st, pk));
       DF_MARK(DFLASH_SEC_LM_GEMM, -1, true);
       DF_HIP(launch_lm_argmax_finalize(lm_part, n_parts, M, B, anchors, D.V, draft, st));
     }
@@ -1073,6 +1086,45 @@ dflash_status step_impl(dflash_handle* h, dflash_kv* kv, int B, int32_t* dev_len
   DF_HIP(launch_advance_lengths(dev_len, accept, nb, B, len_max, status, st));
   const DevLen dl{dev_len, len_max};
   return draft_impl<T>(h, kv, B, anchor, draft, nullptr, nullptr, ws, st, nullptr, &dl);
+}
+
+// ------------------------------------------------------------- packed weights
+// Every bf16 GEMM weight, fragment-major with its rows padded to a multiple
+// of 16, at 256-byte aligned offsets: per layer wq, wk, wv, wo, wg, wu, wd,
+// then fc, then lm_head.
+constexpr int kPackPerLayer = 7;
+struct PackMat {
+  const void* src;
+  int N, K;
+  size_t off;
+};
+struct PackPlan {
+  PackMat m[kPackPerLayer * DFLASH_MAX_LAYERS + 2];
+  int n;
+  size_t total;
+};
+PackPlan pack_plan(const dflash_handle* h) {
+  const Dims D = dims(h->cfg);
+  PackPlan p{};
+  size_t off = 0;
+  auto add = [&](const void* src, int N, int K) {
+    p.m[p.n++] = PackMat{src, N, K, off};
+    off += align_up(static_cast<size_t>((N + 15) / 16) * 16 * K * 2);
+  };
+  for (int l = 0; l < D.L; ++l) {
+    const dflash_layer_weights& w = h->layers[l];
+    add(w.wq, D.qd, D.H);
+    add(w.wk, D.kvd, D.H);
+    add(w.wv, D.kvd, D.H);
+    add(w.wo, D.H, D.qd);
+    add(w.wg, D.F, D.H);
+    add(w.wu, D.F, D.H);
+    add(w.wd, D.H, D.F);
+  }
+  add(h->w.fc, D.H, D.nf * D.H);
+  add(h->w.lm_head, D.V, D.H);
+  p.total = off;
+  return p;
 }
 
 }  // namespace
@@ -1161,7 +1213,53 @@ dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, d
   for (int l = 0; l < cfg->n_layers; ++l) h->layers[l] = w->layers[l];
   h->w.layers = h->layers;
   h->n_timing = 0;
+  h->packed = false;
+  for (int l = 0; l < DFLASH_MAX_LAYERS; ++l) h->pk_layers[l] = dflash_layer_weights{};
+  h->pk_fc = h->pk_lm = nullptr;
   *out = h;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_packed_weights_size(const dflash_handle* h, size_t* bytes) {
+  if (!h || !bytes) return DFLASH_ERR_INVALID_ARG;
+  if (h->cfg.dtype != DFLASH_BF16) return DFLASH_ERR_UNSUPPORTED;
+  *bytes = pack_plan(h).total;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_pack_weights(dflash_handle* h, void* dst, size_t bytes, void* stream) {
+  if (!h) return DFLASH_ERR_INVALID_ARG;
+  if (!dst) {
+    if (bytes) return DFLASH_ERR_INVALID_ARG;
+    h->packed = false;   // back to the caller's row-major weights
+    return DFLASH_OK;
+  }
+  if (h->cfg.dtype != DFLASH_BF16) return DFLASH_ERR_UNSUPPORTED;
+  if (!aligned16(dst)) return DFLASH_ERR_INVALID_ARG;
+  const PackPlan p = pack_plan(h);
+  if (bytes < p.total) return DFLASH_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // unbound until every copy is launched: a failed call leaves the handle on
+  // the row-major weights
+  h->packed = false;
+  char* base = static_cast<char*>(dst);
+  for (int i = 0; i < p.n; ++i)
+    DF_HIP(launch_pack_frag(static_cast<const uint16_t*>(p.m[i].src), p.m[i].N, p.m[i].K,
+                            reinterpret_cast<uint16_t*>(base + p.m[i].off), st));
+  for (int l = 0; l < h->cfg.n_layers; ++l) {
+    const PackMat* m = p.m + kPackPerLayer * l;
+    dflash_layer_weights& w = h->pk_layers[l];
+    w.wq = base + m[0].off;
+    w.wk = base + m[1].off;
+    w.wv = base + m[2].off;
+    w.wo = base + m[3].off;
+    w.wg = base + m[4].off;
+    w.wu = base + m[5].off;
+    w.wd = base + m[6].off;
+  }
+  h->pk_fc = base + p.m[p.n - 2].off;
+  h->pk_lm = base + p.m[p.n - 1].off;
+  h->packed = true;
   return DFLASH_OK;
 }
 

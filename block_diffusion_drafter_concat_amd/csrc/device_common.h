@@ -215,11 +215,13 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
 // so the V^T reads of a 32-key step stay inside the block's rows).
 constexpr int kTrainSlab = 32;
 
-// Fragment-major layout of an M x K activation (K a multiple of 32) that a
-// weight-streaming GEMM reads as its A operand: rows in groups of 16, each
-// group stored as K/32 chunks of 16 rows x 32 columns, row-major inside a
-// chunk.  The 64 lanes of one A-fragment load (16 rows x 4 runs of 8
-// columns) then read one contiguous 16 x 32 chunk instead of 16 row pieces.
+// Fragment-major layout of an M x K matrix (K a multiple of 32): rows in
+// groups of 16, each group stored as K/32 chunks of 16 rows x 32 columns,
+// row-major inside a chunk.  The 64 lanes of one A-fragment load of the
+// weight-streaming GEMM, or of one operand load of the LDS-tiled GEMM (16
+// rows x 4 runs of 8 columns), then read one contiguous 1 KB chunk instead of
+// 16 row pieces.  The drafter's activations use it, and so do packed weights
+// (dflash_pack_weights).
 __host__ __device__ __forceinline__ int64_t frag_major(int m, int k, int K) {
   return (static_cast<int64_t>(m >> 4) * (K >> 5) + (k >> 5)) * 512 + (m & 15) * 32 + (k & 31);
 }

@@ -5,14 +5,23 @@
 // of a batch of blocks (M = 64 .. 256 rows).  Design for CDNA4 (gfx950):
 //   - workgroup tile BM x BN (rows of A x rows of W), WM x WN waves, each wave
 //     (BM/WM) x (BN/WN) as 16 x 16 MFMA tiles with fp32 accumulators;
-//   - K in stages of 64: both operand tiles go through LDS, double buffered.
-//     The next stage is loaded straight into LDS (buffer loads with the
-//     LDS-destination bit, no staging registers) while the current one feeds
-//     the MFMAs.  16-byte chunks are XOR-swizzled by row so that the fragment
-//     reads (16 rows x 16 bytes per instruction) hit distinct banks;
-//   - every 8-row load instruction of the W tile has its own buffer resource,
+//   - K in stages of 32: both operand tiles go through a ring of 4-5 LDS
+//     slots, NS - 1 stages in flight.  Stages are loaded straight into LDS
+//     (buffer loads with the LDS-destination bit, no staging registers) while
+//     the current one feeds the MFMAs.  16-byte chunks are XOR-swizzled by
+//     row so that the fragment reads (16 rows x 16 bytes per instruction)
+//     hit distinct banks;
+//   - every 16-row load instruction of the W tile has its own buffer resource,
 //     from the epilogue's W-row map, so one tile can draw rows from several
 //     matrices (q/k/v, gate/up pairs) and rows past a matrix's end read zero;
+//   - either operand may be stored row-major or fragment-major (blocks of 16
+//     rows x 32 columns, 1 KB each, k fastest: frag_major()).  A load
+//     instruction covers 16 rows x 32 columns either way; fragment-major it
+//     reads one contiguous 1 KB block instead of 16 row pieces of 64 bytes
+//     at the row stride (measured on MI355X: 61 -> 102 GB/s per compute unit
+//     from L2 at one workgroup per CU, and fewer stalls on the stage barrier
+//     for rows streamed from HBM).  The drafter's own activations are stored
+//     that way; weights are when the caller has packed them;
 //   - tiles are walked in an XCD-aware order: workgroup w runs on XCD w % 8,
 //     so consecutive tile indices are given to the same XCD, and inside an
 //     XCD's range tiles go in groups of 4 row-tiles, so the A and W tiles a
@@ -108,10 +117,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, ui
                                            0x00020000);
 }
 
+// wfrag: the W rows the epilogue maps are fragment-major (rows padded with
+// zeros to a multiple of 16; the block of a 16-aligned row n starts at n K,
+// where row-major row n starts, so the row maps serve both layouts).  A
+// fragment-major A has one slab (slab_k == K).
 template <int BM, int BN, int WM, int WN, class Epi>
 __global__ __launch_bounds__(WM * WN * 64) void tiled_gemm_kernel(AOperand<uint16_t> A, int N,
                                                                   int K, int tiles_m,
-                                                                  int tiles_n, Epi epi) {
+                                                                  int tiles_n, int wfrag,
+                                                                  Epi epi) {
   constexpr int NWAVES = WM * WN, NT = NWAVES * 64;
   constexpr int RW = BM / WM, CW = BN / WN;   // wave tile
   constexpr int MI = RW / 16, NJ = CW / 16;
@@ -162,12 +176,18 @@ __global__ __launch_bounds__(WM * WN * 64) void tiled_gemm_kernel(AOperand<uint1
   constexpr int NS = tiled_stages(BM, BN);  // ring slots; NS - 1 stages in flight
   const int lrow = lane >> 2;
   const int gchunk = (lane & 3) ^ ((lane >> 3) & 3);
-  const uint32_t a_voff = static_cast<uint32_t>(lrow * A.lda * 2 + gchunk * 16);
-  const uint32_t w_voff = static_cast<uint32_t>(lrow * K * 2 + gchunk * 16);
-  // bytes of rows [0, valid) of a 16-row run (valid <= 16)
-  auto run_bytes = [](int valid, int ld) -> uint64_t {
-    valid = valid < 16 ? valid : 16;
-    return valid > 0 ? static_cast<uint64_t>(valid) * ld * 2 : 0;
+  // lane offset inside an instruction's 16 rows, and bytes per column of the
+  // k offset: row-major, row lrow at the row stride and 2; fragment-major,
+  // byte lrow * 64 of the 1 KB block and 32 (one block per 32 columns)
+  const uint32_t a_voff = static_cast<uint32_t>((A.frag ? 64 : A.lda * 2) * lrow + gchunk * 16);
+  const uint32_t w_voff = static_cast<uint32_t>((wfrag ? 64 : K * 2) * lrow + gchunk * 16);
+  const uint32_t a_kb = A.frag ? 32 : 2, w_kb = wfrag ? 32 : 2;
+  // bytes a 16-row run of row length ld may read: rows [0, valid) row-major;
+  // the whole block fragment-major (its rows past the end hold zeros or
+  // unused values)
+  auto run_bytes = [](int valid, int ld, int frag) -> uint64_t {
+    if (valid <= 0) return 0;
+    return static_cast<uint64_t>(frag || valid > 16 ? 16 : valid) * ld * 2;
   };
   const int a_row0 = m0 + 16 * LA * wave;   // rows of A this wave loads
   const uint16_t* wptr[LW];   // first W row of each load instruction
@@ -176,7 +196,7 @@ __global__ __launch_bounds__(WM * WN * 64) void tiled_gemm_kernel(AOperand<uint1
   for (int i = 0; i < LW; ++i) {
     const WRows wr = epi.wrows(part, n0 + 16 * (wave * LW + i), N);
     wptr[i] = wr.p;
-    wbytes[i] = run_bytes(wr.valid, K);
+    wbytes[i] = run_bytes(wr.valid, K, wfrag);
   }
   const int n_stages = kper / kTBK;
   // Loads are issued for stages 0, 1, 2, ... in order; the next stage's slab,
@@ -196,15 +216,16 @@ __global__ __launch_bounds__(WM * WN * 64) void tiled_gemm_kernel(AOperand<uint1
     for (int i = 0; i < LA; ++i) {
       const int r0 = a_row0 + 16 * i;
       const __amdgpu_buffer_rsrc_t ars = tile_rsrc(
-          sp + static_cast<int64_t>(min(r0, A.M)) * A.lda, run_bytes(A.M - r0, A.lda));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, la + i * 512, 16, a_voff, nx_col * 2, 0, 0);
+          sp + static_cast<int64_t>(min(r0, A.M)) * A.lda, run_bytes(A.M - r0, A.lda, A.frag));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, la + i * 512, 16, a_voff, nx_col * a_kb, 0,
+                                               0);
     }
 #pragma unroll
     for (int i = 0; i < LW; ++i) {
       // (bound to a local: a resource temporary passed straight to the builtin
       // makes the host pass drop the kernel's launch stub)
       const __amdgpu_buffer_rsrc_t wrs = tile_rsrc(wptr[i], wbytes[i]);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, lw + i * 512, 16, w_voff, nx_k * 2, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, lw + i * 512, 16, w_voff, nx_k * w_kb, 0, 0);
     }
     nx_slot = nx_slot + 1 == NS ? 0 : nx_slot + 1;
     if (++nx_stage < n_stages) {
@@ -389,13 +410,15 @@ struct TEpiQKVParts {
 
 // SwiGLU of a batch of blocks: the columns [0, bn/2) of tile tn are gate rows
 // tn*bn/2 .. +bn/2, the columns [bn/2, bn) the up rows with the same indices;
-// the epilogue writes h[m][tn*bn/2 + c] = silu(g) * u in bf16.
+// the epilogue writes h[m][tn*bn/2 + c] = silu(g) * u in bf16, row-major or
+// fragment-major.
 struct TEpiSwiGLUPair {
   const uint16_t* wg;
   const uint16_t* wu;
   int K, F, bn;
   uint16_t* h;
-  int64_t ldh;
+  int64_t ldh;   // row stride of h; fragment-major: its row length
+  int frag;      // h fragment-major (the down projection's A operand)
   __device__ WRows wrows(int, int n, int) const {
     const int half = bn / 2, tn = n / bn, r = n % bn;
     const int f = tn * half + (r < half ? r : r - half);
@@ -409,7 +432,9 @@ struct TEpiSwiGLUPair {
       const int m = s.row(lr);
       if (m >= s.M) continue;
       const float g = s.at(lr, c), u = s.at(lr, c + half);
-      stf(h + static_cast<int64_t>(m) * ldh + f0 + c, g / (1.0f + expf(-g)) * u);
+      const int j = f0 + c;
+      stf(h + (frag ? frag_major(m, j, static_cast<int>(ldh)) : static_cast<int64_t>(m) * ldh + j),
+          g / (1.0f + expf(-g)) * u);
     }
   }
 };

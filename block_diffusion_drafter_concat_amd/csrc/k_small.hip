@@ -655,5 +655,34 @@ hipError_t launch_bf16_round(const float* in, uint16_t* out, int64_t n, int pack
   return hipGetLastError();
 }
 
-}  // namespace dflash
+// Weight packing: a row-major [N, K] bf16 matrix into fragment-major order
+// (frag_major(); rows padded with zeros to a multiple of 16), 16 bytes per
+// thread: consecutive threads write consecutive bytes of the destination and
+// read 64-byte row pieces of the source.
+__global__ __launch_bounds__(256) void pack_frag_kernel(const uint16_t* __restrict__ src, int N,
+                                                        int K, uint16_t* __restrict__ dst,
+                                                        int64_t chunks) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  const int64_t kb_per_row = K / 32;
+  for (int64_t q = blockIdx.x * 256 + threadIdx.x; q < chunks; q += stride) {
+    // chunk q = 8 elements at dst[8q]: block q / 64 (16 rows x 32 columns),
+    // row (q % 64) / 4 of the block, columns 8 (q % 4) .. + 8
+    const int64_t blk = q >> 6;
+    const int r = static_cast<int>((q >> 2) & 15), c8 = static_cast<int>(q & 3) * 8;
+    const int64_t n = (blk / kb_per_row) * 16 + r;
+    const int64_t k = (blk % kb_per_row) * 32 + c8;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (n < N) v = *reinterpret_cast<const uint4*>(src + n * K + k);
+    *reinterpret_cast<uint4*>(dst + q * 8) = v;
+  }
+}
 
+hipError_t launch_pack_frag(const uint16_t* src, int N, int K, uint16_t* dst, hipStream_t st) {
+  if (N <= 0 || K <= 0 || K % 32) return hipErrorInvalidValue;
+  const int64_t chunks = static_cast<int64_t>((N + 15) / 16) * 16 * (K / 8);
+  const unsigned grid = static_cast<unsigned>(std::min<int64_t>((chunks + 255) / 256, 16384));
+  pack_frag_kernel<<<grid, 256, 0, st>>>(src, N, K, dst, chunks);
+  return hipGetLastError();
+}
+
+}  // namespace dflash

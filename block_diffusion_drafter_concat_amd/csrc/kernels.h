@@ -68,4 +68,8 @@ hipError_t launch_verify(const void* logits, bool bf16, const int32_t* drafts, i
 hipError_t launch_bf16_round(const float* in, uint16_t* out, int64_t n, int packed,
                              hipStream_t st);
 
+// Row-major [N, K] bf16 (K a multiple of 32) -> fragment-major, rows padded
+// with zeros to a multiple of 16 (dst holds ceil(N/16)*16 x K elements).
+hipError_t launch_pack_frag(const uint16_t* src, int N, int K, uint16_t* dst, hipStream_t st);
+
 }  // namespace dflash

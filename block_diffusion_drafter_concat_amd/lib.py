@@ -30,7 +30,7 @@ EXPORTS = ("dflash_target_layer_ids", "dflash_create", "dflash_destroy",
            "dflash_train_forward", "dflash_set_timing", "dflash_status_string",
            "dflash_stochastic_workspace_size", "dflash_sample_drafts",
            "dflash_verify_stochastic", "dflash_step_resident", "dflash_debug_bf16_round",
-           "dflash_draft_block_noalloc")
+           "dflash_draft_block_noalloc", "dflash_packed_weights_size", "dflash_pack_weights")
 
 # dflash_section
 SECTIONS = {"fuse_gemm": 1, "fuse_norm": 2, "inject": 3, "embed": 4, "attn_norm": 5, "qkv": 6,
@@ -96,6 +96,10 @@ def load() -> C.CDLL:
     lib.dflash_destroy.restype = C.c_int
     lib.dflash_workspace_size.argtypes = [vp, i32, i32, i64, C.POINTER(C.c_size_t)]
     lib.dflash_workspace_size.restype = C.c_int
+    lib.dflash_packed_weights_size.argtypes = [vp, C.POINTER(C.c_size_t)]
+    lib.dflash_packed_weights_size.restype = C.c_int
+    lib.dflash_pack_weights.argtypes = [vp, vp, C.c_size_t, vp]
+    lib.dflash_pack_weights.restype = C.c_int
     lib.dflash_fuse_context.argtypes = [vp, C.POINTER(vp), i64, vp, vp, vp]
     lib.dflash_fuse_context.restype = C.c_int
     lib.dflash_inject_kv.argtypes = [vp, vp, pi32, pi32, C.POINTER(KV), vp, vp]
@@ -209,6 +213,7 @@ class Drafter:
         _check(self.lib.dflash_create(C.byref(self.cfg), C.byref(self._weights), C.byref(h)),
                "dflash_create")
         self.handle = h
+        self._packed = None   # the packed-weight buffer while bound
 
     def close(self):
         if getattr(self, "handle", None):
@@ -231,6 +236,25 @@ class Drafter:
         torch = _torch()
         return torch.empty(self.workspace_size(max_batch, max_block, max_tokens),
                            dtype=torch.uint8, device=device)
+
+    def packed_weights_size(self) -> int:
+        n = C.c_size_t()
+        _check(self.lib.dflash_packed_weights_size(self.handle, C.byref(n)),
+               "dflash_packed_weights_size")
+        return int(n.value)
+
+    def pack_weights(self, dst=None, stream=None) -> None:
+        """Fragment-major copy of the bf16 GEMM weights into dst (a device
+        uint8 tensor of at least packed_weights_size() bytes, kept alive by
+        this object while bound); None switches back to the row-major weights."""
+        if dst is None:
+            _check(self.lib.dflash_pack_weights(self.handle, None, 0, _stream(stream)),
+                   "dflash_pack_weights")
+            self._packed = None
+            return
+        _check(self.lib.dflash_pack_weights(self.handle, _ptr(dst), dst.numel() * dst.element_size(),
+                                            _stream(stream)), "dflash_pack_weights")
+        self._packed = dst
 
     def set_timing(self, points) -> None:
         """points: list of (section name, layer, start event, stop event) with

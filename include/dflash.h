@@ -148,6 +148,30 @@ dflash_status dflash_create(const dflash_config *cfg, const dflash_weights *w,
                             dflash_handle **out);
 dflash_status dflash_destroy(dflash_handle *h);
 
+/* Packed weights: a copy of every bf16 GEMM weight (per layer wq, wk, wv, wo,
+ * wg, wu, wd; then fc and lm_head) in fragment-major order -- rows in groups
+ * of 16, each group stored as consecutive 1 KB blocks of 16 rows x 32
+ * columns, rows past a matrix's end zero -- so that the LDS-tiled GEMMs
+ * (fuse/inject of 129 or more rows, blocks of 64 or more rows) read each
+ * operand block as one contiguous run instead of 16 strided row pieces.
+ * A storage layout only: every result is bit-identical with and without it.
+ * The weight-streaming GEMMs (fewer rows) keep reading the row-major weights,
+ * which stay required.
+ *
+ * dflash_packed_weights_size: bytes of the packed copy (bf16 handles; float32
+ * handles get DFLASH_ERR_UNSUPPORTED).
+ * dflash_pack_weights: writes the copy into dst (device, caller-owned, 16-byte
+ * aligned, at least that many bytes) on `stream` and makes the handle's
+ * tiled GEMMs read it from then on.  The caller keeps dst alive and unchanged
+ * while the handle uses it, orders later calls on other streams after this
+ * one, and calls it again after changing the row-major weights.  dst = NULL
+ * with bytes = 0 switches back to the row-major weights (then dst may be
+ * freed once the calls that used it have finished).  DFLASH_ERR_INVALID_ARG
+ * for a short or misaligned dst; on DFLASH_ERR_HIP the handle stays on the
+ * row-major weights. */
+dflash_status dflash_packed_weights_size(const dflash_handle *h, size_t *bytes);
+dflash_status dflash_pack_weights(dflash_handle *h, void *dst, size_t bytes, void *stream);
+
 /* Bytes of workspace that every call below needs for batches up to max_batch,
  * blocks up to max_block slots and fuse/inject calls of up to max_tokens rows. */
 dflash_status dflash_workspace_size(const dflash_handle *h, int32_t max_batch,

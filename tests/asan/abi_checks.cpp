@@ -139,6 +139,14 @@ int main(int argc, char** argv) {
   EXPECT(dflash_debug_bf16_round(static_cast<float*>(p), static_cast<uint16_t*>(p), 7, 1, nullptr),
          DFLASH_ERR_INVALID_ARG);
   EXPECT(std::strlen(dflash_status_string(DFLASH_ERR_SCRATCH)) > 0, 1);
+  // weight packing: size query, short / misaligned buffers, unbinding
+  size_t packed = 0;
+  EXPECT(dflash_packed_weights_size(h, &packed), DFLASH_OK);
+  EXPECT(packed > 0, 1);
+  EXPECT(dflash_pack_weights(h, p, packed - 1, nullptr), DFLASH_ERR_INVALID_ARG);
+  EXPECT(dflash_pack_weights(h, static_cast<char*>(p) + 8, packed, nullptr),
+         DFLASH_ERR_INVALID_ARG);
+  EXPECT(dflash_pack_weights(h, nullptr, 0, nullptr), DFLASH_OK);
 
   if (no_device) {
     // arguments that pass every host check: the first launch fails
@@ -150,6 +158,7 @@ int main(int argc, char** argv) {
     EXPECT(dflash_fuse_context(h, feats, 4, p, p, nullptr), DFLASH_ERR_HIP);
     EXPECT(dflash_draft_block_noalloc(h, &c1.kv, 8, ip, ip, nullptr, nullptr, nullptr),
            DFLASH_ERR_HIP);
+    EXPECT(dflash_pack_weights(h, p, packed, nullptr), DFLASH_ERR_HIP);
   }
   EXPECT(dflash_destroy(h), DFLASH_OK);
   EXPECT(dflash_destroy(nullptr), DFLASH_ERR_INVALID_ARG);

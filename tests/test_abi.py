@@ -344,6 +344,62 @@ def test_launch_without_a_device_returns_hip_error():
     # the no-allocation draft fails at its first device call (the scratch lookup)
     assert lib.dflash_draft_block_noalloc(h, C.byref(kv), 8, p, p, None, None, None) == L.ERR_HIP
     lib.dflash_destroy(h)
+    # weight packing: the first copy's launch fails
+    st, hb, keep_b = _create(configs.QWEN3_8B_LIKE)
+    assert st == L.OK
+    n = C.c_size_t()
+    assert lib.dflash_packed_weights_size(hb, C.byref(n)) == L.OK
+    assert lib.dflash_pack_weights(hb, p, n.value, None) == L.ERR_HIP
+    lib.dflash_destroy(hb)
+
+
+def _packed_bytes(shape):
+    """Bytes of the packed weights: each GEMM weight [N, K] with its rows
+    rounded up to 16, two bytes an element, at 256-byte aligned offsets."""
+    H, F, V = shape.hidden, shape.ffn, shape.vocab
+    qd, kvd = shape.n_q_heads * shape.head_dim, shape.n_kv_heads * shape.head_dim
+    mats = [(qd, H), (kvd, H), (kvd, H), (H, qd), (F, H), (F, H), (H, F)] * shape.n_layers
+    mats += [(H, shape.n_feat * H), (V, H)]
+    return sum(-(-(-(-n // 16) * 16 * k * 2) // 256) * 256 for n, k in mats)
+
+
+@pytest.mark.parametrize("shape", [
+    configs.QWEN3_8B_LIKE, configs.TARGET_27B_LIKE,
+    # a vocabulary that is not a multiple of 16 (the LM head's last group padded)
+    configs.DrafterShape(n_layers=2, hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                         ffn=1536, vocab=76900, n_feat=3)])
+def test_packed_weights_size(shape):
+    st, h, keep = _create(shape)
+    assert st == L.OK
+    n = C.c_size_t()
+    assert L.load().dflash_packed_weights_size(h, C.byref(n)) == L.OK
+    assert n.value == _packed_bytes(shape)
+    L.load().dflash_destroy(h)
+
+
+def test_pack_weights_host_checks():
+    """Packing refuses float32 handles, short or misaligned buffers and null
+    arguments before any launch; a null buffer with zero bytes unbinds."""
+    lib = L.load()
+    st, h, keep = _create(configs.QWEN3_8B_LIKE)
+    assert st == L.OK
+    n = C.c_size_t()
+    assert lib.dflash_packed_weights_size(h, None) == L.ERR_INVALID_ARG
+    assert lib.dflash_packed_weights_size(None, C.byref(n)) == L.ERR_INVALID_ARG
+    assert lib.dflash_packed_weights_size(h, C.byref(n)) == L.OK
+    p = C.c_void_p(_FAKE)
+    assert lib.dflash_pack_weights(h, p, n.value - 1, None) == L.ERR_INVALID_ARG
+    assert lib.dflash_pack_weights(h, C.c_void_p(_FAKE + 8), n.value, None) == L.ERR_INVALID_ARG
+    assert lib.dflash_pack_weights(None, p, n.value, None) == L.ERR_INVALID_ARG
+    assert lib.dflash_pack_weights(h, None, 1, None) == L.ERR_INVALID_ARG
+    assert lib.dflash_pack_weights(h, None, 0, None) == L.OK
+    lib.dflash_destroy(h)
+    st, hf, keep_f = _create(configs.TINY_F32)
+    assert st == L.OK
+    assert lib.dflash_packed_weights_size(hf, C.byref(n)) == L.ERR_UNSUPPORTED
+    assert lib.dflash_pack_weights(hf, p, 1 << 30, None) == L.ERR_UNSUPPORTED
+    assert lib.dflash_pack_weights(hf, None, 0, None) == L.OK
+    lib.dflash_destroy(hf)
 
 
 def test_noalloc_draft_host_checks():
