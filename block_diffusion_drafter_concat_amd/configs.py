@@ -70,6 +70,10 @@ QWEN3_8B_LIKE = DrafterShape(n_layers=5, hidden=4096, n_q_heads=32, n_kv_heads=8
                              head_dim=128, ffn=12288, vocab=151936, dtype="bf16")
 TARGET_27B_LIKE = DrafterShape(n_layers=5, hidden=5120, n_q_heads=40, n_kv_heads=8,
                                head_dim=128, ffn=17408, vocab=151936, dtype="bf16")
+# bf16 test shape with head dim 64, three q heads per kv head and six fused
+# target layers (the largest count the interface takes)
+SMALL_D64_BF16 = DrafterShape(n_layers=2, hidden=384, n_q_heads=6, n_kv_heads=2, head_dim=64,
+                              ffn=1024, vocab=5003, n_feat=6, dtype="bf16")
 
 
 def tiny_f32() -> Workload:

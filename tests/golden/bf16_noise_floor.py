@@ -93,6 +93,10 @@ def cases():
     yield "qwen3-8b-shaped", "batch-16 sequences 0/7/15, B 16", configs.QWEN3_8B_LIKE, 3, [
         wl.ctx[b] for b in (0, 7, 15)], 16
     yield "27b-target-shaped", "ctx 4096 x 2, B 16", configs.TARGET_27B_LIKE, 5, [4096, 4096], 16
+    d64 = configs.SMALL_D64_BF16
+    yield "small-bf16-d64", "contexts 0/45/300, B 16", d64, 81, [0, 45, 300], 16
+    yield "small-bf16-d64", "5 contexts < 400, B 16", d64, 82, list(
+        synth.integers((5,), 0, 400, 82, synth.STREAM_INDICES, "d64_lens")), 16
 
 
 def main():

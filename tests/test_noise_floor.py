@@ -13,6 +13,7 @@ import os
 import sys
 
 import numpy as np
+import pytest
 
 import oracle.dflash_oracle as OD
 from block_diffusion_drafter_concat_amd import configs
@@ -25,18 +26,21 @@ from gpu_util import bf16_noise_floor, id_gate, small_bf16_shape  # noqa: E402
 
 
 def test_floor_file_covers_every_bf16_family():
-    for shape in (small_bf16_shape(), configs.QWEN3_8B_LIKE, configs.TARGET_27B_LIKE):
+    for shape in (small_bf16_shape(), configs.SMALL_D64_BF16, configs.QWEN3_8B_LIKE,
+                  configs.TARGET_27B_LIKE):
         f = bf16_noise_floor(shape)
         assert 1e-4 < f < 0.2, (shape, f)
         assert id_gate(shape) == max(1e-2, 2 * f)
     assert id_gate(configs.TINY_F32) == 1e-2
 
 
-def test_small_family_floor_reproduces():
-    want = bf16_noise_floor(small_bf16_shape())
+@pytest.mark.parametrize("family", ["small-bf16", "small-bf16-d64"])
+def test_small_family_floor_reproduces(family):
+    want = bf16_noise_floor(small_bf16_shape() if family == "small-bf16"
+                            else configs.SMALL_D64_BF16)
     got = 0.0
-    for family, _, shape, wid, lens, B in NF.cases():
-        if family != "small-bf16":
+    for fam, _, shape, wid, lens, B in NF.cases():
+        if fam != family:
             continue
         w = configs.make_weights(shape, wid)
         caches = NF.synthetic_cache(shape, wid, lens)
