@@ -74,6 +74,10 @@ TARGET_27B_LIKE = DrafterShape(n_layers=5, hidden=5120, n_q_heads=40, n_kv_heads
 # target layers (the largest count the interface takes)
 SMALL_D64_BF16 = DrafterShape(n_layers=2, hidden=384, n_q_heads=6, n_kv_heads=2, head_dim=64,
                               ffn=1024, vocab=5003, n_feat=6, dtype="bf16")
+# bf16 test shape at the largest hidden size the interface takes (8192), kept
+# to one layer and two fused target layers so the oracle's weights stay small
+MAX_HIDDEN_BF16 = DrafterShape(n_layers=1, hidden=8192, n_q_heads=32, n_kv_heads=8,
+                               head_dim=128, ffn=4096, vocab=2048, n_feat=2, dtype="bf16")
 
 
 def tiny_f32() -> Workload:

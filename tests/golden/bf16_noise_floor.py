@@ -97,6 +97,7 @@ def cases():
     yield "small-bf16-d64", "contexts 0/45/300, B 16", d64, 81, [0, 45, 300], 16
     yield "small-bf16-d64", "5 contexts < 400, B 16", d64, 82, list(
         synth.integers((5,), 0, 400, 82, synth.STREAM_INDICES, "d64_lens")), 16
+    yield "max-hidden-bf16", "ctx 100, B 16", configs.MAX_HIDDEN_BF16, 85, [100], 16
 
 
 def main():

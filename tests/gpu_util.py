@@ -75,7 +75,7 @@ def bf16_noise_floor(shape) -> float:
     float32 arithmetic (tests/golden/bf16_noise_floor.py; read from the file
     it writes, never from the device)."""
     family = {512: "small-bf16", 384: "small-bf16-d64", 4096: "qwen3-8b-shaped",
-              5120: "27b-target-shaped"}[shape.hidden]
+              5120: "27b-target-shaped", 8192: "max-hidden-bf16"}[shape.hidden]
     with open(_FLOOR_FILE) as f:
         for ln in f:
             if ln.startswith(family + ":"):

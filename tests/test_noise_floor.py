@@ -27,7 +27,7 @@ from gpu_util import bf16_noise_floor, id_gate, small_bf16_shape  # noqa: E402
 
 def test_floor_file_covers_every_bf16_family():
     for shape in (small_bf16_shape(), configs.SMALL_D64_BF16, configs.QWEN3_8B_LIKE,
-                  configs.TARGET_27B_LIKE):
+                  configs.TARGET_27B_LIKE, configs.MAX_HIDDEN_BF16):
         f = bf16_noise_floor(shape)
         assert 1e-4 < f < 0.2, (shape, f)
         assert id_gate(shape) == max(1e-2, 2 * f)
