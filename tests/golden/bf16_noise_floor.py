@@ -88,6 +88,8 @@ def cases():
     yield "small-bf16", "contexts 0/45/300, B 16", small, 31, [0, 45, 300], 16
     yield "small-bf16", "16 contexts < 400, B 16", small, 51, list(
         synth.integers((16,), 0, 400, 51, synth.STREAM_INDICES, "mid_lens16")), 16
+    yield "small-bf16", "vocab 17, 5 contexts < 300, B 16", configs.scaled(small, vocab=17), 87, \
+        list(synth.integers((5,), 0, 300, 87, synth.STREAM_INDICES, "v17_lens")), 16
     yield "qwen3-8b-shaped", "ctx 2048, B 16", configs.QWEN3_8B_LIKE, 2, [2048], 16
     wl = configs.qwen3_8b_b16_ragged()
     yield "qwen3-8b-shaped", "batch-16 sequences 0/7/15, B 16", configs.QWEN3_8B_LIKE, 3, [

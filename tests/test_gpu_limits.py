@@ -6,6 +6,7 @@
 - The largest hidden size, 8192 (configs.MAX_HIDDEN_BF16, one layer): the
   norm kernels at eight float4 per thread and at most four split-K slabs,
   fusion of 37 and 200 rows (both GEMM paths), injection and a draft.
+- A vocabulary smaller than one LM-head tile (17 tokens), on both LM-head paths.
 Bars as in test_gpu_parity.
 """
 import numpy as np
@@ -100,3 +101,24 @@ def test_max_hidden_draft(torch, max_hidden):
     ids, hid, z = _draft(torch, dr, shape, cache, 16, anchors, dr.workspace(1, 16, 1))
     res = O.draft_block(w, shape, caches, anchors, 16)
     draft_compare(shape, res, ids, hid, z, "hidden 8192, ctx 100")
+
+
+@pytest.mark.parametrize("nb", [1, 5])
+def test_vocab_smaller_than_a_tile(torch, nb):
+    """A 17-token vocabulary, less than one LM-head tile: one sequence (16 rows,
+    weight-streaming LM head, one partial 32-row tile) and five (80 rows, tiled
+    LM head, one partial 256-column tile); the same seeded inputs as the small
+    family's vocab-17 noise-floor case for nb = 5."""
+    shape = configs.scaled(small_bf16_shape(), vocab=17)
+    w = configs.make_weights(shape, 87)
+    dr = L.Drafter(shape, w)
+    lens = [int(v) for v in synth.integers((5,), 0, 300, 87, synth.STREAM_INDICES, "v17_lens")]
+    lens = lens[:nb]
+    caches = synthetic_cache(shape, 87, lens)
+    cache = L.KVCache(shape, [n + 32 for n in lens])
+    upload_cache(cache, caches)
+    anchors = configs.make_anchors(shape, 87, nb)
+    ids, hid, z = _draft(torch, dr, shape, cache, 16, anchors, dr.workspace(nb, 16, 1))
+    assert ((ids >= 0) & (ids < shape.vocab)).all()
+    res = O.draft_block(w, shape, caches, anchors, 16)
+    draft_compare(shape, res, ids, hid, z, f"vocab 17, {nb} sequences")
