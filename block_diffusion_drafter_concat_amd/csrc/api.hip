@@ -716,10 +716,12 @@ dflash_status inject_impl(dflash_handle* h, const void* ctx, const SeqTable& seq
     const AOperand<uint16_t> At = a_single<uint16_t>(ctx, D.H, D.H, total);
     // 256 x 256 tiles when they cover the 256 compute units at least twice.
     // Fewer: the parts (layer, K or V) that fill whole rounds on 256 x 256
-    // tiles, the rest on 256 x 128 tiles in a second launch when those fit in
-    // one round (a short last round then costs half a tile's time: 2048 rows,
-    // 320 tiles = 8 parts in one round + 2 parts as 128 half tiles); else
-    // everything on 256 x 128 tiles.
+    // tiles, the rest in a second launch when it fits in one round -- on
+    // 128 x 128 tiles if those fit (2048 rows, 320 tiles = 8 parts in one
+    // round + 2 parts as 256 quarter tiles: every compute unit busy; measured
+    // 207-215 against 235-241 us with the 2 parts as 128 half tiles of
+    // 256 x 128, which leave half the GPU idle), else on 256 x 128 tiles;
+    // else everything on 256 x 128 tiles.
     const int parts = 2 * D.L;
     const int64_t per_part = static_cast<int64_t>((total + kPreBM - 1) / kPreBM) *
                              ((D.kvd + kPreBN - 1) / kPreBN);
@@ -731,7 +733,12 @@ dflash_status inject_impl(dflash_handle* h, const void* ctx, const SeqTable& seq
     } else if (pa >= 1 && pa < parts && (parts - pa) * per_part * 2 <= kCUs) {
       DF_HIP(launch_tiled(At, D.kvd, D.H, pa, 1, te, st, pk));
       te.part_base = pa;
-      DF_HIP((launch_tiled_cfg<kPreBM, 128, 2, 4>(At, D.kvd, D.H, parts - pa, 1, te, st, pk)));
+      const int64_t quarter = static_cast<int64_t>(parts - pa) * ((total + 127) / 128) *
+                              ((D.kvd + 127) / 128);
+      if (quarter <= kCUs)
+        DF_HIP((launch_tiled_cfg<128, 128, 2, 4>(At, D.kvd, D.H, parts - pa, 1, te, st, pk)));
+      else
+        DF_HIP((launch_tiled_cfg<kPreBM, 128, 2, 4>(At, D.kvd, D.H, parts - pa, 1, te, st, pk)));
     } else {
       DF_HIP((launch_tiled_cfg<kPreBM, 128, 2, 4>(At, D.kvd, D.H, parts, 1, te, st, pk)));
     }
