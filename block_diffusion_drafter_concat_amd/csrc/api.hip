@@ -525,14 +525,18 @@ hipError_t launch_tiled(const AOperand<uint16_t>& A, int N, int K, int parts, in
 // LM head of a batch of blocks on the tiled GEMM.  One workgroup per compute
 // unit fits (LDS), so 256-column tiles run in rounds of kCUs tiles; when the
 // last round would be short, the vocabulary rows past the whole rounds go to
-// a second launch of 128-column tiles, which takes half as long per tile
-// (used when those fill at most one round).  `make(n_base, part_base)` builds
-// the epilogue of one launch.
+// a second launch that fits in one round: above 128 rows on 128 x 256 tiles
+// (the two row tiles of a W panel share it through L2; batch 16: 594 tiles =
+// 2.3 rounds become 512 tiles + 164 of 128 x 256, 372 against 383 us with
+// 163 of 256 x 128, whose 128 x 32 wave tiles read the most LDS per MFMA),
+// else on 128-column tiles.  `make(n_base, part_base)` builds the epilogue of
+// one launch.
 constexpr int kCUs = 256;   // compute units of the MI355X
 struct LmSplit {
   int whole;     // 256-column tiles of the first launch (all of them when not split)
   int n_tail;    // vocabulary rows of the second launch (0: not split)
   int n_parts;   // per-row partials of both launches
+  int tail_bn;   // column tile of the second launch: 256 (on 128-row tiles) or 128
 };
 inline LmSplit lm_split(int M, int V) {
   const int bm = M <= 64 ? 64 : M <= 128 ? 128 : 256;
@@ -540,9 +544,14 @@ inline LmSplit lm_split(int M, int V) {
   const int ct = (V + 255) / 256;
   const int whole = (tm * ct / kCUs) * kCUs / tm;   // 256-column tiles in whole rounds
   const int n_tail = V - whole * 256;
+  if (whole < 1 || n_tail <= 0) return LmSplit{ct, 0, ct, 256};
+  if (M > 128) {
+    const int tm2 = (M + 127) / 128, ct2 = (n_tail + 255) / 256;
+    if (tm2 * ct2 <= kCUs) return LmSplit{whole, n_tail, whole + ct2, 256};
+  }
   const int ct_tail = (n_tail + 127) / 128;
-  if (whole < 1 || n_tail <= 0 || tm * ct_tail > kCUs) return LmSplit{ct, 0, ct};
-  return LmSplit{whole, n_tail, whole + ct_tail};
+  if (tm * ct_tail > kCUs) return LmSplit{ct, 0, ct, 256};
+  return LmSplit{whole, n_tail, whole + ct_tail, 128};
 }
 
 // A batch of blocks (M = 64 .. 256 rows): the row tile covers M.
@@ -575,6 +584,9 @@ hipError_t launch_lm_tiled(const AOperand<uint16_t>& A, int V, int K, MakeEpi ma
   if (sp.n_tail == 0) return launch_mid<256>(A, V, K, 1, make(0, 0), st, wfrag);
   hipError_t e = launch_mid<256>(A, sp.whole * 256, K, 1, make(0, 0), st, wfrag);
   if (e != hipSuccess) return e;
+  if (sp.tail_bn == 256)
+    return launch_tiled_cfg<128, 256, 2, 4>(A, sp.n_tail, K, 1, 1, make(sp.whole * 256, sp.whole),
+                                            st, wfrag);
   return launch_mid<128>(A, sp.n_tail, K, 1, make(sp.whole * 256, sp.whole), st, wfrag);
 }
 
