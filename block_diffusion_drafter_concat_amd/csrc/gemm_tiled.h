@@ -34,6 +34,7 @@
 //     pairs (c, c + d/2) of a head are both at hand).
 #pragma once
 
+#include <type_traits>
 #include <utility>
 
 #include "device_common.h"
@@ -316,8 +317,8 @@ __global__ __launch_bounds__(WM * WN * 64) void tiled_gemm_kernel(AOperand<uint1
   // slot st % NS), then the MFMAs of st with the fragment reads of st+1 and
   // the loads of stage st+NS into that slot issued between them, then wait
   // for the fragment reads -- so values that cross the loop edge are always
-  // complete.  Every slot but the one
-  // just freed holds a stage in flight or unread: NS-1 stages of prefetch.
+  // complete.  Every slot but the one just freed holds a stage in flight or
+  // unread: NS-1 stages of prefetch.
   constexpr int kAhead = NS - 1;                     // stages in flight before a wait
 #pragma unroll
   for (int q = 0; q < NS; ++q) issue();
