@@ -164,8 +164,9 @@ def test_packed_against_the_oracle(torch):
 
 
 def test_packed_lm_head_split_bit_identical(torch):
-    """V = 76900 (not a multiple of 16): both LM-head launches (256- and
-    128-column tiles) read the zero-padded last row group."""
+    """V = 76900 (not a multiple of 16): both LM-head launches (256 x 256
+    tiles, then the tail on 128 x 256 tiles) read the zero-padded last row
+    group."""
     shape = dataclasses.replace(small_bf16_shape(), vocab=76900)
     w = configs.make_weights(shape, 74)
     dr = L.Drafter(shape, w)

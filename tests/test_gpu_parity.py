@@ -259,8 +259,10 @@ def test_small_bf16_batch_of_blocks(torch, nb, B):
 def test_small_bf16_batch_lm_head_split(torch):
     """144 block rows against a 76900-token vocabulary: the LM head's 301
     column tiles of 256 overflow one round of the 256 compute units, so the
-    rows past the first 256 tiles run as a second launch of 128-column tiles
-    (argmax partials of both launches, one finalize)."""
+    vocabulary rows past the first 256 tiles run as a second launch, here on
+    128 x 256 tiles (two row tiles, the second with 16 rows; a partial last
+    column tile of 100 rows), with the argmax partials of both launches meeting
+    in one finalize."""
     shape = dataclasses.replace(small_bf16_shape(), vocab=76900)
     w = configs.make_weights(shape, 52)
     dr = L.Drafter(shape, w)

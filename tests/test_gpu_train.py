@@ -91,8 +91,8 @@ def test_train_forward_matches_oracle(torch, which):
 
 def test_train_forward_lm_head_split(torch):
     """144 block rows against a 76900-token vocabulary: the cross-entropy
-    partials come from two LM-head launches (256-column tiles, then the tail on
-    128-column tiles)."""
+    partials come from two LM-head launches (256 x 256 tiles, then the tail on
+    128 x 256 tiles)."""
     shape = dataclasses.replace(small_bf16_shape(), vocab=76900)
     want, z, slot, loss = _run(torch, shape, 66, [300, 0, 77], 16, 5.0)
     _check(shape, want, z, slot, loss, "lm head split")
