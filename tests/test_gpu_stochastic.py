@@ -35,7 +35,9 @@ def _t(torch, a, dtype=np.float32):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=dtype)).cuda()
 
 
-@pytest.mark.parametrize("N,B,V,T", [(5, 6, 3001, 0.7), (3, 16, 20011, 1.3), (7, 2, 37, 0.4)])
+# (16, 16, 151936, 0.8): the batch-16 shape the stochastic path is measured on
+@pytest.mark.parametrize("N,B,V,T", [(5, 6, 3001, 0.7), (3, 16, 20011, 1.3), (7, 2, 37, 0.4),
+                                     (16, 16, 151936, 0.8)])
 def test_sample_drafts_matches_oracle(torch, N, B, V, T):
     z = synth.values((N, B, V), "f32", 71, synth.STREAM_LOGITS, f"drf{V}", std=3.0)
     u = synth.rng(71, synth.STREAM_LOGITS, f"gu{V}").random((N, B - 1, V))
@@ -77,8 +79,12 @@ def _verify_case(torch, N, B, V, T, dtype, wid):
     return tl, dl, drafts, r, u, acc.cpu().numpy(), nxt.cpu().numpy()
 
 
+# (16, 16, 151936, 0.8, "bf16"): the measured batch-16 shape; there most sampling
+# targets lie within the 1e-4 tolerance of a cumulative boundary, so the next
+# token is mostly checked by the interval rule rather than bit for bit
 @pytest.mark.parametrize("N,B,V,T,dtype", [(8, 16, 5003, 0.8, "bf16"), (8, 16, 5003, 1.1, "f32"),
-                                           (4, 8, 20011, 1.0, "bf16"), (6, 2, 37, 0.5, "f32")])
+                                           (4, 8, 20011, 1.0, "bf16"), (6, 2, 37, 0.5, "f32"),
+                                           (16, 16, 151936, 0.8, "bf16")])
 def test_verify_stochastic_matches_oracle(torch, N, B, V, T, dtype):
     tl, dl, drafts, r, u, acc, nxt = _verify_case(torch, N, B, V, T, dtype, 72)
     want_a, want_n = O.verify_stochastic(tl, dl, drafts, T, r, u)
