@@ -77,9 +77,18 @@ def test_resident_steps_match_oracle(torch, which, lens, B):
     """Four device-resident steps from ragged contexts (one empty).  The last
     case has 9 x 16 = 144 block rows: fusion and injection then run on the
     LDS-tiled GEMM and the draft's layer GEMMs on the batched path."""
-    shape = _shape(which)
-    wid = 61 + len(lens)
-    steps, N = 4, len(lens)
+    _resident_steps(torch, _shape(which), 61 + len(lens), lens, B, 4, which)
+
+
+def test_resident_steps_full_size(torch):
+    """The loop as measured: the Qwen3-8B-shaped bf16 drafter, one sequence at
+    context 2048, B = 16, three resident steps (verify, append, draft) against
+    the oracle's cycle."""
+    _resident_steps(torch, configs.QWEN3_8B_LIKE, 2, [2048], 16, 3, "qwen3-8b-shaped")
+
+
+def _resident_steps(torch, shape, wid, lens, B, steps, which):
+    N = len(lens)
     w, dr, caches, cache, len_max = _setup(torch, shape, wid, lens, steps, B)
     anchors = configs.make_anchors(shape, wid, N)
     first = O.draft_block(w, shape, caches, anchors, B)
