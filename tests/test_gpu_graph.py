@@ -27,22 +27,27 @@ def torch():
     return torch
 
 
-def test_draft_and_verify_graph_replays_match_eager(torch):
-    shape = small_bf16_shape()
-    w = configs.make_weights(shape, 41)
+# small: two ragged sequences; headline: the Qwen3-8B-shaped drafter at one
+# sequence of context 2048, the shape whose replayed draft bench.py times
+@pytest.mark.parametrize("which", ["small", "headline"])
+def test_draft_and_verify_graph_replays_match_eager(torch, which):
+    if which == "small":
+        shape, wid, lens = small_bf16_shape(), 41, [300, 45]
+    else:
+        shape, wid, lens = configs.QWEN3_8B_LIKE, 2, [2048]
+    w = configs.make_weights(shape, wid)
     dr = L.Drafter(shape, w)
-    lens = [300, 45]
     N, B, V = len(lens), 16, shape.vocab
     cache = L.KVCache(shape, [n + 32 for n in lens])
-    upload_cache(cache, synthetic_cache(shape, 41, lens))
+    upload_cache(cache, synthetic_cache(shape, wid, lens))
     i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
-    anchors = i32(configs.make_anchors(shape, 41, N))
-    other = i32(configs.make_anchors(shape, 42, N))
+    anchors = i32(configs.make_anchors(shape, wid, N))
+    other = i32(configs.make_anchors(shape, wid + 1, N))
     ws = dr.workspace(N, B, 1)
     ids = torch.empty((N, B - 1), dtype=torch.int32, device="cuda")
     hid = torch.empty((N * B, shape.hidden), dtype=torch.float32, device="cuda")
     z = torch.empty((N * B, V), dtype=torch.float32, device="cuda")
-    lg = synth.values((N, B, V), "bf16", 41, synth.STREAM_LOGITS, "graph_logits")
+    lg = synth.values((N, B, V), "bf16", wid, synth.STREAM_LOGITS, "graph_logits")
     logits = dev(lg.reshape(N * B, V), "bf16").reshape(N, B, V)
     acc = torch.empty(N, dtype=torch.int32, device="cuda")
     bon = torch.empty(N, dtype=torch.int32, device="cuda")
