@@ -297,26 +297,30 @@ def test_small_bf16_ragged_batch_attention_order_near_capacity(torch):
     draft_compare(shape, res, ids, hid, z, f"small-bf16 ragged {nb} x B{B}")
 
 
-def test_autoregressive_stand_in_steps(torch):
+@pytest.mark.parametrize("which", ["small", "qwen"])
+def test_autoregressive_stand_in_steps(torch, which):
     """The autoregressive stand-in used for the draft-latency comparison: a
     1-layer drafter run as 2-slot passes, each pass's draft anchoring the
     next, the anchor's K/V row (written by the pass at the first free row)
     kept by advancing the committed length.  The oracle gets the same
     anchors and a cache extended with the anchor's layer-0 K/V, formed from
     its own pieces (bf16 RMSNorm of the embedding row, projection, RoPE at the
-    anchor's position)."""
-    shape = configs.scaled(small_bf16_shape(), n_layers=1)
-    w = configs.make_weights(shape, 61)
+    anchor's position).  "qwen": the width and context bench.py times it at
+    (the Qwen3-8B-shaped layer, context 2048)."""
+    if which == "small":
+        shape, wid, n0 = configs.scaled(small_bf16_shape(), n_layers=1), 61, 40
+    else:
+        shape, wid, n0 = configs.scaled(configs.QWEN3_8B_LIKE, n_layers=1), 3, 2048
+    w = configs.make_weights(shape, wid)
     dr = L.Drafter(shape, w)
-    n0 = 40
-    caches = synthetic_cache(shape, 61, [n0])
+    caches = synthetic_cache(shape, wid, [n0])
     cache = L.KVCache(shape, [n0 + 32])
     upload_cache(cache, caches)
     ws = dr.workspace(1, 2, 1)
     kc, vc = caches[0][0]
     kc, vc = np.asarray(kc, np.float64), np.asarray(vc, np.float64)
     lw = w["layers"][0]
-    anchor = configs.make_anchors(shape, 61, 1)
+    anchor = configs.make_anchors(shape, wid, 1)
     for step in range(3):
         ids, hid, z = _draft(torch, dr, shape, cache, 2, anchor, ws)
         res = O.draft_block(w, shape, [[(kc, vc)]], anchor, 2)
@@ -324,7 +328,7 @@ def test_autoregressive_stand_in_steps(torch):
         # keep the anchor's K/V: the GPU by advancing the committed length,
         # the oracle by appending the same row
         pos = n0 + step
-        u = O.bf16_round(O.rmsnorm(np.asarray(w["embed"], np.float64)[int(anchor[0])][None],
+        u = O.bf16_round(O.rmsnorm(np.asarray(w["embed"][int(anchor[0])], np.float64)[None],
                                    lw["attn_norm"], shape.rms_eps))
         k = (u @ np.asarray(lw["wk"], np.float64).T).reshape(1, shape.n_kv_heads, shape.head_dim)
         v = (u @ np.asarray(lw["wv"], np.float64).T).reshape(1, shape.n_kv_heads, shape.head_dim)
