@@ -554,8 +554,9 @@ struct TEpiLoss {
     // one wave per row; a wave's rows (wave, wave + nw, ...) go kTileRows at
     // a time so that the rows' butterflies interleave (one row after another
     // left each level's LDS-permute latency exposed: training-layout LM head
-    // 1395 -> 1342 us; the argmax epilogue measured slower that way, 373 ->
-    // 390 us at batch 16, and keeps one row at a time)
+    // 1431 -> 1331 us; the argmax epilogue measured slower that way, 376-382
+    // -> 385-389 us at batch 16 over three alternated runs, and keeps one row
+    // at a time)
     for (int lr0 = wave; lr0 < 64; lr0 += kTileRows * nw) {
       float mx[kTileRows], zl[kTileRows], sm[kTileRows];
 #pragma unroll
